@@ -1,0 +1,148 @@
+"""fp64 CPU oracle for selected block-sparse attention and top-k paged decode.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the package smoke check
+and by the benchmark's CPU-baseline leg, never by the product path.  It shares
+no code with the HIP library; the C source ``fsa_oracle.c`` states the
+definition it implements and the passages of the pages it follows.
+
+``build()`` compiles ``fsa_oracle.c`` with gcc (-O2, OpenMP) into
+``liboracle.so`` beside this file.  The wrappers take CPU tensors (bf16 for
+q/k/v, int32 for indices) and return float64 numpy arrays.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle shared library; returns its path."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-Wall", "-Wextra",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        lib.oracle_selected_attn_fwd.restype = ctypes.c_int
+        lib.oracle_selected_attn_fwd.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                                 f64, i32, P, i64, P, P]
+        lib.oracle_topk_decode.restype = ctypes.c_int
+        lib.oracle_topk_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                           i32, f64, P, i64, P, P]
+        lib.oracle_lse_merge.restype = None
+        lib.oracle_lse_merge.argtypes = [i64, i32, P, P, P, P]
+        lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    assert t.dtype == torch.bfloat16 and t.device.type == "cpu"
+    return t.contiguous().view(torch.int16)
+
+
+def _i32(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        t = t.cpu().numpy()
+    return np.ascontiguousarray(np.asarray(t, dtype=np.int32))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def selected_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blk_idx,
+                      cu_seqlens_q, cu_seqlens_k, block_size: int,
+                      softmax_scale: Optional[float] = None, causal: bool = True,
+                      tokens=None):
+    """Selected attention for every query token (or the listed ``tokens``).
+
+    Returns ``(out [n, Hq, d] float64, lse [n, Hq] float64)``.
+    """
+    lib = _load()
+    total_q, Hq, d = q.shape
+    Hkv = k.shape[1]
+    blk = _i32(blk_idx)
+    topk = blk.shape[-1] if blk.ndim == 3 else 0
+    cuq, cuk = _i32(cu_seqlens_q), _i32(cu_seqlens_k)
+    batch = cuq.size - 1
+    scale = (1.0 / np.sqrt(d)) if softmax_scale is None else float(softmax_scale)
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    if tokens is None:
+        tok_ptr, n = None, total_q
+    else:
+        tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+        tok_ptr, n = tok.ctypes.data, tok.size
+    out = np.zeros((n, Hq, d), dtype=np.float64)
+    lse = np.zeros((n, Hq), dtype=np.float64)
+    rc = lib.oracle_selected_attn_fwd(qb.data_ptr(), kb.data_ptr(), vb.data_ptr(),
+                                      blk.ctypes.data, cuq.ctypes.data, cuk.ctypes.data,
+                                      batch, Hq, Hkv, d, block_size, topk, scale, int(causal),
+                                      tok_ptr, n, out.ctypes.data, lse.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_selected_attn_fwd rejected its arguments")
+    return out, lse
+
+
+def topk_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, tok_idx,
+                block_table, cache_seqlens, softmax_scale: Optional[float] = None, seqs=None):
+    """Top-k gathered decode over a paged cache.  Returns ``(out [n,Hq,d], lse [n,Hq])``."""
+    lib = _load()
+    batch, Hq, d = q.shape
+    num_pages, page_size, Hkv, _ = k_cache.shape
+    tok = _i32(tok_idx)
+    bt = _i32(block_table)
+    cs = _i32(cache_seqlens)
+    topk = tok.shape[-1]
+    max_pages = bt.shape[1]
+    scale = (1.0 / np.sqrt(d)) if softmax_scale is None else float(softmax_scale)
+    qb, kb, vb = _bits(q), _bits(k_cache), _bits(v_cache)
+    if seqs is None:
+        sp, n = None, batch
+    else:
+        sarr = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        sp, n = sarr.ctypes.data, sarr.size
+    out = np.zeros((n, Hq, d), dtype=np.float64)
+    lse = np.zeros((n, Hq), dtype=np.float64)
+    rc = lib.oracle_topk_decode(qb.data_ptr(), kb.data_ptr(), vb.data_ptr(), tok.ctypes.data,
+                                bt.ctypes.data, cs.ctypes.data, batch, Hq, Hkv, d, page_size,
+                                max_pages, num_pages, topk, scale, sp, n, out.ctypes.data,
+                                lse.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_topk_decode rejected its arguments")
+    return out, lse
+
+
+def lse_merge(lse_parts, o_parts):
+    """Merge partials of one row: ``lse_parts [n]``, ``o_parts [n, d]`` -> ``(lse, o [d])``."""
+    lib = _load()
+    lp = np.ascontiguousarray(np.asarray(lse_parts, dtype=np.float64))
+    op = np.ascontiguousarray(np.asarray(o_parts, dtype=np.float64))
+    n, d = op.shape
+    lse = np.zeros(1, dtype=np.float64)
+    o = np.zeros(d, dtype=np.float64)
+    lib.oracle_lse_merge(n, d, lp.ctypes.data, op.ctypes.data, lse.ctypes.data, o.ctypes.data)
+    return float(lse[0]), o

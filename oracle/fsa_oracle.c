@@ -1,0 +1,271 @@
+/*
+ * fsa_oracle.c -- plain fp64 CPU definition of top-k selected block-sparse
+ * attention (prefill) and top-k gathered paged-KV decode.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may load, link or
+ * call this file: only the test suite, the package smoke check and the CPU
+ * baseline leg of the benchmark do.  It shares no code with the HIP library.
+ *
+ * What is computed (the plain definition; every step is written out, there is
+ * no blocking, fusion or reordering beyond it):
+ *
+ *  - Head mapping: query head h reads kv head h / (Hq / Hkv).  (Stated with
+ *    the 6-q-head / 2-kv-head example in the MQA/GQA paragraph of the
+ *    flash_attn_func docstring, flash-attention-npu page.)
+ *  - Causal mask aligned to the bottom-right corner: row i of a sequence with
+ *    S_q queries and S_k keys sees key j iff j <= i + S_k - S_q.  A row with
+ *    no visible key outputs zeros.  (Same docstring, causal paragraph and its
+ *    2x5 / 5x2 examples; FlashAttention basic-usage page section 4.2.)
+ *  - Selection: per (query token, kv head) a list of key-block ids of
+ *    block_size keys each; the row attends to the keys of the listed blocks
+ *    only.  The list is read as a SET: ids outside [0, ceil(S_k/bs)) are
+ *    skipped (-1 is the invalid-index value of the Ascend SFA tiling struct)
+ *    and a repeated id counts once.  (FSA page: selected attention with
+ *    block_size / topk; Ascend SFA blog: gather the top-k K/V rows, then run
+ *    ordinary attention on them.)
+ *  - Scores s_j = scale * <q, k_j>; LSE = ln sum_j exp(s_j), the natural log
+ *    of the softmax normaliser (flash_attn_func docstring, softmax_lse);
+ *    O = sum_j exp(s_j - LSE) v_j.  Empty row: O = 0, LSE = -inf.
+ *  - Decode: one query per sequence; the list holds cache positions t, read
+ *    as a set; t is skipped unless 0 <= t < cache_seqlens[b].  Position t
+ *    lives in page block_table[b, t / page_size] at row t % page_size of the
+ *    cache [num_pages, page_size, Hkv, d] (flash_attn_with_kvcache
+ *    docstring: k_cache / block_table / cache_seqlens).  A position whose
+ *    page slot lies beyond max_pages_per_seq or whose page id is outside
+ *    [0, num_pages) is skipped as well.
+ *  - Merge of partial results over a partition of the key set:
+ *    LSE = ln sum_i exp(LSE_i), O = sum_i exp(LSE_i - LSE) O_i (the split-KV
+ *    reduction of the flash-sparse-attn feature list and of the Ascend SFA
+ *    decode-reduction core).
+ *
+ * Inputs q/k/v are bfloat16 bit patterns; they are widened exactly to fp64.
+ * All arithmetic is fp64.  Rows are independent and run in parallel (OpenMP).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double widen_bf16(uint16_t bits) {
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static int cmp_i64(const void* a, const void* b) {
+    int64_t x = *(const int64_t*)a, y = *(const int64_t*)b;
+    return (x > y) - (x < y);
+}
+
+/* Sort and drop repeats in place; returns the new length. */
+static int64_t sort_unique(int64_t* v, int64_t n) {
+    if (n <= 1) return n;
+    qsort(v, (size_t)n, sizeof(int64_t), cmp_i64);
+    int64_t w = 1;
+    for (int64_t r = 1; r < n; ++r)
+        if (v[r] != v[w - 1]) v[w++] = v[r];
+    return w;
+}
+
+/*
+ * Attention of one query row over the key rows found at element offsets
+ * key_off[0..nkeys) of k and v (each row d contiguous values).
+ * s is scratch of nkeys doubles.
+ */
+static void attend(const uint16_t* qrow, const uint16_t* k, const uint16_t* v,
+                   const int64_t* key_off, int64_t nkeys, int d, double scale,
+                   double* s, double* out, double* lse) {
+    if (nkeys == 0) {
+        for (int c = 0; c < d; ++c) out[c] = 0.0;
+        *lse = -INFINITY;
+        return;
+    }
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        const uint16_t* kr = k + key_off[j];
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += widen_bf16(qrow[c]) * widen_bf16(kr[c]);
+        s[j] = scale * dot;
+        if (s[j] > m) m = s[j];
+    }
+    double sum = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) sum += exp(s[j] - m);
+    double L = m + log(sum);
+    for (int c = 0; c < d; ++c) out[c] = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        double p = exp(s[j] - L);
+        const uint16_t* vr = v + key_off[j];
+        for (int c = 0; c < d; ++c) out[c] += p * widen_bf16(vr[c]);
+    }
+    *lse = L;
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Prefill.  q [total_q, Hq, d], k/v [total_k, Hkv, d] (bf16 bits),
+ * blk_idx [total_q, Hkv, topk], cu_q/cu_k [batch + 1].
+ * tokens: global query-token ids to evaluate (NULL: all total_q tokens, then
+ * ntok must equal total_q).  out [ntok, Hq, d], lse [ntok, Hq] (fp64).
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_selected_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const int32_t* blk_idx, const int32_t* cu_q, const int32_t* cu_k,
+                             int32_t batch, int32_t Hq, int32_t Hkv, int32_t d,
+                             int32_t block_size, int32_t topk, double scale, int32_t causal,
+                             const int64_t* tokens, int64_t ntok, double* out, double* lse) {
+    if (batch < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || block_size <= 0 ||
+        topk < 0)
+        return -1;
+    const int G = Hq / Hkv;
+    const int64_t total_q = cu_q[batch];
+    if (tokens == NULL && ntok != total_q) return -1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        int64_t* blocks = (int64_t*)malloc(sizeof(int64_t) * (size_t)(topk > 0 ? topk : 1));
+        int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)(topk > 0 ? topk : 1) *
+                                         (size_t)block_size);
+        double* s = (double*)malloc(sizeof(double) * (size_t)(topk > 0 ? topk : 1) *
+                                    (size_t)block_size);
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < ntok; ++r) {
+            int64_t t = tokens ? tokens[r] : r;
+            if (t < 0 || t >= total_q) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            /* sequence containing token t */
+            int sq_id = 0;
+            while (sq_id + 1 < batch && cu_q[sq_id + 1] <= t) ++sq_id;
+            const int64_t i = t - cu_q[sq_id];
+            const int64_t Sq = cu_q[sq_id + 1] - cu_q[sq_id];
+            const int64_t Sk = cu_k[sq_id + 1] - cu_k[sq_id];
+            const int64_t nblk = (Sk + block_size - 1) / block_size;
+            for (int g = 0; g < Hkv; ++g) {
+                /* the selected block set */
+                int64_t nb = 0;
+                const int32_t* lst = blk_idx + (t * Hkv + g) * (int64_t)topk;
+                for (int e = 0; e < topk; ++e)
+                    if (lst[e] >= 0 && lst[e] < nblk) blocks[nb++] = lst[e];
+                nb = sort_unique(blocks, nb);
+                /* the visible keys of those blocks */
+                int64_t nk = 0;
+                for (int64_t bi = 0; bi < nb; ++bi) {
+                    for (int64_t j = blocks[bi] * block_size;
+                         j < (blocks[bi] + 1) * block_size && j < Sk; ++j) {
+                        if (causal && j > i + Sk - Sq) continue;
+                        keys[nk++] = ((cu_k[sq_id] + j) * Hkv + g) * (int64_t)d;
+                    }
+                }
+                for (int hh = 0; hh < G; ++hh) {
+                    int h = g * G + hh;
+                    attend(q + (t * Hq + h) * (int64_t)d, k, v, keys, nk, d, scale, s,
+                           out + (r * Hq + h) * (int64_t)d, lse + r * Hq + h);
+                }
+            }
+        }
+        free(blocks);
+        free(keys);
+        free(s);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Top-k decode.  q [batch, Hq, d]; k_cache/v_cache [num_pages, page_size, Hkv, d];
+ * tok_idx [batch, Hkv, topk]; block_table [batch, max_pages]; cache_seqlens [batch].
+ * seqs: batch entries to evaluate (NULL: all, nseq == batch).
+ * out [nseq, Hq, d], lse [nseq, Hq].
+ */
+int oracle_topk_decode(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache,
+                       const int32_t* tok_idx, const int32_t* block_table,
+                       const int32_t* cache_seqlens, int32_t batch, int32_t Hq, int32_t Hkv,
+                       int32_t d, int32_t page_size, int32_t max_pages, int32_t num_pages,
+                       int32_t topk, double scale, const int64_t* seqs, int64_t nseq,
+                       double* out, double* lse) {
+    if (batch < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || page_size <= 0 ||
+        max_pages < 0 || topk < 0)
+        return -1;
+    if (seqs == NULL && nseq != batch) return -1;
+    const int G = Hq / Hkv;
+    int bad = 0;
+#pragma omp parallel
+    {
+        int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)(topk > 0 ? topk : 1));
+        int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)(topk > 0 ? topk : 1));
+        double* s = (double*)malloc(sizeof(double) * (size_t)(topk > 0 ? topk : 1));
+#pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int64_t r = 0; r < nseq; ++r) {
+            for (int g = 0; g < Hkv; ++g) {
+                int64_t b = seqs ? seqs[r] : r;
+                if (b < 0 || b >= batch) {
+#pragma omp atomic write
+                    bad = 1;
+                    continue;
+                }
+                const int64_t L = cache_seqlens[b];
+                const int32_t* lst = tok_idx + (b * Hkv + g) * (int64_t)topk;
+                int64_t n = 0;
+                for (int e = 0; e < topk; ++e) {
+                    int64_t t = lst[e];
+                    if (t < 0 || t >= L) continue;
+                    if (t / page_size >= max_pages) continue;
+                    int64_t page = block_table[b * max_pages + t / page_size];
+                    if (page < 0 || page >= num_pages) continue;
+                    pos[n++] = t;
+                }
+                n = sort_unique(pos, n);
+                for (int64_t e = 0; e < n; ++e) {
+                    int64_t t = pos[e];
+                    int64_t page = block_table[b * max_pages + t / page_size];
+                    keys[e] = ((page * page_size + t % page_size) * Hkv + g) * (int64_t)d;
+                }
+                for (int hh = 0; hh < G; ++hh) {
+                    int h = g * G + hh;
+                    attend(q + (b * Hq + h) * (int64_t)d, k_cache, v_cache, keys, n, d, scale,
+                           s, out + (r * Hq + h) * (int64_t)d, lse + r * Hq + h);
+                }
+            }
+        }
+        free(pos);
+        free(keys);
+        free(s);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Merge n partial results (lse_parts[n], o_parts[n, d]) of one row computed on
+ * disjoint key subsets.  An empty part carries LSE = -inf and adds nothing.
+ */
+void oracle_lse_merge(int64_t n, int32_t d, const double* lse_parts, const double* o_parts,
+                      double* lse, double* o) {
+    double m = -INFINITY;
+    for (int64_t i = 0; i < n; ++i)
+        if (lse_parts[i] > m) m = lse_parts[i];
+    for (int c = 0; c < d; ++c) o[c] = 0.0;
+    if (m == -INFINITY) {
+        *lse = -INFINITY;
+        return;
+    }
+    double sum = 0.0;
+    for (int64_t i = 0; i < n; ++i) sum += exp(lse_parts[i] - m);
+    double L = m + log(sum);
+    for (int64_t i = 0; i < n; ++i) {
+        double w = exp(lse_parts[i] - L);
+        for (int c = 0; c < d; ++c) o[c] += w * o_parts[i * d + c];
+    }
+    *lse = L;
+}

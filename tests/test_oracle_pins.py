@@ -1,0 +1,437 @@
+"""Pins for the fp64 oracle: facts the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: the worked
+mask examples and the GQA table printed on the pages (``tests/golden``),
+brute-force dense attention written here with numpy, a library routine
+(torch SDPA in float64), closed forms (uniform scores, a single visible key,
+merges of equal parts) and invariances that set semantics imply.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([int(x) for x in line.split()])
+    return np.array(rows)
+
+
+def bf16(x):
+    return torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+def rand_bf16(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g).to(torch.bfloat16)
+
+
+def f64(t):
+    return t.to(torch.float64).numpy()
+
+
+def full_lists(total_q, hkv, nblk, topk, rng, dup=False):
+    """Every block id in [0, nblk) per list (shuffled), -1 pads, optional repeats."""
+    assert topk >= nblk
+    out = np.full((total_q, hkv, topk), -1, dtype=np.int32)
+    for t in range(total_q):
+        for g in range(hkv):
+            ids = list(rng.permutation(nblk))
+            if dup and topk > nblk:
+                ids.append(int(rng.integers(nblk)))
+            out[t, g, :len(ids)] = ids
+    return out
+
+
+def dense_reference(q, k, v, cu_q, cu_k, scale, causal, kv_of_head):
+    """Brute-force masked softmax attention (numpy fp64), bottom-right causal."""
+    total_q, hq, d = q.shape
+    out = np.zeros((total_q, hq, d))
+    lse = np.full((total_q, hq), -np.inf)
+    for s in range(len(cu_q) - 1):
+        qa, qb_ = cu_q[s], cu_q[s + 1]
+        ka, kb = cu_k[s], cu_k[s + 1]
+        sq, sk = qb_ - qa, kb - ka
+        i = np.arange(sq)[:, None]
+        j = np.arange(sk)[None, :]
+        vis = np.ones((sq, sk), bool) if not causal else (j <= i + sk - sq)
+        for h in range(hq):
+            g = kv_of_head[h]
+            S = scale * (q[qa:qb_, h, :] @ k[ka:kb, g, :].T)
+            S = np.where(vis, S, -np.inf)
+            for r in range(sq):
+                if not vis[r].any():
+                    continue
+                m = S[r].max()
+                e = np.exp(S[r] - m)
+                out[qa + r, h] = (e / e.sum()) @ v[ka:kb, g, :]
+                lse[qa + r, h] = m + np.log(e.sum())
+    return out, lse
+
+
+# ---------------------------------------------------------------- worked examples
+
+@pytest.mark.parametrize("fixture,sq,sk", [("causal_mask_q2_k5.txt", 2, 5),
+                                           ("causal_mask_q5_k2.txt", 5, 2)])
+@pytest.mark.parametrize("bs", [1, 2, "sk"])
+def test_mask_worked_examples(fixture, sq, sk, bs):
+    mask = load_golden(fixture)
+    assert mask.shape == (sq, sk)
+    bs = sk if bs == "sk" else bs
+    d = 8
+    nblk = -(-sk // bs)
+    q = rand_bf16((sq, 1, d), 11)
+    k = rand_bf16((sk, 1, d), 12)
+    # V rows are unit vectors: O[i, j] is the probability of key j for row i
+    v = bf16(np.eye(sk, d)[:, None, :])
+    blk = np.tile(np.arange(nblk, dtype=np.int32)[::-1], (sq, 1, 1)).reshape(sq, 1, nblk)
+    out, lse = oracle.selected_attn_fwd(q, k, v, blk, [0, sq], [0, sk], bs)
+    probs = out[:, 0, :sk]
+    assert np.array_equal((probs > 0).astype(int), mask)
+    for i in range(sq):
+        if mask[i].any():
+            assert abs(probs[i].sum() - 1.0) < 1e-12
+            assert np.isfinite(lse[i, 0])
+        else:
+            assert np.all(out[i] == 0.0)            # all-zero mask row -> zero output
+            assert lse[i, 0] == -np.inf
+
+
+def test_gqa_golden_table():
+    table = load_golden("gqa_q6_kv2.txt")
+    kv_of_head = dict((int(a), int(b)) for a, b in table)
+    hq, hkv, d, s = 6, 2, 16, 40
+    q = rand_bf16((s, hq, d), 21)
+    k = rand_bf16((s, hkv, d), 22)
+    # kv head 0 values are all 1, kv head 1 values are all -2
+    v = bf16(np.stack([np.full((s, d), 1.0), np.full((s, d), -2.0)], axis=1))
+    rng = np.random.default_rng(0)
+    blk = full_lists(s, hkv, 3, 4, rng)
+    out, _ = oracle.selected_attn_fwd(q, k, v, blk, [0, s], [0, s], 16)
+    for h in range(hq):
+        want = 1.0 if kv_of_head[h] == 0 else -2.0
+        assert np.allclose(out[:, h, :], want, atol=1e-12, rtol=0)
+
+
+def test_gqa_golden_table_per_head():
+    """Each q head equals single-head attention against the kv head the table names."""
+    table = load_golden("gqa_q6_kv2.txt")
+    hq, hkv, d, s, bs = 6, 2, 16, 70, 16
+    q = rand_bf16((s, hq, d), 31)
+    k = rand_bf16((s, hkv, d), 32)
+    v = rand_bf16((s, hkv, d), 33)
+    rng = np.random.default_rng(1)
+    nblk = -(-s // bs)
+    blk = np.full((s, hkv, 3), -1, np.int32)
+    for t in range(s):
+        for g in range(hkv):
+            blk[t, g] = rng.choice(nblk, 3, replace=False)
+    out, lse = oracle.selected_attn_fwd(q, k, v, blk, [0, s], [0, s], bs)
+    for h, g in table:
+        o1, l1 = oracle.selected_attn_fwd(q[:, h:h + 1].contiguous(), k[:, g:g + 1].contiguous(),
+                                          v[:, g:g + 1].contiguous(), blk[:, g:g + 1].copy(),
+                                          [0, s], [0, s], bs)
+        assert np.array_equal(out[:, h], o1[:, 0])
+        assert np.array_equal(lse[:, h], l1[:, 0])
+
+
+# ---------------------------------------------------------------- dense equivalence
+
+DENSE_CASES = [
+    # seqlens_q, seqlens_k, hq, hkv, d, bs, causal
+    ((37,), (37,), 2, 1, 8, 8, True),
+    ((130,), (130,), 4, 2, 16, 64, True),        # ragged last block
+    ((50, 17, 64), (50, 17, 64), 3, 3, 8, 16, True),
+    ((5, 20), (12, 33), 6, 2, 8, 4, True),       # S_q < S_k: bottom-right offset
+    ((9, 3), (4, 2), 2, 1, 8, 2, True),          # S_q > S_k: leading empty rows
+    ((33,), (45,), 2, 2, 8, 8, False),
+    ((0, 12), (0, 12), 2, 1, 8, 4, True),        # an empty sequence
+]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES)
+def test_all_blocks_equal_dense_bruteforce(case):
+    sqs, sks, hq, hkv, d, bs, causal = case
+    cu_q = np.concatenate([[0], np.cumsum(sqs)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(sks)]).astype(np.int32)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    q = rand_bf16((tq, hq, d), 41)
+    k = rand_bf16((tk, hkv, d), 42)
+    v = rand_bf16((tk, hkv, d), 43)
+    rng = np.random.default_rng(2)
+    nblk = max(-(-s // bs) for s in sks)
+    blk = full_lists(tq, hkv, nblk, nblk + 2, rng, dup=True)
+    scale = 0.37
+    out, lse = oracle.selected_attn_fwd(q, k, v, blk, cu_q, cu_k, bs, scale, causal)
+    G = hq // hkv
+    ref_o, ref_l = dense_reference(f64(q), f64(k), f64(v), cu_q, cu_k, scale, causal,
+                                   [h // G for h in range(hq)])
+    assert np.allclose(out, ref_o, atol=1e-12, rtol=0)
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.allclose(lse[fin], ref_l[fin], atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("s,hq,hkv,d,bs", [(96, 4, 1, 32, 16), (150, 8, 2, 64, 64)])
+def test_all_blocks_equal_torch_sdpa(s, hq, hkv, d, bs):
+    q = rand_bf16((s, hq, d), 51)
+    k = rand_bf16((s, hkv, d), 52)
+    v = rand_bf16((s, hkv, d), 53)
+    nblk = -(-s // bs)
+    blk = full_lists(s, hkv, nblk, nblk, np.random.default_rng(3))
+    out, _ = oracle.selected_attn_fwd(q, k, v, blk, [0, s], [0, s], bs)
+    G = hq // hkv
+    qt = q.to(torch.float64).permute(1, 0, 2)[None]
+    kt = k.to(torch.float64).repeat_interleave(G, dim=1).permute(1, 0, 2)[None]
+    vt = v.to(torch.float64).repeat_interleave(G, dim=1).permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    ref = ref[0].permute(1, 0, 2).numpy()
+    assert np.allclose(out, ref, atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_uniform_scores_give_log_count():
+    """q = 0: every visible key scores 0, so LSE = ln|J| and O = mean of visible V rows.
+
+    The lists carry repeats, -1 pads, ids past the last block and future
+    blocks; |J| is counted here by testing every key for membership.
+    """
+    sqs, hq, hkv, d, bs, topk = (77, 40), 2, 2, 8, 8, 9
+    cu = np.concatenate([[0], np.cumsum(sqs)]).astype(np.int32)
+    tq = int(cu[-1])
+    q = torch.zeros((tq, hq, d), dtype=torch.bfloat16)
+    k = rand_bf16((tq, hkv, d), 61)
+    v = rand_bf16((tq, hkv, d), 62)
+    rng = np.random.default_rng(4)
+    blk = rng.integers(-3, 14, size=(tq, hkv, topk)).astype(np.int32)
+    blk[:, :, -1] = blk[:, :, 0]                            # a repeat in every list
+    out, lse = oracle.selected_attn_fwd(q, k, v, blk, cu, cu, bs)
+    vv = f64(v)
+    for s in range(len(sqs)):
+        for i in range(sqs[s]):
+            t = cu[s] + i
+            for h in range(hq):
+                g = h // (hq // hkv)
+                members = set(int(x) for x in blk[t, g])
+                vis = [j for j in range(sqs[s]) if (j // bs) in members and j <= i]
+                if not vis:
+                    assert lse[t, h] == -np.inf and np.all(out[t, h] == 0)
+                    continue
+                assert abs(lse[t, h] - math.log(len(vis))) < 1e-12
+                assert np.allclose(out[t, h], vv[cu[s] + np.array(vis), g].mean(0), atol=1e-12)
+
+
+def test_single_visible_key():
+    """Row 0 under causal attention with block 0 listed sees only key 0."""
+    d, s = 16, 20
+    q = rand_bf16((s, 1, d), 71)
+    k = rand_bf16((s, 1, d), 72)
+    v = rand_bf16((s, 1, d), 73)
+    blk = np.full((s, 1, 2), -1, np.int32)
+    blk[:, 0, 0] = 0
+    scale = 0.25
+    out, lse = oracle.selected_attn_fwd(q, k, v, blk, [0, s], [0, s], 4, scale)
+    assert np.array_equal(out[0, 0], f64(v)[0, 0])
+    want = scale * float(f64(q)[0, 0] @ f64(k)[0, 0])
+    assert abs(lse[0, 0] - want) < 1e-12
+
+
+def test_default_scale_is_inverse_sqrt_d():
+    d, s = 64, 10
+    q, k, v = rand_bf16((s, 1, d), 74), rand_bf16((s, 1, d), 75), rand_bf16((s, 1, d), 76)
+    blk = np.zeros((s, 1, 1), np.int32)
+    a = oracle.selected_attn_fwd(q, k, v, blk, [0, s], [0, s], 64)
+    b = oracle.selected_attn_fwd(q, k, v, blk, [0, s], [0, s], 64, softmax_scale=0.125)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------- set semantics
+
+def test_list_invariances():
+    s, hq, hkv, d, bs, topk = 300, 4, 2, 16, 32, 5
+    q, k, v = rand_bf16((s, hq, d), 81), rand_bf16((s, hkv, d), 82), rand_bf16((s, hkv, d), 83)
+    rng = np.random.default_rng(5)
+    nblk = -(-s // bs)
+    blk = np.full((s, hkv, topk), -1, np.int32)
+    for t in range(s):
+        for g in range(hkv):
+            qb = t // bs
+            blk[t, g, :3] = rng.choice(qb + 1, min(3, qb + 1), replace=False).tolist() + \
+                [-1] * (3 - min(3, qb + 1))
+    base = oracle.selected_attn_fwd(q, k, v, blk, [0, s], [0, s], bs)
+    shuffled = rng.permuted(blk, axis=2)
+    padded = blk.copy()
+    padded[:, :, 3] = blk[:, :, 0]            # repeat
+    padded[:, :, 4] = -7                      # invalid
+    future = blk.copy()
+    future[:, :, 3] = nblk - 1                # future block for most rows (visible for the last)
+    future[:, :, 4] = nblk + 5                # past the last block
+    for variant in (shuffled, padded):
+        o, l = oracle.selected_attn_fwd(q, k, v, variant, [0, s], [0, s], bs)
+        assert np.array_equal(o, base[0]) and np.array_equal(l, base[1])
+    o, l = oracle.selected_attn_fwd(q, k, v, future, [0, s], [0, s], bs)
+    early = np.arange(s) < (nblk - 1) * bs
+    assert np.array_equal(o[early], base[0][early]) and np.array_equal(l[early], base[1][early])
+
+
+def test_split_identity_and_merge():
+    """Attention over a partition of the selected blocks, merged, equals the whole."""
+    s, hq, hkv, d, bs, topk = 256, 2, 1, 16, 16, 8
+    q, k, v = rand_bf16((s, hq, d), 91), rand_bf16((s, hkv, d), 92), rand_bf16((s, hkv, d), 93)
+    rng = np.random.default_rng(6)
+    blk = np.full((s, hkv, topk), -1, np.int32)
+    for t in range(s):
+        n = min(topk, t // bs + 1)
+        blk[t, 0, :n] = rng.choice(t // bs + 1, n, replace=False)
+    whole = oracle.selected_attn_fwd(q, k, v, blk, [0, s], [0, s], bs)
+    parts = []
+    for lo, hi in ((0, 3), (3, 5), (5, 8)):
+        p = np.full_like(blk, -1)
+        p[:, :, lo:hi] = blk[:, :, lo:hi]
+        parts.append(oracle.selected_attn_fwd(q, k, v, p, [0, s], [0, s], bs))
+    for t in range(0, s, 7):
+        for h in range(hq):
+            lse, o = oracle.lse_merge([p[1][t, h] for p in parts], [p[0][t, h] for p in parts])
+            assert abs(lse - whole[1][t, h]) < 1e-12
+            assert np.allclose(o, whole[0][t, h], atol=1e-12, rtol=0)
+
+
+def test_merge_closed_forms():
+    o = np.arange(6, dtype=np.float64).reshape(2, 3)
+    lse, out = oracle.lse_merge([1.5, 1.5], o)              # equal weights
+    assert abs(lse - (1.5 + math.log(2))) < 1e-15
+    assert np.allclose(out, o.mean(0), atol=1e-15)
+    lse, out = oracle.lse_merge([-np.inf, 0.3], o)          # an empty part adds nothing
+    assert lse == 0.3 and np.array_equal(out, o[1])
+    lse, out = oracle.lse_merge([-np.inf, -np.inf], o)      # nothing at all
+    assert lse == -np.inf and np.all(out == 0)
+
+
+def test_mha_expansion_equivalence():
+    """GQA equals MHA with K/V repeated per query head and lists repeated to match."""
+    s, hq, hkv, d, bs, topk = 200, 6, 2, 16, 32, 3
+    q, k, v = rand_bf16((s, hq, d), 101), rand_bf16((s, hkv, d), 102), rand_bf16((s, hkv, d), 103)
+    rng = np.random.default_rng(7)
+    blk = np.full((s, hkv, topk), -1, np.int32)
+    for t in range(s):
+        for g in range(hkv):
+            n = min(topk, t // bs + 1)
+            blk[t, g, :n] = rng.choice(t // bs + 1, n, replace=False)
+    a = oracle.selected_attn_fwd(q, k, v, blk, [0, s], [0, s], bs)
+    G = hq // hkv
+    b = oracle.selected_attn_fwd(q, k.repeat_interleave(G, 1).contiguous(),
+                                 v.repeat_interleave(G, 1).contiguous(),
+                                 np.repeat(blk, G, axis=1), [0, s], [0, s], bs)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_token_subset_matches_full_run():
+    s, hq, hkv, d, bs, topk = 100, 2, 1, 8, 16, 3
+    q, k, v = rand_bf16((s, hq, d), 111), rand_bf16((s, hkv, d), 112), rand_bf16((s, hkv, d), 113)
+    blk = np.random.default_rng(8).integers(-1, 7, (s, hkv, topk)).astype(np.int32)
+    full = oracle.selected_attn_fwd(q, k, v, blk, [0, s], [0, s], bs)
+    toks = [99, 0, 17, 64]
+    sub = oracle.selected_attn_fwd(q, k, v, blk, [0, s], [0, s], bs, tokens=toks)
+    assert np.array_equal(sub[0], full[0][toks]) and np.array_equal(sub[1], full[1][toks])
+
+
+# ---------------------------------------------------------------- decode
+
+def _contig_cache(batch, L, hkv, d, seed):
+    k = rand_bf16((batch, L, hkv, d), seed)
+    v = rand_bf16((batch, L, hkv, d), seed + 1)
+    return k, v
+
+
+def test_decode_full_list_equals_dense_single_query():
+    batch, hq, hkv, d, L, P = 3, 4, 2, 16, 50, 8
+    kc, vc = _contig_cache(batch, L, hkv, d, 121)
+    q = rand_bf16((batch, hq, d), 123)
+    pages = -(-L // P)
+    pad = pages * P - L
+    kpad = torch.cat([kc, torch.zeros(batch, pad, hkv, d, dtype=kc.dtype)], 1)
+    vpad = torch.cat([vc, torch.zeros(batch, pad, hkv, d, dtype=vc.dtype)], 1)
+    k_cache = kpad.reshape(batch * pages, P, hkv, d).contiguous()
+    v_cache = vpad.reshape(batch * pages, P, hkv, d).contiguous()
+    bt = np.arange(batch * pages, dtype=np.int32).reshape(batch, pages)
+    seqlens = np.array([50, 31, 1], np.int32)
+    rng = np.random.default_rng(9)
+    tok = np.stack([np.stack([rng.permutation(L) for _ in range(hkv)]) for _ in range(batch)])
+    out, lse = oracle.topk_decode(q, k_cache, v_cache, tok.astype(np.int32), bt, seqlens)
+    G = hq // hkv
+    for b in range(batch):
+        Lb = seqlens[b]
+        ref_o, ref_l = dense_reference(f64(q[b:b + 1]), f64(kc[b, :Lb]), f64(vc[b, :Lb]),
+                                       [0, 1], [0, Lb], 1 / math.sqrt(d), False,
+                                       [h // G for h in range(hq)])
+        assert np.allclose(out[b], ref_o[0], atol=1e-12, rtol=0)
+        assert np.allclose(lse[b], ref_l[0], atol=1e-12, rtol=0)
+
+
+def test_decode_paged_identity():
+    """A permuted block table over a cache permuted to match gives the same result."""
+    batch, hq, hkv, d, L, P, topk = 4, 4, 1, 8, 64, 16, 20
+    pages = L // P
+    num_pages = batch * pages
+    kc = rand_bf16((num_pages, P, hkv, d), 131)
+    vc = rand_bf16((num_pages, P, hkv, d), 132)
+    q = rand_bf16((batch, hq, d), 133)
+    rng = np.random.default_rng(10)
+    tok = rng.integers(-2, L + 3, size=(batch, hkv, topk)).astype(np.int32)
+    seqlens = np.array([64, 40, 17, 0], np.int32)
+    bt = np.arange(num_pages, dtype=np.int32).reshape(batch, pages)
+    a = oracle.topk_decode(q, kc, vc, tok, bt, seqlens)
+    perm = rng.permutation(num_pages)              # physical page of logical page p
+    kc2 = torch.empty_like(kc)
+    vc2 = torch.empty_like(vc)
+    kc2[perm] = kc
+    vc2[perm] = vc
+    bt2 = perm[bt].astype(np.int32)
+    b = oracle.topk_decode(q, kc2, vc2, tok, bt2, seqlens)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.all(a[1][3] == -np.inf) and np.all(a[0][3] == 0)   # empty cache
+
+
+def test_decode_uniform_scores_log_count():
+    batch, hq, hkv, d, L, P, topk = 2, 2, 2, 8, 40, 8, 30
+    pages = L // P
+    kc = rand_bf16((batch * pages, P, hkv, d), 141)
+    vc = rand_bf16((batch * pages, P, hkv, d), 142)
+    q = torch.zeros((batch, hq, d), dtype=torch.bfloat16)
+    rng = np.random.default_rng(11)
+    tok = rng.integers(-3, L + 5, size=(batch, hkv, topk)).astype(np.int32)
+    bt = rng.permutation(batch * pages).astype(np.int32).reshape(batch, pages)
+    seqlens = np.array([40, 23], np.int32)
+    out, lse = oracle.topk_decode(q, kc, vc, tok, bt, seqlens)
+    vv = f64(vc)
+    for b in range(batch):
+        for h in range(hq):
+            g = h // (hq // hkv)
+            vis = sorted(set(int(t) for t in tok[b, g] if 0 <= t < seqlens[b]))
+            assert abs(lse[b, h] - math.log(len(vis))) < 1e-12
+            rows = [vv[bt[b, t // P], t % P, g] for t in vis]
+            assert np.allclose(out[b, h], np.mean(rows, 0), atol=1e-12)
+
+
+def test_oracle_rejects_bad_arguments():
+    q = torch.zeros((4, 3, 8), dtype=torch.bfloat16)
+    k = torch.zeros((4, 2, 8), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):          # 3 query heads over 2 kv heads
+        oracle.selected_attn_fwd(q, k, k, np.zeros((4, 2, 1), np.int32), [0, 4], [0, 4], 4)
+    q = torch.zeros((4, 2, 8), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):          # token id out of range
+        oracle.selected_attn_fwd(q, k, k, np.zeros((4, 2, 1), np.int32), [0, 4], [0, 4], 4,
+                                 tokens=[5])
