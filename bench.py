@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark: selected-attention prefill TFLOP/s and top-k decode GB/s on one GPU.
+
+One step = one pass of the hot path over resident synthetic inputs:
+  * prefill: fsa_selected_attn_fwd on B=2, S=8192, Hq=32, Hkv=8, d=128,
+    block 64, topk 16 (init 1, local 2, uniform remainder), causal;
+  * decode: fsa_topk_decode on 32 sequences, Hq=32, Hkv=8, d=128, paged cache
+    of 32768 tokens in pages of 256, topk 2048 (last 128 + uniform rest),
+    alternating between two cache copies so a call does not find its rows
+    still on chip from the previous one.
+The prefill phase and the decode phase are each timed over exactly K calls,
+bracketed by device synchronisation, after W warm-up steps.  ``value`` is the
+prefill's effective TFLOP/s (4*d*64*G flops per distinct selected (token, kv
+head, block) triple); decode GB/s counts the algorithmic bytes (selected K/V
+rows, lists, q, out, block table).  Per-launch durations come from HIP events
+on the stream the kernels run on.  The fp64 CPU oracle is timed on a bounded
+sample of the same prefill workload on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "selected-attn fwd effective TFLOP/s + decode HBM GB/s, % roofline (1 GPU)"
+PREFILL = "prefill_b2_s8192_h32_kv8_d128_top16"
+DECODE = "decode_b32_h32_kv8_d128_L32768_p256_top2048"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_src, units):
+    """HBM bytes per launch from the committed PMC summary, if it still
+    describes the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(units)
+    if not ent:
+        return None
+    if ent.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the selected-attention path has no multi-GPU "
+              "mode (no sharding or collectives are built); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import top_block_sparse_amd as fsa
+    from top_block_sparse_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    fsa._lib.load()          # fails loudly when libfsa.so is not built
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- inputs (generated on the host, then resident in HBM)
+    pspec = inputs.PREFILL_WORKLOADS[PREFILL]
+    log(f"generating {PREFILL}")
+    pd = inputs.make_prefill(pspec)
+    G = pspec.num_heads_q // pspec.num_heads_kv
+    pairs = inputs.count_valid_pairs(pd["blk_idx"].numpy(), pd["cu_seqlens_q"].numpy(),
+                                     pd["cu_seqlens_k"].numpy(), pspec.block_size)
+    flops = 4.0 * pspec.head_dim * pspec.block_size * G * pairs
+    pg = {k: pd[k].to(dev) for k in ("q", "k", "v", "blk_idx", "cu_seqlens_q", "cu_seqlens_k")}
+    p_out = torch.empty_like(pg["q"])
+    p_lse = torch.empty((pspec.num_heads_q, pg["q"].shape[0]), dtype=torch.float32, device=dev)
+    total_q = pg["q"].shape[0]
+    p_ws_bytes = fsa.fsa_selected_attn_fwd_workspace_size(
+        len(pspec.seqlens), total_q, pd["max_seqlen_q"], pspec.num_heads_q, pspec.num_heads_kv,
+        pspec.head_dim, pspec.block_size, pspec.topk, 0)
+    p_ws = torch.empty(max(p_ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    dspec = inputs.DECODE_WORKLOADS[DECODE]
+    log(f"generating {DECODE}")
+    dd = inputs.make_decode(dspec)
+    sets = []
+    kc = dd["k_cache"].to(dev)
+    vc = dd["v_cache"].to(dev)
+    sets.append((kc, vc))
+    sets.append((kc.clone(), vc.clone()))          # second copy at other addresses
+    dq = dd["q"].to(dev)
+    dtok = dd["tok_idx"].to(dev)
+    dbt = dd["block_table"].to(dev)
+    dcs = dd["cache_seqlens"].to(dev)
+    d_out = torch.empty_like(dq)
+    d_lse = torch.empty((dspec.batch, dspec.num_heads_q), dtype=torch.float32, device=dev)
+    d_ws = torch.empty(fsa.fsa_topk_decode_workspace_size(
+        dspec.batch, dspec.num_heads_q, dspec.num_heads_kv, dspec.head_dim, dspec.topk, 0),
+        dtype=torch.uint8, device=dev)
+    n_sel = dspec.batch * dspec.num_heads_kv * dspec.topk          # lists hold distinct positions
+    d_bytes = (n_sel * 2 * dspec.head_dim * 2                      # selected K and V rows
+               + dtok.numel() * 4 + dbt.numel() * 4 + dcs.numel() * 4
+               + dq.numel() * 2 + d_out.numel() * 2 + d_lse.numel() * 4)
+
+    def prefill():
+        fsa.fsa_selected_attn_fwd(pg["q"], pg["k"], pg["v"], pg["blk_idx"], pg["cu_seqlens_q"],
+                                  pg["cu_seqlens_k"], pd["max_seqlen_q"], pd["max_seqlen_k"],
+                                  out=p_out, lse=p_lse, workspace=p_ws)
+
+    def decode(i):
+        k_, v_ = sets[i % 2]
+        fsa.fsa_topk_decode(dq, k_, v_, dtok, dbt, dcs, out=d_out, lse=d_lse, workspace=d_ws)
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        prefill()
+        decode(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    p_ev = [(ev(), ev()) for _ in range(K)]
+    d_ev = [(ev(), ev()) for _ in range(K)]
+
+    log(f"timing {K} prefill calls")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        p_ev[i][0].record(stream)
+        prefill()
+        p_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_prefill = time.perf_counter() - t0
+
+    log(f"timing {K} decode calls")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        d_ev[i][0].record(stream)
+        decode(i)
+        d_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_decode = time.perf_counter() - t0
+
+    p_ms = np.array([a.elapsed_time(b) for a, b in p_ev])
+    d_ms = np.array([a.elapsed_time(b) for a, b in d_ev])
+    p_tflops_wall = flops * K / t_prefill / 1e12
+    p_tflops_evt = flops / (p_ms.mean() * 1e-3) / 1e12
+    d_gbs_evt = d_bytes / (d_ms.mean() * 1e-3) / 1e9
+    d_gbs_wall = d_bytes * K / t_decode / 1e9
+    log(f"prefill: mean {p_ms.mean():.3f} ms  min {p_ms.min():.3f} ms  "
+        f"{p_tflops_evt:.1f} TFLOP/s (events), {p_tflops_wall:.1f} (wall)")
+    log(f"decode : mean {d_ms.mean() * 1e3:.1f} us  min {d_ms.min() * 1e3:.1f} us  "
+        f"{d_gbs_evt:.0f} GB/s (events), {d_gbs_wall:.0f} (wall)")
+
+    kern_src = os.path.join(ROOT, "top_block_sparse_amd", "csrc", "sel_attn_fwd.hip")
+    traffic = measured_traffic(kern_src, PREFILL)
+    roofline = {"bound": "mfma", "achieved": round(p_tflops_evt, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(p_tflops_evt / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "sel_attn_fwd_kernel<128>",
+                "flops_per_launch": flops, "avg_launch_ms": round(float(p_ms.mean()), 4)}
+    dec_src = os.path.join(ROOT, "top_block_sparse_amd", "csrc", "topk_decode.hip")
+    d_traffic = measured_traffic(dec_src, DECODE)
+    decode_obj = {
+        "value": round(d_gbs_evt, 1), "unit": "GB/s", "workload": DECODE,
+        "us_per_call": round(float(d_ms.mean()) * 1e3, 2), "gbs_wall": round(d_gbs_wall, 1),
+        "roofline": {"bound": "hbm", "achieved": round(d_gbs_evt, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(d_gbs_evt / PEAK_HBM_GBS, 4),
+                     "traffic": d_traffic, "bytes_per_call": d_bytes,
+                     "scope": "whole call: prepass + split + merge kernels"},
+    }
+
+    result = {
+        "metric": METRIC,
+        "value": round(p_tflops_wall, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round((t_prefill + t_decode) * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{PREFILL} + {DECODE}", "batch": len(pspec.seqlens),
+                   "seq_len": pspec.seqlens[0], "num_heads_q": pspec.num_heads_q,
+                   "num_heads_kv": pspec.num_heads_kv, "head_dim": pspec.head_dim,
+                   "block_size": pspec.block_size, "topk": pspec.topk, "causal": True,
+                   "selected_pairs": pairs, "flops_per_call": flops,
+                   "decode_bytes_per_call": d_bytes},
+        "roofline": roofline,
+        "decode": decode_obj,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(pd, pspec, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(pd, pspec, budget_s):
+    """The fp64 oracle on a seeded sample of the prefill workload's tokens."""
+    import numpy as np
+
+    import oracle
+    from top_block_sparse_amd import inputs
+
+    G = pspec.num_heads_q // pspec.num_heads_kv
+    cu = pd["cu_seqlens_q"].numpy()
+    blk = pd["blk_idx"].numpy()
+    rng = np.random.default_rng(1234)
+    total = int(cu[-1])
+
+    def flops_of(tokens):
+        # selected pairs of the sampled tokens, priced like the GPU figure
+        n = 0
+        for s in range(len(cu) - 1):
+            sel = tokens[(tokens >= cu[s]) & (tokens < cu[s + 1])]
+            if sel.size == 0:
+                continue
+            sub = blk[sel]
+            local = sel - cu[s]
+            ok = (sub >= 0) & (sub * pspec.block_size <= local[:, None, None])
+            srt = np.sort(np.where(ok, sub, -1), axis=2)
+            first = np.concatenate([np.ones(srt.shape[:2] + (1,), bool),
+                                    srt[:, :, 1:] != srt[:, :, :-1]], axis=2)
+            n += int(((srt >= 0) & first).sum())
+        return 4.0 * pspec.head_dim * pspec.block_size * G * n
+
+    oracle.build(force=False)
+    probe = np.sort(rng.choice(total, 64, replace=False))
+    t0 = time.perf_counter()
+    oracle.selected_attn_fwd(pd["q"], pd["k"], pd["v"], pd["blk_idx"], pd["cu_seqlens_q"],
+                             pd["cu_seqlens_k"], pspec.block_size, tokens=probe)
+    dt = max(time.perf_counter() - t0, 1e-3)
+    n = int(min(total, max(64, 64 * budget_s / dt)))
+    toks = np.sort(rng.choice(total, n, replace=False))
+    log(f"cpu baseline: oracle on {n} sampled tokens ({oracle.max_threads()} threads)")
+    t0 = time.perf_counter()
+    oracle.selected_attn_fwd(pd["q"], pd["k"], pd["v"], pd["blk_idx"], pd["cu_seqlens_q"],
+                             pd["cu_seqlens_k"], pspec.block_size, tokens=toks)
+    dt = time.perf_counter() - t0
+    fl = flops_of(toks)
+    _ = inputs
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"{n} of {total} query tokens of {PREFILL} (all 32 heads each), "
+                      f"{dt:.1f} s, fp64"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * fsa.h -- C ABI of libfsa: top-k selected block-sparse flash attention
+ * (prefill forward) and top-k gathered paged-KV decode for AMD MI355X
+ * (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor arguments are DEVICE pointers into memory the caller owns and
+ *   keeps alive until the enqueued work has finished.  The library never
+ *   allocates, frees or synchronises; it enqueues kernels on `stream`
+ *   (a hipStream_t passed as void*, NULL = the default stream) and returns.
+ *   FSA_SUCCESS therefore means "validated and enqueued".
+ * - bf16 tensors are IEEE bfloat16 bit patterns, row-major, innermost
+ *   dimension contiguous, with exactly the shapes given below (no strides).
+ * - Argument errors (null pointer, bad size, unsupported shape, workspace too
+ *   small) are detected on the host before anything is enqueued and before
+ *   any device memory is written.
+ * - Index CONTENTS never produce an error or a fault.  Block ids, token
+ *   positions and page ids that point outside the valid range are skipped,
+ *   and a repeated id counts once (the lists are sets).  A query row that
+ *   ends up with no visible key gets O = 0 and LSE = -inf.
+ * - softmax_scale <= 0 selects the default 1/sqrt(head_dim).
+ * - Calls are thread-safe: there is no global mutable state.
+ *
+ * Semantics follow the pages this library is built from:
+ * - GQA: query head h reads kv head h / (num_heads_q / num_heads_kv);
+ *   num_heads_q must be a multiple of num_heads_kv (flash-attention-npu page,
+ *   flash_attn_func docstring, MQA/GQA paragraph with the 6/2-head example).
+ * - Causal masking is aligned to the bottom-right corner: row i of a sequence
+ *   with S_q queries and S_k keys sees key j iff j <= i + S_k - S_q; an
+ *   all-masked row outputs zeros (same docstring, causal paragraph and its
+ *   2x5 / 5x2 examples).
+ * - LSE is the natural-log logsumexp of the scaled scores of each row, stored
+ *   fp32 with layout (num_heads_q, total_q) for the varlen prefill
+ *   (flash_attn_varlen_func docstring, softmax_lse) and (batch, num_heads_q)
+ *   for decode.
+ * - Selected attention: each (query token, kv head) carries a list of topk
+ *   key-block ids (blocks of block_size consecutive keys of its sequence);
+ *   its G query heads attend to the keys of those blocks only (FSA page:
+ *   NSA selected attention with block_size / topk; the Ascend SFA blog:
+ *   gather the selected K/V rows, then ordinary attention, -1 = invalid).
+ */
+#ifndef FSA_H_
+#define FSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FSA_ABI_VERSION 1
+
+typedef enum {
+    FSA_SUCCESS = 0,
+    FSA_ERROR_INVALID_VALUE = 1,  /* null pointer, negative or inconsistent size */
+    FSA_ERROR_NOT_SUPPORTED = 2,  /* shape outside what the kernels are built for */
+    FSA_ERROR_WORKSPACE = 3,      /* workspace missing or smaller than required */
+    FSA_ERROR_LAUNCH = 4          /* a kernel launch was rejected by the HIP runtime */
+} fsa_status_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fsa_status_string(fsa_status_t status);
+
+/* FSA_ABI_VERSION of the built library. */
+int32_t fsa_abi_version(void);
+
+/*
+ * Bytes of device workspace fsa_selected_attn_fwd needs for these arguments
+ * (0 when no workspace is needed).  num_splits = 0 prices the automatic
+ * choice.  Returns 0 as well for arguments fsa_selected_attn_fwd would reject.
+ */
+size_t fsa_selected_attn_fwd_workspace_size(int32_t batch, int64_t total_q,
+                                             int32_t max_seqlen_q, int32_t num_heads_q,
+                                             int32_t num_heads_kv, int32_t head_dim,
+                                             int32_t block_size, int32_t topk,
+                                             int32_t num_splits);
+
+/*
+ * Selected block-sparse attention forward (prefill), varlen layout.
+ *
+ *   q        bf16 [total_q, num_heads_q, head_dim]
+ *   k, v     bf16 [total_k, num_heads_kv, head_dim]
+ *   blk_idx  int32 [total_q, num_heads_kv, topk]: key-block ids of the token's
+ *            sequence, block b = keys [b*block_size, (b+1)*block_size); any
+ *            order; -1 (or any id outside [0, ceil(S_k/block_size))) = unused
+ *   cu_seqlens_q, cu_seqlens_k  int32 [batch + 1] prefix sums of the per-
+ *            sequence lengths (they may be the same pointer); must be non-
+ *            decreasing with cu_seqlens_q[batch] <= total_q and
+ *            cu_seqlens_k[batch] <= total_k (rows past those are not touched)
+ *   max_seqlen_q  >= every S_q; max_seqlen_k >= every S_k
+ *   head_dim 64 or 128; block_size 64; 1 <= topk <= 64;
+ *   num_heads_q / num_heads_kv <= 256
+ *   causal   nonzero: bottom-right causal mask; zero: no mask
+ *   num_splits  0 = automatic; n >= 1 splits every tile's selected-block set
+ *            into n parts computed by separate workgroups and merged by
+ *            logsumexp (needs workspace when n > 1); at most 16
+ *   workspace, workspace_bytes  device scratch of at least
+ *            fsa_selected_attn_fwd_workspace_size(...) bytes (may be NULL when
+ *            that size is 0); contents on entry are ignored
+ *   out      bf16 [total_q, num_heads_q, head_dim]
+ *   lse      fp32 [num_heads_q, total_q], or NULL to skip it
+ */
+fsa_status_t fsa_selected_attn_fwd(const void* q, const void* k, const void* v,
+                                   const int32_t* blk_idx, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k, int32_t batch, int64_t total_q,
+                                   int64_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                   int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                   int32_t block_size, int32_t topk, float softmax_scale,
+                                   int32_t causal, int32_t num_splits, void* workspace,
+                                   size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * Bytes of device workspace fsa_topk_decode needs (never 0 for valid
+ * arguments: the normalised index lists live there).  num_splits = 0 prices
+ * the automatic choice.  Returns 0 for arguments fsa_topk_decode rejects.
+ */
+size_t fsa_topk_decode_workspace_size(int32_t batch, int32_t num_heads_q, int32_t num_heads_kv,
+                                      int32_t head_dim, int32_t topk, int32_t num_splits);
+
+/* The split count fsa_topk_decode uses for num_splits = 0. */
+int32_t fsa_topk_decode_auto_splits(int32_t batch, int32_t num_heads_kv, int32_t topk);
+
+/*
+ * Top-k gathered decode over a paged KV cache: one query token per sequence
+ * attends to the cache positions listed for its kv head.
+ *
+ *   q          bf16 [batch, num_heads_q, head_dim]
+ *   k_cache, v_cache  bf16 [num_pages, page_size, num_heads_kv, head_dim]
+ *   tok_idx    int32 [batch, num_heads_kv, topk]: logical cache positions,
+ *              any order; entries outside [0, cache_seqlens[b]) are skipped,
+ *              repeats count once
+ *   block_table int32 [batch, max_pages_per_seq]: position t of sequence b is
+ *              row t % page_size of page block_table[b][t / page_size]; a
+ *              position whose page slot is >= max_pages_per_seq or whose page
+ *              id is outside [0, num_pages) is skipped
+ *   cache_seqlens int32 [batch]
+ *   head_dim 64 or 128; 1 <= topk <= 8192; num_heads_q / num_heads_kv <= 16;
+ *   num_pages * page_size < 2^31
+ *   num_splits 0 = automatic (fsa_topk_decode_auto_splits), else 1..64: each
+ *              (sequence, kv head) list is cut into that many parts whose
+ *              partial results are merged by logsumexp
+ *   workspace  at least fsa_topk_decode_workspace_size(...) bytes
+ *   out        bf16 [batch, num_heads_q, head_dim]
+ *   lse        fp32 [batch, num_heads_q], or NULL
+ * The query sits after every cache position, so the bottom-right causal rule
+ * leaves every listed position t < cache_seqlens[b] visible.
+ */
+fsa_status_t fsa_topk_decode(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* tok_idx, const int32_t* block_table,
+                             const int32_t* cache_seqlens, int32_t batch, int32_t num_heads_q,
+                             int32_t num_heads_kv, int32_t head_dim, int32_t page_size,
+                             int32_t max_pages_per_seq, int32_t num_pages, int32_t topk,
+                             float softmax_scale, int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSA_H_ */

@@ -1,0 +1,150 @@
+"""libfsa loads, exports what include/fsa.h declares, and rejects bad arguments
+on the host before anything reaches the GPU (no compute calls here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from top_block_sparse_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fsa.h")
+
+INVALID, NOT_SUPPORTED, WORKSPACE = 1, 2, 3
+FAKE = 0x10000          # an aligned, never-dereferenced stand-in for a device pointer
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fsa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from top_block_sparse_amd.build import build_library
+        build_library()
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 7
+    assert sorted(names) == sorted(_lib.EXPORTS)
+    nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fsa_\w+)", nm))
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_version_and_status_strings(lib):
+    assert lib.fsa_abi_version() == 1
+    for code, name in _lib._STATUS.items():
+        assert lib.fsa_status_string(code).decode() == name
+    assert lib.fsa_status_string(99).decode() == "FSA_ERROR_UNKNOWN"
+
+
+def prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, blk=FAKE, cuq=FAKE, cuk=FAKE, batch=2, total_q=100,
+             total_k=100, msq=50, msk=50, hq=8, hkv=2, d=128, bs=64, topk=16, scale=0.0,
+             causal=1, splits=1, ws=None, ws_bytes=0, out=FAKE, lse=None, stream=None)
+    a.update(kw)
+    return lib.fsa_selected_attn_fwd(a["q"], a["k"], a["v"], a["blk"], a["cuq"], a["cuk"],
+                                     a["batch"], a["total_q"], a["total_k"], a["msq"], a["msk"],
+                                     a["hq"], a["hkv"], a["d"], a["bs"], a["topk"], a["scale"],
+                                     a["causal"], a["splits"], a["ws"], a["ws_bytes"], a["out"],
+                                     a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=6, hkv=4), INVALID),            # query heads not a multiple of kv heads
+    (dict(d=96), NOT_SUPPORTED),
+    (dict(bs=32), NOT_SUPPORTED),
+    (dict(topk=0), INVALID),
+    (dict(topk=65), NOT_SUPPORTED),
+    (dict(hq=512, hkv=1), NOT_SUPPORTED),     # GQA group above 256
+    (dict(splits=17), NOT_SUPPORTED),
+    (dict(splits=-1), INVALID),
+    (dict(batch=-1), INVALID),
+    (dict(total_q=-5), INVALID),
+    (dict(q=None), INVALID),
+    (dict(blk=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(k=FAKE + 2), INVALID),              # not 16-byte aligned
+    (dict(splits=4), WORKSPACE),              # split partials need workspace
+    (dict(splits=4, ws=FAKE, ws_bytes=16), WORKSPACE),
+])
+def test_prefill_argument_errors(lib, kw, code):
+    assert prefill(lib, **kw) == code
+
+
+def test_prefill_nothing_to_do_is_success(lib):
+    # nothing is launched for an empty problem, even with null tensors
+    assert prefill(lib, batch=0, q=None, k=None, v=None, out=None) == 0
+    assert prefill(lib, total_q=0, msq=0, q=None, out=None) == 0
+
+
+def test_prefill_workspace_sizes(lib):
+    f = lib.fsa_selected_attn_fwd_workspace_size
+    assert f(2, 16384, 8192, 32, 8, 128, 64, 16, 1) == 0
+    want = 4 * 16384 * 32 * 128 * 4 + 4 * 16384 * 32 * 4
+    assert f(2, 16384, 8192, 32, 8, 128, 64, 16, 4) == want
+    assert f(1, 1024, 1024, 4, 1, 64, 64, 4, 0) > 0          # tiny grid -> automatic splits
+    assert f(2, 16384, 8192, 32, 8, 96, 64, 16, 1) == 0       # rejected shape
+
+
+def decode(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, tok=FAKE, bt=FAKE, cs=FAKE, batch=4, hq=8, hkv=2, d=128,
+             page=256, maxp=8, npages=32, topk=100, scale=0.0, splits=0, ws=FAKE,
+             ws_bytes=1 << 30, out=FAKE, lse=None, stream=None)
+    a.update(kw)
+    return lib.fsa_topk_decode(a["q"], a["kc"], a["vc"], a["tok"], a["bt"], a["cs"], a["batch"],
+                               a["hq"], a["hkv"], a["d"], a["page"], a["maxp"], a["npages"],
+                               a["topk"], a["scale"], a["splits"], a["ws"], a["ws_bytes"],
+                               a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=6, hkv=4), INVALID),
+    (dict(d=80), NOT_SUPPORTED),
+    (dict(topk=0), INVALID),
+    (dict(topk=8193), NOT_SUPPORTED),
+    (dict(hq=64, hkv=2), NOT_SUPPORTED),      # group above 16
+    (dict(splits=65), NOT_SUPPORTED),
+    (dict(page=0), INVALID),
+    (dict(npages=-1), INVALID),
+    (dict(npages=1 << 24, page=256), NOT_SUPPORTED),   # 2^32 cache rows
+    (dict(tok=None), INVALID),
+    (dict(bt=None), INVALID),
+    (dict(cs=None), INVALID),
+    (dict(vc=FAKE + 8), INVALID),
+    (dict(ws=None), WORKSPACE),
+    (dict(ws_bytes=100), WORKSPACE),
+    (dict(ws=FAKE + 16), WORKSPACE),          # workspace must be 256-byte aligned
+])
+def test_decode_argument_errors(lib, kw, code):
+    assert decode(lib, **kw) == code
+
+
+def test_decode_workspace_and_splits(lib):
+    assert lib.fsa_topk_decode_auto_splits(32, 8, 2048) >= 1
+    s = lib.fsa_topk_decode_auto_splits(32, 8, 2048)
+    ws = lib.fsa_topk_decode_workspace_size(32, 32, 8, 128, 2048, 0)
+    assert ws == lib.fsa_topk_decode_workspace_size(32, 32, 8, 128, 2048, s)
+    assert ws >= 32 * 8 * 2048 * 4 + 32 * 8 * 4 + s * 4 * 32 * 32 * 129 * 4
+    assert lib.fsa_topk_decode_workspace_size(32, 32, 8, 128, 9000, 0) == 0
+    assert lib.fsa_topk_decode_auto_splits(1, 1, 10) == 1
+    assert decode(lib, batch=0, q=None) == 0
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load()

@@ -1,0 +1,345 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bars (fixed by the benchmark spec of the workloads): O max-abs <= 2e-2 and
+mean-abs <= 2e-3 against the oracle; LSE abs <= 1e-3; which rows are empty
+(LSE = -inf, O = 0) must match exactly; with q = 0 every visible key scores
+the same, so LSE = ln|J| and the visible set is checked to 1e-5.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import top_block_sparse_amd as fsa
+from top_block_sparse_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+O_MAX, O_MEAN, LSE_TOL = 2e-2, 2e-3, 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    fsa._lib.load()
+    yield
+
+
+DEV = "cuda:0"
+
+
+def to_dev(d, keys):
+    return {k: d[k].to(DEV) for k in keys}
+
+
+def run_prefill(d, num_splits=0, causal=True, lse=True):
+    g = to_dev(d, ("q", "k", "v", "blk_idx", "cu_seqlens_q", "cu_seqlens_k"))
+    out, l = fsa.fsa_selected_attn_fwd(g["q"], g["k"], g["v"], g["blk_idx"], g["cu_seqlens_q"],
+                                       g["cu_seqlens_k"], d["max_seqlen_q"], d["max_seqlen_k"],
+                                       causal=causal, num_splits=num_splits, return_lse=lse)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), (None if l is None else l.cpu().numpy())
+
+
+def compare(out, lse_hq_tok, ro, rl, tokens=None, what=""):
+    if tokens is not None:
+        out = out[tokens]
+        lse_hq_tok = lse_hq_tok[:, tokens] if lse_hq_tok is not None else None
+    assert np.isfinite(out).all(), what
+    err = np.abs(out - ro)
+    assert err.max() <= O_MAX, f"{what} max|dO|={err.max():.3e}"
+    assert err.mean() <= O_MEAN, f"{what} mean|dO|={err.mean():.3e}"
+    if lse_hq_tok is not None:
+        lse = lse_hq_tok.T
+        fin = np.isfinite(rl)
+        assert np.array_equal(fin, np.isfinite(lse)), f"{what} empty-row pattern differs"
+        assert np.all(lse[~fin] == -np.inf), what
+        assert np.all(out[~fin] == 0.0), f"{what} empty rows must be zero"
+        if fin.any():
+            le = np.abs(lse[fin] - rl[fin])
+            assert le.max() <= LSE_TOL, f"{what} max|dLSE|={le.max():.3e}"
+
+
+def mutate_lists(blk, cu_q, cu_k, bs, rng, frac=0.25):
+    """Shuffle every list and overwrite some slots with repeats, -1, negative,
+    past-the-end and future-block ids (the same lists go to both sides)."""
+    b = rng.permuted(blk, axis=2).copy()
+    T, H, K = b.shape
+    for s in range(len(cu_q) - 1):
+        sq, sk = cu_q[s + 1] - cu_q[s], cu_k[s + 1] - cu_k[s]
+        nblk = -(-sk // bs)
+        for t in range(cu_q[s], cu_q[s + 1]):
+            i = t - cu_q[s]
+            qb = (i + sk - sq) // bs
+            for h in range(H):
+                for slot in range(K):
+                    if rng.random() >= frac:
+                        continue
+                    kind = rng.integers(5)
+                    if kind == 0 and K > 1:
+                        b[t, h, slot] = b[t, h, rng.integers(K)]          # repeat
+                    elif kind == 1:
+                        b[t, h, slot] = -1
+                    elif kind == 2:
+                        b[t, h, slot] = -int(rng.integers(2, 1000))
+                    elif kind == 3:
+                        b[t, h, slot] = nblk + int(rng.integers(0, 5))     # past the last block
+                    elif qb + 1 < nblk:
+                        b[t, h, slot] = int(rng.integers(qb + 1, nblk))    # causally future
+    return b
+
+
+def make_case(seqlens, hq, hkv, d, topk, seed, seqlens_k=None, mutate=True, zero_q=False):
+    spec = inputs.PrefillSpec("t", tuple(seqlens), hq, hkv, d, topk, seed=seed,
+                              seqlens_k=None if seqlens_k is None else tuple(seqlens_k))
+    dd = inputs.make_prefill(spec)
+    if mutate:
+        rng = np.random.default_rng(seed)
+        dd["blk_idx"] = torch.from_numpy(mutate_lists(dd["blk_idx"].numpy(),
+                                                      dd["cu_seqlens_q"].numpy(),
+                                                      dd["cu_seqlens_k"].numpy(), 64, rng))
+    if zero_q:
+        dd["q"] = torch.zeros_like(dd["q"])
+    return dd
+
+
+def oracle_prefill(dd, tokens=None, causal=True):
+    return oracle.selected_attn_fwd(dd["q"], dd["k"], dd["v"], dd["blk_idx"], dd["cu_seqlens_q"],
+                                    dd["cu_seqlens_k"], 64, causal=causal, tokens=tokens)
+
+
+# ------------------------------------------------------------------ prefill
+
+def test_prefill_small_workload_every_row():
+    spec = inputs.PREFILL_WORKLOADS["prefill_s1024_h4_kv1_d64_top4"]
+    dd = inputs.make_prefill(spec)
+    out, lse = run_prefill(dd)
+    ro, rl = oracle_prefill(dd)
+    compare(out, lse, ro, rl, what=spec.name)
+
+
+SHAPES = [
+    # seqlens, hq, hkv, d, topk, seqlens_k
+    ((700,), 4, 1, 64, 4, None),
+    ((1000, 333), 8, 2, 128, 8, None),
+    ((257, 64, 1, 900), 4, 4, 128, 16, None),          # G = 1, ragged, one-token sequence
+    ((640,), 6, 2, 128, 5, None),                      # G = 3: m-tiles straddle tokens
+    ((500,), 16, 2, 64, 7, None),                      # G = 8
+    ((450,), 16, 1, 128, 12, None),                    # G = 16
+    ((300,), 64, 2, 128, 9, None),                     # G = 32
+    ((200, 90), 8, 2, 128, 6, (520, 91)),              # S_q < S_k (bottom-right offset)
+    ((130, 400), 4, 1, 64, 3, (70, 400)),              # S_q > S_k: leading rows see nothing
+    ((2100,), 8, 2, 128, 64, None),                    # largest topk
+    ((0, 300, 0), 4, 2, 64, 5, None),                  # empty sequences around a real one
+]
+
+
+@pytest.mark.parametrize("case", SHAPES, ids=lambda c: f"s{c[0]}_h{c[1]}_kv{c[2]}_d{c[3]}_k{c[4]}")
+def test_prefill_random_shapes_with_index_edge_cases(case):
+    seqlens, hq, hkv, d, topk, sk = case
+    dd = make_case(seqlens, hq, hkv, d, topk, seed=sum(seqlens) + hq + d, seqlens_k=sk)
+    out, lse = run_prefill(dd)
+    ro, rl = oracle_prefill(dd)
+    compare(out, lse, ro, rl, what=str(case))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_causal_flag(causal):
+    dd = make_case((333, 129), 8, 2, 128, 6, seed=77, seqlens_k=(400, 129))
+    out, lse = run_prefill(dd, causal=causal)
+    ro, rl = oracle_prefill(dd, causal=causal)
+    compare(out, lse, ro, rl, what=f"causal={causal}")
+
+
+@pytest.mark.parametrize("case", [((1000, 200), 8, 2, 128, 16), ((777,), 4, 4, 64, 9),
+                                  ((500,), 32, 2, 128, 12)])
+def test_prefill_visible_set_exact(case):
+    """q = 0: LSE = ln|J| exactly; the GPU must keep exactly the oracle's key set."""
+    seqlens, hq, hkv, d, topk = case
+    dd = make_case(seqlens, hq, hkv, d, topk, seed=5, zero_q=True)
+    out, lse = run_prefill(dd)
+    ro, rl = oracle_prefill(dd)
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(lse.T))
+    assert np.abs(lse.T[fin] - rl[fin]).max() <= 1e-5
+    compare(out, lse, ro, rl)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 16])
+def test_prefill_split_k_matches(splits):
+    dd = make_case((1500, 300), 8, 2, 128, 16, seed=splits)
+    out, lse = run_prefill(dd, num_splits=splits)
+    ro, rl = oracle_prefill(dd)
+    compare(out, lse, ro, rl, what=f"splits={splits}")
+
+
+def test_prefill_without_lse_output():
+    dd = make_case((400,), 8, 2, 128, 8, seed=3)
+    out, lse = run_prefill(dd, lse=False)
+    assert lse is None
+    ro, rl = oracle_prefill(dd)
+    compare(out, None, ro, rl)
+
+
+def test_prefill_all_lists_empty():
+    dd = make_case((300, 50), 4, 2, 64, 4, seed=4, mutate=False)
+    dd["blk_idx"] = torch.full_like(dd["blk_idx"], -1)
+    out, lse = run_prefill(dd)
+    assert np.all(out == 0.0) and np.all(lse == -np.inf)
+
+
+def test_prefill_zero_batch():
+    q = torch.zeros((0, 4, 64), dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros((0, 1, 64), dtype=torch.bfloat16, device=DEV)
+    blk = torch.zeros((0, 1, 4), dtype=torch.int32, device=DEV)
+    cu = torch.zeros((1,), dtype=torch.int32, device=DEV)
+    out, lse = fsa.fsa_selected_attn_fwd(q, k, k, blk, cu, cu, 0, 0)
+    assert out.shape == (0, 4, 64) and lse.shape == (4, 0)
+
+
+def sample_tokens(cu_q, n, seed):
+    """Spread over every sequence: its first and last tokens, tile edges, random rest."""
+    rng = np.random.default_rng(seed)
+    toks = set()
+    for s in range(len(cu_q) - 1):
+        a, b = int(cu_q[s]), int(cu_q[s + 1])
+        if b > a:
+            toks.update([a, b - 1, a + 63 if a + 63 < b else a, a + 64 if a + 64 < b else a])
+    total = int(cu_q[-1])
+    toks.update(rng.choice(total, size=min(n, total), replace=False).tolist())
+    return np.array(sorted(toks), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name,nsample", [
+    ("prefill_b2_s8192_h32_kv8_d128_top16", 768),
+    ("varlen_65536+32768_h4_kv4_d128_top16", 2048),
+    ("long_s131072_h64_kv4_d128_top32_zipf", 192),
+])
+def test_prefill_full_size_workloads_sampled(name, nsample):
+    """Full-size workload in the benchmark's launch configuration (automatic
+    splits); sampled rows against the oracle, every row finite."""
+    spec = inputs.PREFILL_WORKLOADS[name]
+    print(f"[gpu] {name}: generating inputs", flush=True)
+    dd = inputs.make_prefill(spec)
+    print(f"[gpu] {name}: running HIP path", flush=True)
+    g = to_dev(dd, ("q", "k", "v", "blk_idx", "cu_seqlens_q", "cu_seqlens_k"))
+    out, lse = fsa.fsa_selected_attn_fwd(g["q"], g["k"], g["v"], g["blk_idx"], g["cu_seqlens_q"],
+                                         g["cu_seqlens_k"], dd["max_seqlen_q"], dd["max_seqlen_k"])
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    toks = sample_tokens(dd["cu_seqlens_q"].numpy(), nsample, seed=len(name))
+    o = out[torch.from_numpy(toks).to(DEV)].float().cpu().numpy()
+    l = lse[:, torch.from_numpy(toks).to(DEV)].cpu().numpy()
+    del out, lse, g
+    print(f"[gpu] {name}: oracle on {toks.size} tokens", flush=True)
+    ro, rl = oracle_prefill(dd, tokens=toks)
+    compare(o, l, ro, rl, what=name)
+
+
+# ------------------------------------------------------------------ decode
+
+def run_decode(dd, tok=None, num_splits=0, lse=True, cache_seqlens=None, block_table=None):
+    tok = dd["tok_idx"] if tok is None else tok
+    cs = dd["cache_seqlens"] if cache_seqlens is None else cache_seqlens
+    bt = dd["block_table"] if block_table is None else block_table
+    o, l = fsa.fsa_topk_decode(dd["q"].to(DEV), dd["k_cache"].to(DEV), dd["v_cache"].to(DEV),
+                               tok.to(DEV), bt.to(DEV), cs.to(DEV), num_splits=num_splits,
+                               return_lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.topk_decode(dd["q"], dd["k_cache"], dd["v_cache"], tok, bt, cs)
+    return o.float().cpu().numpy(), (None if l is None else l.cpu().numpy()), ro, rl
+
+
+def compare_decode(o, l, ro, rl, what=""):
+    assert np.isfinite(o).all(), what
+    err = np.abs(o - ro)
+    assert err.max() <= O_MAX, f"{what} max|dO|={err.max():.3e}"
+    assert err.mean() <= O_MEAN, f"{what} mean|dO|={err.mean():.3e}"
+    if l is not None:
+        fin = np.isfinite(rl)
+        assert np.array_equal(fin, np.isfinite(l)), what
+        assert np.all(l[~fin] == -np.inf) and np.all(o[~fin] == 0.0), what
+        if fin.any():
+            assert np.abs(l[fin] - rl[fin]).max() <= LSE_TOL, what
+
+
+def mutate_tok(tok, rng, L):
+    t = tok.numpy().copy()
+    B, H, K = t.shape
+    m = rng.random(t.shape)
+    t[m < 0.05] = -1
+    t[(m >= 0.05) & (m < 0.08)] = L + 7
+    t[(m >= 0.08) & (m < 0.10)] = -12345
+    rep = (m >= 0.10) & (m < 0.15)
+    src = rng.integers(0, K, size=t.shape)
+    t[rep] = np.take_along_axis(t, src, axis=2)[rep]
+    return torch.from_numpy(t)
+
+
+DECODE_SHAPES = [
+    # batch, hq, hkv, d, cache_len, page, topk
+    (3, 8, 2, 128, 1000, 64, 300),
+    (2, 4, 4, 64, 513, 16, 77),        # G = 1, partial last page
+    (4, 16, 1, 128, 3000, 256, 1024),  # G = 16
+    (2, 6, 2, 64, 700, 100, 200),      # G = 3, page size not a power of two
+    (5, 32, 8, 128, 2048, 256, 2048),
+    (1, 8, 1, 128, 9000, 512, 8192),   # largest topk
+]
+
+
+@pytest.mark.parametrize("case", DECODE_SHAPES, ids=lambda c: "_".join(map(str, c)))
+def test_decode_shapes_with_index_edge_cases(case):
+    batch, hq, hkv, d, L, P, topk = case
+    spec = inputs.DecodeSpec("t", batch, hq, hkv, d, L, P, topk, recent=min(64, topk), seed=L + P)
+    dd = inputs.make_decode(spec)
+    rng = np.random.default_rng(L)
+    tok = mutate_tok(dd["tok_idx"], rng, L)
+    cs = dd["cache_seqlens"].clone()
+    cs[0] = L // 2 + 1                       # shorter cache for the first sequence
+    if batch > 2:
+        cs[2] = 0                            # an empty cache
+    bt = dd["block_table"].clone()
+    if bt.shape[1] > 2:
+        bt[-1, 1] = -3                       # an invalid page id
+        bt[-1, 2] = 10 ** 6
+    o, l, ro, rl = run_decode(dd, tok=tok, cache_seqlens=cs, block_table=bt)
+    compare_decode(o, l, ro, rl, what=str(case))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5, 64])
+def test_decode_split_counts_match(splits):
+    spec = inputs.DecodeSpec("t", 3, 8, 2, 128, 4000, 256, 1500, seed=splits)
+    dd = inputs.make_decode(spec)
+    o, l, ro, rl = run_decode(dd, num_splits=splits)
+    compare_decode(o, l, ro, rl, what=f"splits={splits}")
+
+
+def test_decode_visible_set_exact():
+    spec = inputs.DecodeSpec("t", 4, 8, 2, 128, 2500, 128, 900, seed=11)
+    dd = inputs.make_decode(spec)
+    dd["q"] = torch.zeros_like(dd["q"])
+    tok = mutate_tok(dd["tok_idx"], np.random.default_rng(1), 2500)
+    o, l, ro, rl = run_decode(dd, tok=tok)
+    assert np.abs(l - rl).max() <= 1e-5
+    compare_decode(o, l, ro, rl)
+
+
+def test_decode_without_lse_output():
+    spec = inputs.DecodeSpec("t", 2, 8, 2, 128, 600, 64, 200, seed=12)
+    dd = inputs.make_decode(spec)
+    o, l, ro, rl = run_decode(dd, lse=False)
+    assert l is None
+    compare_decode(o, None, ro, rl)
+
+
+def test_decode_full_size_workload():
+    """The decode workload at full size, every (sequence, head) against the oracle."""
+    spec = inputs.DECODE_WORKLOADS["decode_b32_h32_kv8_d128_L32768_p256_top2048"]
+    print("[gpu] decode workload: generating inputs", flush=True)
+    dd = inputs.make_decode(spec)
+    print("[gpu] decode workload: HIP path + oracle", flush=True)
+    o, l, ro, rl = run_decode(dd)
+    compare_decode(o, l, ro, rl, what=spec.name)

@@ -1,0 +1,25 @@
+"""top_block_sparse_amd: top-k selected block-sparse flash attention for MI355X.
+
+The compute lives in ``libfsa.so`` (HIP kernels for gfx950 behind the C ABI
+of ``include/fsa.h``); ``top_block_sparse_amd._lib`` is its ctypes binding
+and exports the same names.  ``top_block_sparse_amd.inputs`` holds the seeded
+synthetic input generators.  Importing the package loads nothing; the first
+call through the binding loads the library and raises if it is not built.
+"""
+
+from ._lib import (  # noqa: F401
+    FsaError,
+    fsa_abi_version,
+    fsa_selected_attn_fwd,
+    fsa_selected_attn_fwd_workspace_size,
+    fsa_status_string,
+    fsa_topk_decode,
+    fsa_topk_decode_auto_splits,
+    fsa_topk_decode_workspace_size,
+)
+
+__all__ = [
+    "FsaError", "fsa_abi_version", "fsa_selected_attn_fwd",
+    "fsa_selected_attn_fwd_workspace_size", "fsa_status_string", "fsa_topk_decode",
+    "fsa_topk_decode_auto_splits", "fsa_topk_decode_workspace_size",
+]

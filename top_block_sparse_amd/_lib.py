@@ -1,0 +1,207 @@
+"""ctypes binding of libfsa (include/fsa.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libfsa.so``.  PyTorch supplies device memory (outputs and
+workspace are allocated with ``torch.empty`` when the caller passes none) and
+the current HIP stream.  If the built library is missing, every call raises:
+there is no other implementation behind these names.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfsa.so")
+
+FSA_SUCCESS = 0
+_STATUS = {0: "FSA_SUCCESS", 1: "FSA_ERROR_INVALID_VALUE", 2: "FSA_ERROR_NOT_SUPPORTED",
+           3: "FSA_ERROR_WORKSPACE", 4: "FSA_ERROR_LAUNCH"}
+
+# Every symbol include/fsa.h declares.
+EXPORTS = ("fsa_status_string", "fsa_abi_version", "fsa_selected_attn_fwd_workspace_size",
+           "fsa_selected_attn_fwd", "fsa_topk_decode_workspace_size",
+           "fsa_topk_decode_auto_splits", "fsa_topk_decode")
+
+_lib = None
+
+
+class FsaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_STATUS.get(status, status)}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libfsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libfsa is not built ({LIB_PATH} missing); run "
+                           "`python -m top_block_sparse_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+    lib.fsa_status_string.restype = ctypes.c_char_p
+    lib.fsa_status_string.argtypes = [ctypes.c_int]
+    lib.fsa_abi_version.restype = i32
+    lib.fsa_abi_version.argtypes = []
+    lib.fsa_selected_attn_fwd_workspace_size.restype = sz
+    lib.fsa_selected_attn_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32, i32]
+    lib.fsa_selected_attn_fwd.restype = ctypes.c_int
+    lib.fsa_selected_attn_fwd.argtypes = [P, P, P, P, P, P, i32, i64, i64, i32, i32, i32, i32, i32,
+                                          i32, i32, f32, i32, i32, P, sz, P, P, P]
+    lib.fsa_topk_decode_workspace_size.restype = sz
+    lib.fsa_topk_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.fsa_topk_decode_auto_splits.restype = i32
+    lib.fsa_topk_decode_auto_splits.argtypes = [i32, i32, i32]
+    lib.fsa_topk_decode.restype = ctypes.c_int
+    lib.fsa_topk_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f32,
+                                    i32, P, sz, P, P, P]
+    _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _check_dev(name: str, t: torch.Tensor, dtype: torch.dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fsa_status_string(status: int) -> str:
+    return load().fsa_status_string(status).decode()
+
+
+def fsa_abi_version() -> int:
+    return int(load().fsa_abi_version())
+
+
+def fsa_selected_attn_fwd_workspace_size(batch: int, total_q: int, max_seqlen_q: int,
+                                         num_heads_q: int, num_heads_kv: int, head_dim: int,
+                                         block_size: int, topk: int, num_splits: int = 0) -> int:
+    return int(load().fsa_selected_attn_fwd_workspace_size(batch, total_q, max_seqlen_q,
+                                                            num_heads_q, num_heads_kv, head_dim,
+                                                            block_size, topk, num_splits))
+
+
+def fsa_topk_decode_workspace_size(batch: int, num_heads_q: int, num_heads_kv: int,
+                                   head_dim: int, topk: int, num_splits: int = 0) -> int:
+    return int(load().fsa_topk_decode_workspace_size(batch, num_heads_q, num_heads_kv, head_dim,
+                                                     topk, num_splits))
+
+
+def fsa_topk_decode_auto_splits(batch: int, num_heads_kv: int, topk: int) -> int:
+    return int(load().fsa_topk_decode_auto_splits(batch, num_heads_kv, topk))
+
+
+def fsa_selected_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          blk_idx: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                          cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                          block_size: int = 64, softmax_scale: Optional[float] = None,
+                          causal: bool = True, num_splits: int = 0,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, return_lse: bool = True
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Selected block-sparse attention forward; returns ``(out, lse)``.
+
+    Shapes as in include/fsa.h: q ``[total_q, Hq, d]``, k/v ``[total_k, Hkv, d]``
+    (bf16), blk_idx ``[total_q, Hkv, topk]`` and cu_seqlens int32, all on one GPU.
+    """
+    lib = load()
+    _check_dev("q", q, torch.bfloat16, 3)
+    _check_dev("k", k, torch.bfloat16, 3)
+    _check_dev("v", v, torch.bfloat16, 3)
+    _check_dev("blk_idx", blk_idx, torch.int32, 3)
+    _check_dev("cu_seqlens_q", cu_seqlens_q, torch.int32, 1)
+    _check_dev("cu_seqlens_k", cu_seqlens_k, torch.int32, 1)
+    total_q, hq, d = q.shape
+    total_k, hkv, _ = k.shape
+    topk = blk_idx.shape[2]
+    batch = cu_seqlens_q.numel() - 1
+    if tuple(v.shape) != tuple(k.shape) or k.shape[2] != d:
+        raise ValueError("k and v must both be [total_k, Hkv, d] with q's d")
+    if tuple(blk_idx.shape[:2]) != (total_q, hkv) or cu_seqlens_k.numel() != batch + 1:
+        raise ValueError("blk_idx must be [total_q, Hkv, topk]; cu_seqlens_k must match cu_seqlens_q")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, total_q), dtype=torch.float32, device=q.device)
+    need = lib.fsa_selected_attn_fwd_workspace_size(batch, total_q, max_seqlen_q, hq, hkv, d,
+                                                    block_size, topk, num_splits)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = lib.fsa_selected_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(blk_idx), _ptr(cu_seqlens_q),
+                                   _ptr(cu_seqlens_k), batch, total_q, total_k, max_seqlen_q,
+                                   max_seqlen_k, hq, hkv, d, block_size, topk, scale, int(causal),
+                                   num_splits, _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+                                   _stream(q.device))
+    if st != FSA_SUCCESS:
+        raise FsaError(st, "fsa_selected_attn_fwd")
+    return out, lse
+
+
+def fsa_topk_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    tok_idx: torch.Tensor, block_table: torch.Tensor, cache_seqlens: torch.Tensor,
+                    softmax_scale: Optional[float] = None, num_splits: int = 0,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, return_lse: bool = True
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Top-k gathered paged decode; returns ``(out [B,Hq,d], lse [B,Hq])``."""
+    lib = load()
+    _check_dev("q", q, torch.bfloat16, 3)
+    _check_dev("k_cache", k_cache, torch.bfloat16, 4)
+    _check_dev("v_cache", v_cache, torch.bfloat16, 4)
+    _check_dev("tok_idx", tok_idx, torch.int32, 3)
+    _check_dev("block_table", block_table, torch.int32, 2)
+    _check_dev("cache_seqlens", cache_seqlens, torch.int32, 1)
+    batch, hq, d = q.shape
+    num_pages, page_size, hkv, _ = k_cache.shape
+    topk = tok_idx.shape[2]
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[3] != d:
+        raise ValueError("k_cache and v_cache must both be [num_pages, page_size, Hkv, d]")
+    if tuple(tok_idx.shape[:2]) != (batch, hkv) or block_table.shape[0] != batch \
+            or cache_seqlens.numel() != batch:
+        raise ValueError("tok_idx [B,Hkv,topk], block_table [B,max_pages], cache_seqlens [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    need = lib.fsa_topk_decode_workspace_size(batch, hq, hkv, d, topk, num_splits)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = lib.fsa_topk_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(tok_idx),
+                             _ptr(block_table), _ptr(cache_seqlens), batch, hq, hkv, d, page_size,
+                             block_table.shape[1], num_pages, topk, scale, num_splits,
+                             _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(q.device))
+    if st != FSA_SUCCESS:
+        raise FsaError(st, "fsa_topk_decode")
+    return out, lse
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

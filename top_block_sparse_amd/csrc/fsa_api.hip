@@ -1,0 +1,314 @@
+// fsa_api.hip -- host side of libfsa: argument checks, planning, launches.
+//
+// The entry points are declared (with their contracts) in include/fsa.h.
+// Nothing here allocates, frees or synchronises device memory; every check
+// runs before the first launch so a rejected call leaves the device
+// untouched.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/fsa.h"
+#include "fsa_common.h"
+#include "fsa_params.h"
+
+namespace {
+
+constexpr int kMaxTopkPrefill = 64;
+constexpr int kMaxGroupPrefill = 256;
+constexpr int kMaxSplitsPrefill = 16;
+constexpr int kMaxTopkDecode = 8192;
+constexpr int kMaxGroupDecode = 16;
+constexpr int kMaxSplitsDecode = 64;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Prefill tiling: T tokens per workgroup so that T*G query rows fill at most
+// 16 MFMA m-tiles, and at most 64 tokens (one bit each in the block masks).
+struct PrefillPlan {
+    int T, mtiles, tiles_per_seq, splits, n_wg;
+};
+
+fsa_status_t check_prefill_shape(int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_t Hkv,
+                                 int32_t D, int32_t bs, int32_t topk, int32_t num_splits) {
+    if (batch < 0 || max_seqlen_q < 0 || Hq <= 0 || Hkv <= 0 || topk <= 0 || num_splits < 0)
+        return FSA_ERROR_INVALID_VALUE;
+    if (Hq % Hkv != 0) return FSA_ERROR_INVALID_VALUE;
+    if (D != 64 && D != 128) return FSA_ERROR_NOT_SUPPORTED;
+    if (bs != fsa::kBlockKeys) return FSA_ERROR_NOT_SUPPORTED;
+    if (topk > kMaxTopkPrefill) return FSA_ERROR_NOT_SUPPORTED;
+    if (Hq / Hkv > kMaxGroupPrefill) return FSA_ERROR_NOT_SUPPORTED;
+    if (num_splits > kMaxSplitsPrefill) return FSA_ERROR_NOT_SUPPORTED;
+    return FSA_SUCCESS;
+}
+
+PrefillPlan plan_prefill(int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_t Hkv,
+                         int32_t num_splits) {
+    PrefillPlan pl{};
+    const int G = Hq / Hkv;
+    int T = 256 / G;
+    if (T > 64) T = 64;
+    if (T < 1) T = 1;
+    pl.T = T;
+    pl.mtiles = (T * G + 15) / 16;
+    pl.tiles_per_seq = (max_seqlen_q + T - 1) / T;
+    const long long base = (long long)batch * pl.tiles_per_seq * Hkv;
+    int s = num_splits;
+    if (s == 0) {
+        // enough workgroups to cover 256 CUs a few times over
+        s = 1;
+        if (base > 0 && base < 1024) {
+            s = (int)((1024 + base - 1) / base);
+            if (s > 8) s = 8;
+        }
+    }
+    pl.splits = s;
+    pl.n_wg = (int)(base * s);
+    return pl;
+}
+
+int decode_auto_splits(int32_t batch, int32_t Hkv, int32_t topk) {
+    const long long units = (long long)batch * Hkv;
+    if (units <= 0) return 1;
+    const int waves = fsa::decode_waves_per_split();
+    long long s = (2048 + units * waves - 1) / (units * waves);
+    const long long cap = topk / (waves * 32) > 1 ? topk / (waves * 32) : 1;   // >= 32 rows per wave
+    if (s > cap) s = cap;
+    if (s > kMaxSplitsDecode) s = kMaxSplitsDecode;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+int next_pow2(int x) {
+    int n = 1;
+    while (n < x) n <<= 1;
+    return n;
+}
+
+fsa_status_t check_decode_shape(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int32_t topk,
+                                int32_t num_splits) {
+    if (batch < 0 || Hq <= 0 || Hkv <= 0 || topk <= 0 || num_splits < 0)
+        return FSA_ERROR_INVALID_VALUE;
+    if (Hq % Hkv != 0) return FSA_ERROR_INVALID_VALUE;
+    if (D != 64 && D != 128) return FSA_ERROR_NOT_SUPPORTED;
+    if (topk > kMaxTopkDecode) return FSA_ERROR_NOT_SUPPORTED;
+    if (Hq / Hkv > kMaxGroupDecode) return FSA_ERROR_NOT_SUPPORTED;
+    if (num_splits > kMaxSplitsDecode) return FSA_ERROR_NOT_SUPPORTED;
+    return FSA_SUCCESS;
+}
+
+struct DecodeLayout {
+    size_t rows, counts, part_o, part_lse, total;
+    int splits, nparts;
+};
+
+DecodeLayout decode_layout(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int32_t topk,
+                           int32_t num_splits) {
+    DecodeLayout l{};
+    l.splits = num_splits == 0 ? decode_auto_splits(batch, Hkv, topk) : num_splits;
+    l.nparts = l.splits * fsa::decode_waves_per_split();
+    size_t off = 0;
+    l.rows = off;
+    off = align_up(off + (size_t)batch * Hkv * topk * 4);
+    l.counts = off;
+    off = align_up(off + (size_t)batch * Hkv * 4);
+    l.part_o = off;
+    off = align_up(off + (size_t)l.nparts * batch * Hq * D * 4);
+    l.part_lse = off;
+    off = align_up(off + (size_t)l.nparts * batch * Hq * 4);
+    l.total = off;
+    return l;
+}
+
+float resolve_scale(float s, int D) { return s > 0.f ? s : 1.0f / std::sqrt((float)D); }
+
+}  // namespace
+
+extern "C" {
+
+const char* fsa_status_string(fsa_status_t status) {
+    switch (status) {
+        case FSA_SUCCESS: return "FSA_SUCCESS";
+        case FSA_ERROR_INVALID_VALUE: return "FSA_ERROR_INVALID_VALUE";
+        case FSA_ERROR_NOT_SUPPORTED: return "FSA_ERROR_NOT_SUPPORTED";
+        case FSA_ERROR_WORKSPACE: return "FSA_ERROR_WORKSPACE";
+        case FSA_ERROR_LAUNCH: return "FSA_ERROR_LAUNCH";
+    }
+    return "FSA_ERROR_UNKNOWN";
+}
+
+int32_t fsa_abi_version(void) { return FSA_ABI_VERSION; }
+
+size_t fsa_selected_attn_fwd_workspace_size(int32_t batch, int64_t total_q, int32_t max_seqlen_q,
+                                             int32_t num_heads_q, int32_t num_heads_kv,
+                                             int32_t head_dim, int32_t block_size, int32_t topk,
+                                             int32_t num_splits) {
+    if (total_q < 0) return 0;
+    if (check_prefill_shape(batch, max_seqlen_q, num_heads_q, num_heads_kv, head_dim, block_size,
+                            topk, num_splits) != FSA_SUCCESS)
+        return 0;
+    const PrefillPlan pl = plan_prefill(batch, max_seqlen_q, num_heads_q, num_heads_kv, num_splits);
+    if (pl.splits <= 1) return 0;
+    const size_t rows = (size_t)total_q * num_heads_q;
+    return align_up((size_t)pl.splits * rows * head_dim * 4) + align_up((size_t)pl.splits * rows * 4);
+}
+
+fsa_status_t fsa_selected_attn_fwd(const void* q, const void* k, const void* v,
+                                   const int32_t* blk_idx, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k, int32_t batch, int64_t total_q,
+                                   int64_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                   int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                   int32_t block_size, int32_t topk, float softmax_scale,
+                                   int32_t causal, int32_t num_splits, void* workspace,
+                                   size_t workspace_bytes, void* out, float* lse, void* stream) {
+    fsa_status_t st = check_prefill_shape(batch, max_seqlen_q, num_heads_q, num_heads_kv, head_dim,
+                                          block_size, topk, num_splits);
+    if (st != FSA_SUCCESS) return st;
+    if (total_q < 0 || total_k < 0 || max_seqlen_k < 0) return FSA_ERROR_INVALID_VALUE;
+    if (total_q > INT32_MAX || total_k > INT32_MAX) return FSA_ERROR_NOT_SUPPORTED;
+    if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FSA_SUCCESS;   // nothing to do
+    if (!q || !k || !v || !blk_idx || !cu_seqlens_q || !cu_seqlens_k || !out)
+        return FSA_ERROR_INVALID_VALUE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return FSA_ERROR_INVALID_VALUE;
+    const PrefillPlan pl = plan_prefill(batch, max_seqlen_q, num_heads_q, num_heads_kv, num_splits);
+    const size_t need = fsa_selected_attn_fwd_workspace_size(
+        batch, total_q, max_seqlen_q, num_heads_q, num_heads_kv, head_dim, block_size, topk,
+        num_splits);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+        return FSA_ERROR_WORKSPACE;
+    if (pl.n_wg <= 0) return FSA_SUCCESS;
+
+    fsa::SelFwdParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.blk_idx = blk_idx;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.out = static_cast<uint16_t*>(out);
+    p.lse = lse;
+    p.total_q = total_q;
+    p.total_k = total_k;
+    p.batch = batch;
+    p.Hq = num_heads_q;
+    p.Hkv = num_heads_kv;
+    p.G = num_heads_q / num_heads_kv;
+    p.topk = topk;
+    p.causal = causal ? 1 : 0;
+    p.num_splits = pl.splits;
+    p.T = pl.T;
+    p.mtiles = pl.mtiles;
+    p.tiles_per_seq = pl.tiles_per_seq;
+    p.n_wg = pl.n_wg;
+    p.scale_log2 = resolve_scale(softmax_scale, head_dim) * fsa::kLog2e;
+    const size_t rows = (size_t)total_q * num_heads_q;
+    if (pl.splits > 1) {
+        p.part_o = static_cast<float*>(workspace);
+        p.part_lse = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                              align_up((size_t)pl.splits * rows * head_dim * 4));
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    hipError_t e = head_dim == 64 ? fsa::launch_sel_attn_fwd<64>(p, s)
+                                  : fsa::launch_sel_attn_fwd<128>(p, s);
+    if (e != hipSuccess) return FSA_ERROR_LAUNCH;
+    if (pl.splits > 1) {
+        fsa::MergeParams m{};
+        m.part_o = p.part_o;
+        m.part_lse = p.part_lse;
+        m.out = p.out;
+        m.lse = lse;
+        m.nrows = (int64_t)rows;
+        m.nparts = pl.splits;
+        m.lse_mode = 0;
+        m.Hq = num_heads_q;
+        m.ntok = total_q;
+        m.ntok_live = cu_seqlens_q + batch;
+        e = fsa::launch_lse_merge(m, head_dim, s);
+        if (e != hipSuccess) return FSA_ERROR_LAUNCH;
+    }
+    return FSA_SUCCESS;
+}
+
+int32_t fsa_topk_decode_auto_splits(int32_t batch, int32_t num_heads_kv, int32_t topk) {
+    return decode_auto_splits(batch, num_heads_kv, topk);
+}
+
+size_t fsa_topk_decode_workspace_size(int32_t batch, int32_t num_heads_q, int32_t num_heads_kv,
+                                      int32_t head_dim, int32_t topk, int32_t num_splits) {
+    if (check_decode_shape(batch, num_heads_q, num_heads_kv, head_dim, topk, num_splits) !=
+        FSA_SUCCESS)
+        return 0;
+    return decode_layout(batch, num_heads_q, num_heads_kv, head_dim, topk, num_splits).total;
+}
+
+fsa_status_t fsa_topk_decode(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* tok_idx, const int32_t* block_table,
+                             const int32_t* cache_seqlens, int32_t batch, int32_t num_heads_q,
+                             int32_t num_heads_kv, int32_t head_dim, int32_t page_size,
+                             int32_t max_pages_per_seq, int32_t num_pages, int32_t topk,
+                             float softmax_scale, int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, void* out, float* lse, void* stream) {
+    fsa_status_t st = check_decode_shape(batch, num_heads_q, num_heads_kv, head_dim, topk,
+                                         num_splits);
+    if (st != FSA_SUCCESS) return st;
+    if (page_size <= 0 || max_pages_per_seq < 0 || num_pages < 0) return FSA_ERROR_INVALID_VALUE;
+    if ((int64_t)num_pages * page_size >= (int64_t)INT32_MAX) return FSA_ERROR_NOT_SUPPORTED;
+    if (batch == 0) return FSA_SUCCESS;
+    if (!q || !k_cache || !v_cache || !tok_idx || !block_table || !cache_seqlens || !out)
+        return FSA_ERROR_INVALID_VALUE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return FSA_ERROR_INVALID_VALUE;
+    const DecodeLayout lay = decode_layout(batch, num_heads_q, num_heads_kv, head_dim, topk,
+                                           num_splits);
+    if (workspace == nullptr || workspace_bytes < lay.total ||
+        (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return FSA_ERROR_WORKSPACE;
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    fsa::DecodeParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.kc = static_cast<const uint16_t*>(k_cache);
+    p.vc = static_cast<const uint16_t*>(v_cache);
+    p.tok_idx = tok_idx;
+    p.block_table = block_table;
+    p.cache_seqlens = cache_seqlens;
+    p.rows = reinterpret_cast<int32_t*>(ws + lay.rows);
+    p.counts = reinterpret_cast<int32_t*>(ws + lay.counts);
+    p.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+    p.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
+    p.batch = batch;
+    p.Hq = num_heads_q;
+    p.Hkv = num_heads_kv;
+    p.G = num_heads_q / num_heads_kv;
+    p.page_size = page_size;
+    p.max_pages = max_pages_per_seq;
+    p.num_pages = num_pages;
+    p.topk = topk;
+    p.splits = lay.splits;
+    p.sort_n = next_pow2(topk);
+    p.scale_log2 = resolve_scale(softmax_scale, head_dim) * fsa::kLog2e;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (fsa::launch_decode_prepass(p, s) != hipSuccess) return FSA_ERROR_LAUNCH;
+    if (fsa::launch_decode_split(p, head_dim, s) != hipSuccess) return FSA_ERROR_LAUNCH;
+    fsa::MergeParams m{};
+    m.part_o = p.part_o;
+    m.part_lse = p.part_lse;
+    m.out = static_cast<uint16_t*>(out);
+    m.lse = lse;
+    m.nrows = (int64_t)batch * num_heads_q;
+    m.nparts = lay.nparts;
+    m.lse_mode = 1;
+    m.Hq = num_heads_q;
+    m.ntok = batch;
+    if (fsa::launch_lse_merge(m, head_dim, s) != hipSuccess) return FSA_ERROR_LAUNCH;
+    return FSA_SUCCESS;
+}
+
+}  // extern "C"

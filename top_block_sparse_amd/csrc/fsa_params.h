@@ -1,0 +1,71 @@
+// fsa_params.h -- kernel parameter blocks and launcher declarations of libfsa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fsa {
+
+// Selected-attention prefill (sel_attn_fwd.hip).
+struct SelFwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* blk_idx;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    uint16_t* out;
+    float* lse;
+    float* part_o;      // [num_splits][total_q*Hq][D]   (num_splits > 1)
+    float* part_lse;    // [num_splits][total_q*Hq]
+    int64_t total_q;
+    int64_t total_k;
+    int batch, Hq, Hkv, G, topk, causal, num_splits;
+    int T;              // query tokens per tile (<= 64)
+    int mtiles;         // ceil(T*G/16) 16-row MFMA tiles per tile
+    int tiles_per_seq;
+    int n_wg;
+    float scale_log2;   // softmax_scale * log2(e)
+};
+
+// Top-k paged decode (topk_decode.hip).
+struct DecodeParams {
+    const uint16_t* q;
+    const uint16_t* kc;
+    const uint16_t* vc;
+    const int32_t* tok_idx;
+    const int32_t* block_table;
+    const int32_t* cache_seqlens;
+    int32_t* rows;          // workspace: [batch*Hkv][topk] physical cache rows
+    int32_t* counts;        // workspace: [batch*Hkv]
+    float* part_o;          // workspace: [nparts][batch*Hq][D]
+    float* part_lse;        // workspace: [nparts][batch*Hq]
+    int batch, Hq, Hkv, G, page_size, max_pages, num_pages, topk, splits;
+    int sort_n;             // power of two >= topk
+    float scale_log2;
+};
+
+// Logsumexp merge of split partials (lse_merge.hip).
+struct MergeParams {
+    const float* part_o;     // [nparts][nrows][D]
+    const float* part_lse;   // [nparts][nrows]
+    uint16_t* out;           // [nrows][D] bf16
+    float* lse;              // optional
+    int64_t nrows;
+    int nparts;
+    int lse_mode;            // 0: lse[(row % Hq) * ntok + row / Hq]; 1: lse[row]
+    int Hq;
+    int64_t ntok;
+    const int32_t* ntok_live;   // optional: rows of tokens >= *ntok_live are left untouched
+};
+
+template <int D>
+hipError_t launch_sel_attn_fwd(const SelFwdParams& p, hipStream_t stream);
+size_t sel_attn_fwd_lds_bytes(int D, int T, int topk);
+hipError_t launch_decode_prepass(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_split(const DecodeParams& p, int D, hipStream_t stream);
+int decode_waves_per_split();
+hipError_t launch_lse_merge(const MergeParams& p, int D, hipStream_t stream);
+
+}  // namespace fsa
