@@ -69,6 +69,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("full", "prefill", "decode", "copy"), default="full",
+                    help="profiling runs: launch only one kernel family (or a plain 1 GiB "
+                         "device copy used to calibrate HBM byte counters) --steps times, "
+                         "print timings, no JSON line")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -90,44 +94,57 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
 
-    # ---------------- inputs (generated on the host, then resident in HBM)
-    pspec = inputs.PREFILL_WORKLOADS[PREFILL]
-    log(f"generating {PREFILL}")
-    pd = inputs.make_prefill(pspec)
-    G = pspec.num_heads_q // pspec.num_heads_kv
-    pairs = inputs.count_valid_pairs(pd["blk_idx"].numpy(), pd["cu_seqlens_q"].numpy(),
-                                     pd["cu_seqlens_k"].numpy(), pspec.block_size)
-    flops = 4.0 * pspec.head_dim * pspec.block_size * G * pairs
-    pg = {k: pd[k].to(dev) for k in ("q", "k", "v", "blk_idx", "cu_seqlens_q", "cu_seqlens_k")}
-    p_out = torch.empty_like(pg["q"])
-    p_lse = torch.empty((pspec.num_heads_q, pg["q"].shape[0]), dtype=torch.float32, device=dev)
-    total_q = pg["q"].shape[0]
-    p_ws_bytes = fsa.fsa_selected_attn_fwd_workspace_size(
-        len(pspec.seqlens), total_q, pd["max_seqlen_q"], pspec.num_heads_q, pspec.num_heads_kv,
-        pspec.head_dim, pspec.block_size, pspec.topk, 0)
-    p_ws = torch.empty(max(p_ws_bytes, 1), dtype=torch.uint8, device=dev)
+    if args.mode == "copy":
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)     # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy: {args.warmup + args.steps} launches of 1 GiB")
+        return
 
+    # ---------------- inputs (generated on the host, then resident in HBM)
+    want_p = args.mode in ("full", "prefill")
+    want_d = args.mode in ("full", "decode")
+    pspec = inputs.PREFILL_WORKLOADS[PREFILL]
     dspec = inputs.DECODE_WORKLOADS[DECODE]
-    log(f"generating {DECODE}")
-    dd = inputs.make_decode(dspec)
-    sets = []
-    kc = dd["k_cache"].to(dev)
-    vc = dd["v_cache"].to(dev)
-    sets.append((kc, vc))
-    sets.append((kc.clone(), vc.clone()))          # second copy at other addresses
-    dq = dd["q"].to(dev)
-    dtok = dd["tok_idx"].to(dev)
-    dbt = dd["block_table"].to(dev)
-    dcs = dd["cache_seqlens"].to(dev)
-    d_out = torch.empty_like(dq)
-    d_lse = torch.empty((dspec.batch, dspec.num_heads_q), dtype=torch.float32, device=dev)
-    d_ws = torch.empty(fsa.fsa_topk_decode_workspace_size(
-        dspec.batch, dspec.num_heads_q, dspec.num_heads_kv, dspec.head_dim, dspec.topk, 0),
-        dtype=torch.uint8, device=dev)
-    n_sel = dspec.batch * dspec.num_heads_kv * dspec.topk          # lists hold distinct positions
-    d_bytes = (n_sel * 2 * dspec.head_dim * 2                      # selected K and V rows
-               + dtok.numel() * 4 + dbt.numel() * 4 + dcs.numel() * 4
-               + dq.numel() * 2 + d_out.numel() * 2 + d_lse.numel() * 4)
+    if want_p:
+        log(f"generating {PREFILL}")
+        pd = inputs.make_prefill(pspec)
+        G = pspec.num_heads_q // pspec.num_heads_kv
+        pairs = inputs.count_valid_pairs(pd["blk_idx"].numpy(), pd["cu_seqlens_q"].numpy(),
+                                         pd["cu_seqlens_k"].numpy(), pspec.block_size)
+        flops = 4.0 * pspec.head_dim * pspec.block_size * G * pairs
+        pg = {k: pd[k].to(dev) for k in ("q", "k", "v", "blk_idx", "cu_seqlens_q", "cu_seqlens_k")}
+        p_out = torch.empty_like(pg["q"])
+        p_lse = torch.empty((pspec.num_heads_q, pg["q"].shape[0]), dtype=torch.float32, device=dev)
+        total_q = pg["q"].shape[0]
+        p_ws_bytes = fsa.fsa_selected_attn_fwd_workspace_size(
+            len(pspec.seqlens), total_q, pd["max_seqlen_q"], pspec.num_heads_q,
+            pspec.num_heads_kv, pspec.head_dim, pspec.block_size, pspec.topk, 0)
+        p_ws = torch.empty(max(p_ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    if want_d:
+        log(f"generating {DECODE}")
+        dd = inputs.make_decode(dspec)
+        sets = []
+        kc = dd["k_cache"].to(dev)
+        vc = dd["v_cache"].to(dev)
+        sets.append((kc, vc))
+        sets.append((kc.clone(), vc.clone()))          # second copy at other addresses
+        dq = dd["q"].to(dev)
+        dtok = dd["tok_idx"].to(dev)
+        dbt = dd["block_table"].to(dev)
+        dcs = dd["cache_seqlens"].to(dev)
+        d_out = torch.empty_like(dq)
+        d_lse = torch.empty((dspec.batch, dspec.num_heads_q), dtype=torch.float32, device=dev)
+        d_ws = torch.empty(fsa.fsa_topk_decode_workspace_size(
+            dspec.batch, dspec.num_heads_q, dspec.num_heads_kv, dspec.head_dim, dspec.topk, 0),
+            dtype=torch.uint8, device=dev)
+        n_sel = dspec.batch * dspec.num_heads_kv * dspec.topk      # lists hold distinct positions
+        d_bytes = (n_sel * 2 * dspec.head_dim * 2                  # selected K and V rows
+                   + dtok.numel() * 4 + dbt.numel() * 4 + dcs.numel() * 4
+                   + dq.numel() * 2 + d_out.numel() * 2 + d_lse.numel() * 4)
 
     def prefill():
         fsa.fsa_selected_attn_fwd(pg["q"], pg["k"], pg["v"], pg["blk_idx"], pg["cu_seqlens_q"],
@@ -137,6 +154,13 @@ def main():
     def decode(i):
         k_, v_ = sets[i % 2]
         fsa.fsa_topk_decode(dq, k_, v_, dtok, dbt, dcs, out=d_out, lse=d_lse, workspace=d_ws)
+
+    if args.mode in ("prefill", "decode"):
+        for i in range(args.warmup + args.steps):
+            prefill() if args.mode == "prefill" else decode(i)
+        torch.cuda.synchronize()
+        log(f"{args.mode}: {args.warmup + args.steps} launches")
+        return
 
     log(f"warmup {args.warmup} steps")
     for i in range(args.warmup):

@@ -91,7 +91,7 @@ size_t fsa_selected_attn_fwd_workspace_size(int32_t batch, int64_t total_q,
  *            cu_seqlens_k[batch] <= total_k (rows past those are not touched)
  *   max_seqlen_q  >= every S_q; max_seqlen_k >= every S_k
  *   head_dim 64 or 128; block_size 64; 1 <= topk <= 64;
- *   num_heads_q / num_heads_kv <= 256
+ *   num_heads_q / num_heads_kv <= 224
  *   causal   nonzero: bottom-right causal mask; zero: no mask
  *   num_splits  0 = automatic; n >= 1 splits every tile's selected-block set
  *            into n parts computed by separate workgroups and merged by

@@ -15,7 +15,7 @@
 namespace {
 
 constexpr int kMaxTopkPrefill = 64;
-constexpr int kMaxGroupPrefill = 256;
+constexpr int kMaxGroupPrefill = 224;   // one tile covers at most 14 m-tiles of 16 rows
 constexpr int kMaxSplitsPrefill = 16;
 constexpr int kMaxTopkDecode = 8192;
 constexpr int kMaxGroupDecode = 16;
@@ -49,7 +49,7 @@ PrefillPlan plan_prefill(int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_
                          int32_t num_splits) {
     PrefillPlan pl{};
     const int G = Hq / Hkv;
-    int T = 256 / G;
+    int T = fsa::sel_attn_fwd_rows_per_tile() / G;
     if (T > 64) T = 64;
     if (T < 1) T = 1;
     pl.T = T;
@@ -204,6 +204,9 @@ fsa_status_t fsa_selected_attn_fwd(const void* q, const void* k, const void* v,
     p.mtiles = pl.mtiles;
     p.tiles_per_seq = pl.tiles_per_seq;
     p.n_wg = pl.n_wg;
+    p.ring = fsa::sel_attn_fwd_ring(head_dim, pl.T, topk);
+    if (fsa::sel_attn_fwd_lds_bytes(head_dim, pl.T, topk, p.ring) > 160 * 1024)
+        return FSA_ERROR_NOT_SUPPORTED;
     p.scale_log2 = resolve_scale(softmax_scale, head_dim) * fsa::kLog2e;
     const size_t rows = (size_t)total_q * num_heads_q;
     if (pl.splits > 1) {

@@ -29,12 +29,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 pair -> packed bf16 pair, round to nearest even (hardware convert).
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// fp32 pair -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 a = (__bf16)lo;
-    __bf16 b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // Workgroups are handed to the 8 XCDs round-robin (id % 8).  Give each XCD a

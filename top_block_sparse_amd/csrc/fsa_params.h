@@ -26,6 +26,7 @@ struct SelFwdParams {
     int mtiles;         // ceil(T*G/16) 16-row MFMA tiles per tile
     int tiles_per_seq;
     int n_wg;
+    int ring;           // LDS ring slots of K/V blocks (3 or 4)
     float scale_log2;   // softmax_scale * log2(e)
 };
 
@@ -62,7 +63,9 @@ struct MergeParams {
 
 template <int D>
 hipError_t launch_sel_attn_fwd(const SelFwdParams& p, hipStream_t stream);
-size_t sel_attn_fwd_lds_bytes(int D, int T, int topk);
+size_t sel_attn_fwd_lds_bytes(int D, int T, int topk, int ring);
+int sel_attn_fwd_ring(int D, int T, int topk);   // ring slots that fit in LDS
+int sel_attn_fwd_rows_per_tile();   // query rows (T*G) one workgroup covers
 hipError_t launch_decode_prepass(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeParams& p, int D, hipStream_t stream);
 int decode_waves_per_split();

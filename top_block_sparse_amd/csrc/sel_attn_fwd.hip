@@ -12,70 +12,153 @@
 // r % G), so the query group forms the MFMA M dimension.  The workgroup
 // builds, in LDS, the ascending union of the blocks its tokens selected
 // together with a per-block bitmask of the selecting tokens, then streams the
-// union: each K/V block is loaded once (coalesced 16-byte loads), staged in
-// LDS double-buffered (K row-major, V transposed), and consumed by every
-// m-tile that contains a selecting token.  Rows whose token did not select
-// the block are masked to -inf, exactly like causally masked keys.
+// union through a ring of LDS slots:
+//   - two producer waves copy each K/V block straight from HBM/L2 into a ring
+//     slot with buffer->LDS loads (16 bytes per lane, no registers involved;
+//     rows past the sequence end read as zero), keep up to three blocks in
+//     flight, and publish a slot by writing its sequence number once their
+//     loads have landed;
+//   - each of the fourteen consumer waves owns one m-tile, waits for the next
+//     slot, computes it if any of its tokens selected the block, and counts
+//     itself done with the slot; a producer reuses a slot only after all
+//     consumers are done with it.
+// Consumers never wait for one another, so the uneven per-block work of
+// random selections evens out over the tile instead of costing a barrier per
+// block.  Every wait is a bounded spin, so a logic error can only produce
+// wrong values, never a hung GPU.
 //
 // Per m-tile and block the contraction runs transposed, S^T = K * Q^T with
 // v_mfma_f32_16x16x32_bf16: the key index is the MFMA row, the query row the
 // column.  The accumulator layout of S^T leaves each lane holding, for one
 // query row, exactly the keys that lane must supply to the P^T operand of
-// O^T = V^T * P^T, so P never leaves registers.  Online softmax runs in the
-// log2 domain (scale folded with log2 e); a row's running max is shared by
-// its four lanes through two cross-lane exchanges per block.
+// O^T = V^T * P^T, so P never leaves registers; the V^T operand is read from
+// the row-major V tile with the gfx950 transposing LDS load
+// (ds_read_b64_tr_b16).  Online softmax runs in the log2 domain (scale * log2 e
+// folded into one FMA); a row's running max is shared by its four lanes through
+// two permlane swaps per block.
 #include "fsa_common.h"
 #include "fsa_params.h"
 
+#include <type_traits>
+
 namespace fsa {
 
-constexpr int kSelWaves = 8;                       // waves per workgroup
+constexpr int kSelConsumers = 14;                  // waves that own an m-tile
+constexpr int kSelProducers = 2;                   // waves that stream K/V
+constexpr int kSelWaves = kSelConsumers + kSelProducers;
 constexpr int kSelThreads = kSelWaves * 64;
-constexpr int kSelMtPerWave = 2;                   // m-tiles owned by each wave
-constexpr int kSelWin = 512;                       // blocks per union-building window
+constexpr int kSelWin = 256;                       // blocks per union-building window
+constexpr int kSelRingMax = 4;                     // LDS slots of K/V blocks (3 if LDS is short)
+constexpr int kSelDepth = 3;                       // blocks in flight per producer (<= slots)
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kSpinLimit = 1 << 22;                // bounded waits (normal waits are ~1e3)
 
-
-// LDS layout (bytes) for head dim D.
+// LDS layout (bytes) for head dim D.  A slot holds one 64-key block: the K tile
+// then the V tile, both row-major with padded rows.  K rows are 16 bytes longer
+// than d bf16 values, so the 16 keys a lane group reads at one 16-byte column
+// fall on 16 distinct bank groups; V rows are 32 bytes longer, so the 8
+// consecutive keys two lane groups gather with transposing reads (32 bytes
+// per key) fall on disjoint banks.  Every fragment address is then one per-lane
+// base plus a compile-time offset.  Both tiles are whole KiBs; each
+// buffer->LDS load fills 1 KiB of a tile contiguously (lane i -> bytes 16i),
+// its padding lanes reading out of range (zeros).
 template <int D>
 struct SelLds {
-    static constexpr int kK = kBlockKeys * D * 2;        // K tile, row-major, swizzled
-    static constexpr int kVt = D * kBlockKeys * 2;       // V^T tile, swizzled
-    static constexpr int kStage = kK + kVt;
-    static constexpr int kMasks = 2 * kStage;            // u64 [kSelWin]
-    static constexpr int kUMask = kMasks + kSelWin * 8;  // u64 [kSelWin]
-    static constexpr int kUList = kUMask + kSelWin * 8;  // i32 [kSelWin]
-    static constexpr int kCount = kUList + kSelWin * 4;  // i32
-    static constexpr int kEnt = kCount + 16;             // i32 [T*topk]
-    static size_t bytes(int T, int topk) { return (size_t)kEnt + (size_t)T * topk * 4; }
+    static constexpr int kKRow = D * 2 + 16;
+    static constexpr int kVRow = D * 2 + 32;
+    static constexpr int kKTile = kBlockKeys * kKRow;
+    static constexpr int kVTile = kBlockKeys * kVRow;
+    static_assert(kKTile % 1024 == 0 && kVTile % 1024 == 0, "tiles are whole KiBs");
+    static constexpr int kSlot = kKTile + kVTile;
+    // union buffers and ring flags follow the ring of `ring` slots
+    __host__ __device__ static int masks(int ring) { return ring * kSlot; }                // u64 [kSelWin]
+    __host__ __device__ static int umask(int ring) { return masks(ring) + kSelWin * 8; }   // u64 [kSelWin]
+    __host__ __device__ static int ulist(int ring) { return umask(ring) + kSelWin * 8; }   // i32 [kSelWin]
+    __host__ __device__ static int count(int ring) { return ulist(ring) + kSelWin * 4; }   // i32
+    __host__ __device__ static int ready(int ring) { return count(ring) + 16; }            // u32 [ring][producers]
+    __host__ __device__ static int done(int ring) { return ready(ring) + kSelRingMax * kSelProducers * 4; }
+    __host__ __device__ static int ent(int ring) { return done(ring) + kSelRingMax * 4; }  // i32 [T*topk]
+    __host__ __device__ static size_t bytes(int T, int topk, int ring) { return (size_t)ent(ring) + (size_t)T * topk * 4; }
 };
 
-template <int D>
-__device__ __forceinline__ int k_lds_off(int key, int chunk) {
-    constexpr int NCH = D / 8;
-    return key * (D * 2) + ((chunk ^ (key & (NCH - 1))) << 4);
+__device__ __forceinline__ unsigned long long uniform_u64(unsigned long long x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return ((unsigned long long)hi << 32) | lo;
 }
-__device__ __forceinline__ int vt_lds_off(int d, int chunk) {
-    return d * (kBlockKeys * 2) + ((chunk ^ (d & 7)) << 4);
+
+__device__ __forceinline__ float lane_max4(float x) {
+    // max over lanes l, l^16, l^32, l^48 (the four lanes holding one query row)
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float lane_sum4(float x) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Transposing LDS read: within each 16-lane group, lane j receives the 16-bit
+// word at (address of lane j/4 + 4k) + 2*(j%4), k = 0..3.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint8_t* p) {
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+    return __builtin_bit_cast(u32x2_t, v);
+}
+
+// LDS word read that completes before it returns.  Used by the ring protocol
+// (flags written by other waves) and by the producers, whose buffer->LDS
+// loads the compiler would otherwise make every LDS read wait for.
+__device__ __forceinline__ uint32_t lds_load_sync(const void* p) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(v)
+                 : "v"((uint32_t)(uintptr_t)p)
+                 : "memory");
+    return v;
+}
+
+// Workgroup barrier that orders LDS only (no drain of global loads).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 template <int D>
 __global__ void __launch_bounds__(kSelThreads)
 sel_attn_fwd_kernel(const SelFwdParams p) {
-    constexpr int NCH = D / 8;                  // 16-byte chunks per K/V row
     constexpr int KS = D / 32;                  // MFMA k-steps over the head dim
     constexpr int DT = D / 16;                  // 16-wide tiles of the head dim
-    constexpr int KCH = (kBlockKeys * NCH) / kSelThreads;   // K chunks per thread
-    constexpr int VSB = 16 * NCH;               // 4-key x 8-dim V sub-blocks per block
-    static_assert(KCH >= 1 && (kBlockKeys * NCH) % kSelThreads == 0, "K staging split");
-    static_assert(VSB <= kSelThreads, "V staging split");
     using L = SelLds<D>;
+    constexpr int NIK = L::kKTile / 1024, NIV = L::kVTile / 1024;
+    constexpr int NI = NIK + NIV;                           // 1 KiB loads per block
+    constexpr int NIP0 = (NI + 1) / 2, NIP1 = NI - NIP0;    // ... per producer wave
+    static_assert(kSelProducers == 2 && NIP0 * kSelDepth <= 63, "vmcnt budget");
 
     extern __shared__ __align__(16) uint8_t smem[];
-    unsigned long long* s_masks = reinterpret_cast<unsigned long long*>(smem + L::kMasks);
-    unsigned long long* s_umask = reinterpret_cast<unsigned long long*>(smem + L::kUMask);
-    int* s_ulist = reinterpret_cast<int*>(smem + L::kUList);
-    int* s_count = reinterpret_cast<int*>(smem + L::kCount);
-    int* s_ent = reinterpret_cast<int*>(smem + L::kEnt);
+    const int ring = p.ring;
+    unsigned long long* s_masks = reinterpret_cast<unsigned long long*>(smem + L::masks(ring));
+    unsigned long long* s_umask = reinterpret_cast<unsigned long long*>(smem + L::umask(ring));
+    int* s_ulist = reinterpret_cast<int*>(smem + L::ulist(ring));
+    int* s_count = reinterpret_cast<int*>(smem + L::count(ring));
+    uint32_t* s_ready = reinterpret_cast<uint32_t*>(smem + L::ready(ring));
+    uint32_t* s_done = reinterpret_cast<uint32_t*>(smem + L::done(ring));
+    int* s_ent = reinterpret_cast<int*>(smem + L::ent(ring));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -113,6 +196,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     }
     const int topk = p.topk;
     const int G = p.G;
+    const float c_log2 = p.scale_log2;
 
     // ---- the tile's lists -> LDS, dropping ids outside the range and fully-future blocks
     const int nent = ntok * topk;
@@ -124,168 +208,178 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         if (ok && p.causal) ok = id * kBlockKeys <= tok0 + tl + off;
         s_ent[e] = ok ? id : -1;
     }
+    if (tid < kSelRingMax * (kSelProducers + 1)) s_ready[tid] = 0u;   // s_ready and s_done
 
-    // ---- per-lane row bookkeeping for the owned m-tiles
-    float m_run[kSelMtPerWave], l_run[kSelMtPerWave];
-    f32x4_t acc[kSelMtPerWave][DT];
-    u32x4_t qf[kSelMtPerWave][KS];
-    unsigned long long mt_tok[kSelMtPerWave];   // tokens covered by the m-tile
-    int row_tl[kSelMtPerWave], row_lim[kSelMtPerWave];
+    const bool consumer = wave < kSelConsumers;
+
+    // ---- consumer bookkeeping for its m-tile (row = mt*16 + lr)
+    const int mt = wave;
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4_t acc[DT];
 #pragma unroll
-    for (int t = 0; t < kSelMtPerWave; ++t) {
-        const int mt = wave * kSelMtPerWave + t;
-        m_run[t] = -INFINITY;
-        l_run[t] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[t][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    u32x4_t qf[KS];
+    unsigned long long mt_tok = 0ull;           // tokens covered by the m-tile (wave-uniform)
+    int row_tok = 64, row_lim = 0, lo_lim = 0x7fffffff;
+    {
         const int row = mt * 16 + lr;
         const int tl = row / G;
         const int hh = row - tl * G;
-        const bool valid = mt < p.mtiles && tl < ntok;
-        row_tl[t] = valid ? tl : 63;
-        // keys with local index < row_lim are visible to this row
+        const bool valid = consumer && mt < p.mtiles && tl < ntok;
+        row_tok = valid ? tl : 64;
         int lim = Sk;
         if (p.causal) {
             const int c = tok0 + tl + off + 1;
             lim = c < lim ? c : lim;
         }
-        row_lim[t] = valid ? lim : 0;
+        row_lim = lim;
+        int lo = valid ? lim : 0x7fffffff;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_xor(lo, o);
+            lo = y < lo ? y : lo;
+        }
+        lo_lim = __builtin_amdgcn_readfirstlane(lo);
         const uint16_t* qrow = p.q + ((q0 + tok0 + tl) * p.Hq + g * G + hh) * (int64_t)D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            qf[t][s] = valid ? *reinterpret_cast<const u32x4_t*>(qrow + s * 32 + lg * 8)
-                             : u32x4_t{0u, 0u, 0u, 0u};
+            qf[s] = valid ? *reinterpret_cast<const u32x4_t*>(qrow + s * 32 + lg * 8)
+                          : u32x4_t{0u, 0u, 0u, 0u};
         }
         unsigned long long mk = 0ull;
-        if (mt < p.mtiles) {
+        if (consumer && mt < p.mtiles) {
             const int t_first = (mt * 16) / G;
             int t_last = (mt * 16 + 15) / G;
             t_last = t_last < ntok - 1 ? t_last : ntok - 1;
             for (int x = t_first; x <= t_last; ++x) mk |= 1ull << x;
         }
-        mt_tok[t] = mk;
+        mt_tok = uniform_u64(mk);
     }
 
-    // ---- staging of one K/V block: global -> registers -> LDS (K row-major, V transposed)
-    u32x4_t kreg[KCH];
-    u32x4_t vreg[4];
-    const uint16_t* kbase = p.k + (k0 * p.Hkv + g) * (int64_t)D;
-    const uint16_t* vbase = p.v + (k0 * p.Hkv + g) * (int64_t)D;
-    const int64_t krow_stride = (int64_t)p.Hkv * D;
+    // consumer fragment addresses (bytes within a slot)
+    // K: lane (lr, lg) reads key kt*16 + lr, head-dim chunk 4s + lg
+    const int kbase = lr * L::kKRow + lg * 16;
+    // V: lane (lr, lg) points at key 32ks + 16h + 4lg + lr/4, dims dt*16 + 4(lr%4)
+    const int vbase = L::kKTile + (4 * lg + (lr >> 2)) * L::kVRow + 8 * (lr & 3);
 
-    auto issue_loads = [&](int blk) {
-#pragma unroll
-        for (int r = 0; r < KCH; ++r) {
-            const int idx = tid + kSelThreads * r;
-            const int key = idx / NCH, c = idx % NCH;
-            const int krow = blk * kBlockKeys + key;
-            kreg[r] = krow < Sk ? *reinterpret_cast<const u32x4_t*>(kbase + krow * krow_stride + c * 8)
-                                : u32x4_t{0u, 0u, 0u, 0u};
-        }
-        if (tid < VSB) {
-            const int c = tid % NCH, kg = tid / NCH;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int krow = blk * kBlockKeys + 4 * kg + r;
-                vreg[r] = krow < Sk ? *reinterpret_cast<const u32x4_t*>(vbase + krow * krow_stride + c * 8)
-                                    : u32x4_t{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto write_stage = [&](int buf) {
-        uint8_t* kb = smem + buf * L::kStage;
-        uint8_t* vt = kb + L::kK;
-#pragma unroll
-        for (int r = 0; r < KCH; ++r) {
-            const int idx = tid + kSelThreads * r;
-            const int key = idx / NCH, c = idx % NCH;
-            *reinterpret_cast<u32x4_t*>(kb + k_lds_off<D>(key, c)) = kreg[r];
-        }
-        if (tid < VSB) {
-            const int c = tid % NCH, kg = tid / NCH;
-            // keys 4kg..4kg+3 = 32*ks + 16*h + 4*gg + i  ->  position 32*ks + 8*gg + 4*h + i
-            const int ks = kg >> 3, h = (kg >> 2) & 1, gg = kg & 3;
-            const int pchunk = 4 * ks + gg;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const uint32_t w0 = vreg[0][x], w1 = vreg[1][x], w2 = vreg[2][x], w3 = vreg[3][x];
-                const u32x2_t lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
-                const u32x2_t hi = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
-                const int d0 = c * 8 + 2 * x;
-                *reinterpret_cast<u32x2_t*>(vt + vt_lds_off(d0, pchunk) + 8 * h) = lo;
-                *reinterpret_cast<u32x2_t*>(vt + vt_lds_off(d0 + 1, pchunk) + 8 * h) = hi;
-            }
-        }
-    };
-
-    // ---- one m-tile against one staged block
-    auto compute = [&](int t, int buf, int blk, unsigned long long bmask) {
-        const uint8_t* kb = smem + buf * L::kStage;
-        const uint8_t* vt = kb + L::kK;
+    // ---- one block for this consumer's m-tile
+    auto compute = [&](const uint8_t* sl, int blk, unsigned long long bm) {
         f32x4_t st[4];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kb + k_lds_off<D>(kt * 16 + lr, 4 * s + lg));
-                st[kt] = mfma_16x16x32(a, qf[t][s], st[kt]);
-            }
+        for (int s = 0; s < KS; ++s) {
+            u32x4_t kf[4];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+                kf[kt] = *reinterpret_cast<const u32x4_t*>(sl + kbase + kt * 16 * L::kKRow + s * 64);
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt) st[kt] = mfma_16x16x32(kf[kt], qf[s], st[kt]);
         }
-        // mask: token did not select the block, causal limit, sequence end
-        const int lim = ((bmask >> row_tl[t]) & 1ull) ? row_lim[t] - blk * kBlockKeys : 0;
+        // online softmax (log2 domain)
+        const bool sel = row_tok < 64 && ((bm >> row_tok) & 1ull) != 0ull;
         float x[16];
-        float mloc = -INFINITY;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = kt * 16 + lg * 4 + i;
-                const float v = key < lim ? st[kt][i] * p.scale_log2 : -INFINITY;
-                x[kt * 4 + i] = v;
-                mloc = fmaxf(mloc, v);
-            }
+            for (int i = 0; i < 4; ++i) x[kt * 4 + i] = st[kt][i];
+        if (blk * kBlockKeys + kBlockKeys > lo_lim) {           // causal edge / sequence end
+            const int lim = row_lim - blk * kBlockKeys;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (kt * 16 + lg * 4 + i >= lim) x[kt * 4 + i] = -INFINITY;
         }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-        const float m_new = fmaxf(m_run[t], mloc);
-        const float msub = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[t] - msub);
-        m_run[t] = m_new;
-        float lsum = 0.f;
+        float mx = x[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
+        mx = lane_max4(mx);
+        const float m_new = sel ? fmaxf(m_run, mx * c_log2) : m_run;
+        const float msub = sel ? m_new : INFINITY;
+        const float alpha = sel ? fast_exp2(m_run - m_new) : 1.f;
+        m_run = m_new;
+        float ls = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            x[e] = fast_exp2(x[e] - msub);
-            lsum += x[e];
+            x[e] = fast_exp2(fmaf(x[e], c_log2, -msub));
+            ls += x[e];
         }
-        l_run[t] = l_run[t] * alpha + lsum;
+        l_run = l_run * alpha + ls;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0ull) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[t][dt] *= alpha;
+            for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+        }
+        u32x4_t pb[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const u32x4_t pb = {pack_bf16x2(x[8 * ks + 0], x[8 * ks + 1]),
-                                pack_bf16x2(x[8 * ks + 2], x[8 * ks + 3]),
-                                pack_bf16x2(x[8 * ks + 4], x[8 * ks + 5]),
-                                pack_bf16x2(x[8 * ks + 6], x[8 * ks + 7])};
+            pb[ks] = u32x4_t{pack_bf16x2(x[8 * ks + 0], x[8 * ks + 1]),
+                             pack_bf16x2(x[8 * ks + 2], x[8 * ks + 3]),
+                             pack_bf16x2(x[8 * ks + 4], x[8 * ks + 5]),
+                             pack_bf16x2(x[8 * ks + 6], x[8 * ks + 7])};
+        }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(vt + vt_lds_off(dt * 16 + lr, 4 * ks + lg));
-                acc[t][dt] = mfma_16x16x32(a, pb, acc[t][dt]);
+                const uint8_t* p0 = sl + vbase + 32 * ks * L::kVRow + dt * 32;
+                const u32x2_t lo = lds_read_tr16(p0);
+                const u32x2_t hi = lds_read_tr16(p0 + 16 * L::kVRow);
+                acc[dt] = mfma_16x16x32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb[ks], acc[dt]);
             }
         }
     };
 
-    __syncthreads();   // s_ent ready
+    // ---- producer: block -> ring slot with buffer->LDS loads
+    const int pw = wave - kSelConsumers;        // producer index (valid for producers)
+    const int64_t row_bytes = (int64_t)p.Hkv * D * 2;
+    const uint8_t* kseq = reinterpret_cast<const uint8_t*>(p.k + (k0 * p.Hkv + g) * (int64_t)D);
+    const uint8_t* vseq = reinterpret_cast<const uint8_t*>(p.v + (k0 * p.Hkv + g) * (int64_t)D);
+    auto produce = [&](auto nip_c, int first, int blk, int slot) {
+        constexpr int NIPW = decltype(nip_c)::value;
+        const int rows = Sk - blk * kBlockKeys < kBlockKeys ? Sk - blk * kBlockKeys : kBlockKeys;
+        const uint32_t nrec = (uint32_t)((rows - 1) * row_bytes + D * 2);
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(kseq + blk * kBlockKeys * row_bytes), 0, nrec, 0x00020000);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(vseq + blk * kBlockKeys * row_bytes), 0, nrec, 0x00020000);
+        uint8_t* sl = smem + slot * L::kSlot;
+#pragma unroll
+        for (int x = 0; x < NIPW; ++x) {
+            const int inst = first + x;                     // which 1 KiB of the slot
+            const bool isv = inst >= NIK;
+            const int rowb = isv ? L::kVRow : L::kKRow;
+            const int byte = (inst - (isv ? NIK : 0)) * 1024 + lane * 16;   // within the tile
+            const int row = byte / rowb, col = byte - row * rowb;
+            // padding bytes (col >= 2D) read out of range, i.e. zeros
+            const uint32_t goff = col < D * 2 ? (uint32_t)(row * row_bytes + col) : 0xfffffff0u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vr : kr, (lds_void_t*)(sl + inst * 1024),
+                                                     16, goff, 0, 0, 0);
+        }
+    };
+    auto publish = [&](int slot, uint32_t seq_plus1) {
+        if (lane == 0) {
+            asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                         :
+                         : "v"((uint32_t)(uintptr_t)(s_ready + slot * kSelProducers + pw)),
+                           "v"(seq_plus1)
+                         : "memory");
+        }
+    };
 
+    lds_barrier();   // s_ent and ring flags ready
+
+    uint32_t seq0 = 0;    // ring sequence number of the window's first block
     for (int win_lo = 0; win_lo < nb_range; win_lo += kSelWin) {
         const int win_n = (nb_range - win_lo) < kSelWin ? (nb_range - win_lo) : kSelWin;
         for (int x = tid; x < kSelWin; x += kSelThreads) s_masks[x] = 0ull;
-        __syncthreads();
+        lds_barrier();
         for (int e = tid; e < nent; e += kSelThreads) {
             const int id = s_ent[e];
             if (id >= win_lo && id < win_lo + win_n) atomicOr(&s_masks[id - win_lo], 1ull << (e / topk));
         }
-        __syncthreads();
+        lds_barrier();
         if (wave == 0) {      // ascending compaction of the non-empty blocks
             int n = 0;
             for (int c = 0; c < win_n; c += 64) {
@@ -301,64 +395,96 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
             }
             if (lane == 0) s_count[0] = n;
         }
-        __syncthreads();
-        const int n_u = s_count[0];
+        lds_barrier();
+        const int n_u = __builtin_amdgcn_readfirstlane(s_count[0]);
         const int u_beg = (int)(((long long)n_u * split) / p.num_splits);
         const int u_end = (int)(((long long)n_u * (split + 1)) / p.num_splits);
-        if (u_beg < u_end) {
-            issue_loads(s_ulist[u_beg]);
-            write_stage(0);
-            __syncthreads();
-            for (int u = u_beg; u < u_end; ++u) {
-                const int buf = (u - u_beg) & 1;
-                const bool has_next = u + 1 < u_end;
-                if (has_next) issue_loads(s_ulist[u + 1]);
-                const int blk = s_ulist[u];
-                const unsigned long long bm = s_umask[u];
-#pragma unroll
-                for (int t = 0; t < kSelMtPerWave; ++t) {
-                    if (bm & mt_tok[t]) compute(t, buf, blk, bm);
+        const int n = u_end - u_beg;
+
+        if (!consumer) {
+            // producer: issue block i, then publish block i - (kSelDepth - 1)
+            for (int i = 0; i < n; ++i) {
+                const uint32_t seq = seq0 + (uint32_t)i;
+                const int slot = (int)(seq % (uint32_t)ring);
+                const uint32_t need_done = kSelConsumers * (seq / (uint32_t)ring);
+                for (int sp = 0; sp < kSpinLimit && lds_load_sync(s_done + slot) < need_done; ++sp)
+                    __builtin_amdgcn_s_sleep(1);
+                const int blk = __builtin_amdgcn_readfirstlane(
+                    (int)lds_load_sync(s_ulist + u_beg + i));
+                if (pw == 0)
+                    produce(std::integral_constant<int, NIP0>{}, 0, blk, slot);
+                else
+                    produce(std::integral_constant<int, NIP1>{}, NIP0, blk, slot);
+                if (i >= kSelDepth - 1) {
+                    if (pw == 0)
+                        wait_vmcnt<NIP0 * (kSelDepth - 1)>();
+                    else
+                        wait_vmcnt<NIP1 * (kSelDepth - 1)>();
+                    const uint32_t ps = seq - (kSelDepth - 1);
+                    publish((int)(ps % (uint32_t)ring), ps + 1);
                 }
-                if (has_next) write_stage(buf ^ 1);
-                __syncthreads();
+            }
+            wait_vmcnt<0>();
+            const int first = n > kSelDepth - 1 ? n - (kSelDepth - 1) : 0;
+            for (int i = first; i < n; ++i) {
+                const uint32_t ps = seq0 + (uint32_t)i;
+                publish((int)(ps % (uint32_t)ring), ps + 1);
+            }
+        } else {
+            for (int i = 0; i < n; ++i) {
+                const uint32_t seq = seq0 + (uint32_t)i;
+                const int slot = (int)(seq % (uint32_t)ring);
+                for (int sp = 0; sp < kSpinLimit; ++sp) {
+                    bool ok = true;
+#pragma unroll
+                    for (int q = 0; q < kSelProducers; ++q)
+                        ok = ok && lds_load_sync(s_ready + slot * kSelProducers + q) >= seq + 1;
+                    if (ok) break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                const int u = u_beg + i;
+                const int blk = __builtin_amdgcn_readfirstlane(s_ulist[u]);
+                const unsigned long long bm = uniform_u64(s_umask[u]);
+                const int need = __builtin_amdgcn_readfirstlane((bm & mt_tok) != 0ull ? 1 : 0);
+                if (need) compute(smem + slot * L::kSlot, blk, bm);
+                // done with the slot: its reads have completed before the count
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                if (lane == 0) __hip_atomic_fetch_add(s_done + slot, 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
+        seq0 += (uint32_t)n;
+        lds_barrier();   // window done: union buffers may be rebuilt
     }
 
     // ---- epilogue: normalise, write O (bf16) and LSE, or the split partials
-#pragma unroll
-    for (int t = 0; t < kSelMtPerWave; ++t) {
-        const int mt = wave * kSelMtPerWave + t;
-        if (mt >= p.mtiles) continue;
-        float l = l_run[t];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+    if (consumer && mt < p.mtiles) {
+        const float l = lane_sum4(l_run);
         const int row = mt * 16 + lr;
         const int tl = row / G;
         const int hh = row - tl * G;
-        if (tl >= ntok) continue;
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        const float lse_v = l > 0.f ? (m_run[t] + __log2f(l)) * kLn2 : -INFINITY;
-        const int64_t tok = q0 + tok0 + tl;
-        const int head = g * G + hh;
-        const int64_t orow = tok * p.Hq + head;
-        if (p.num_splits == 1) {
-            uint16_t* o = p.out + orow * D + lg * 4;
+        if (tl < ntok) {
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const float lse_v = l > 0.f ? (m_run + __log2f(l)) * kLn2 : -INFINITY;
+            const int64_t tok = q0 + tok0 + tl;
+            const int head = g * G + hh;
+            const int64_t orow = tok * p.Hq + head;
+            if (p.num_splits == 1) {
+                uint16_t* o = p.out + orow * D + lg * 4;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const u32x2_t pk = {pack_bf16x2(acc[t][dt][0] * inv, acc[t][dt][1] * inv),
-                                    pack_bf16x2(acc[t][dt][2] * inv, acc[t][dt][3] * inv)};
-                *reinterpret_cast<u32x2_t*>(o + dt * 16) = pk;
-            }
-            if (p.lse != nullptr && lg == 0) p.lse[(int64_t)head * p.total_q + tok] = lse_v;
-        } else {
-            const int64_t prow = (int64_t)split * p.total_q * p.Hq + orow;
-            float* o = p.part_o + prow * D + lg * 4;
+                for (int dt = 0; dt < DT; ++dt) {
+                    const u32x2_t pk = {pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
+                                        pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv)};
+                    *reinterpret_cast<u32x2_t*>(o + dt * 16) = pk;
+                }
+                if (p.lse != nullptr && lg == 0) p.lse[(int64_t)head * p.total_q + tok] = lse_v;
+            } else {
+                const int64_t prow = (int64_t)split * p.total_q * p.Hq + orow;
+                float* o = p.part_o + prow * D + lg * 4;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                *reinterpret_cast<f32x4_t*>(o + dt * 16) = acc[t][dt] * inv;
+                for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4_t*>(o + dt * 16) = acc[dt] * inv;
+                if (lg == 0) p.part_lse[prow] = lse_v;
             }
-            if (lg == 0) p.part_lse[prow] = lse_v;
         }
     }
 }
@@ -366,7 +492,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
 // Launch helpers (host side).
 template <int D>
 hipError_t launch_sel_attn_fwd(const SelFwdParams& p, hipStream_t stream) {
-    const size_t lds = SelLds<D>::bytes(p.T, p.topk);
+    const size_t lds = SelLds<D>::bytes(p.T, p.topk, p.ring);
     static bool attr_set = false;   // idempotent; racing threads set the same value
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sel_attn_fwd_kernel<D>),
@@ -381,8 +507,16 @@ hipError_t launch_sel_attn_fwd(const SelFwdParams& p, hipStream_t stream) {
 template hipError_t launch_sel_attn_fwd<64>(const SelFwdParams&, hipStream_t);
 template hipError_t launch_sel_attn_fwd<128>(const SelFwdParams&, hipStream_t);
 
-size_t sel_attn_fwd_lds_bytes(int D, int T, int topk) {
-    return D == 64 ? SelLds<64>::bytes(T, topk) : SelLds<128>::bytes(T, topk);
+int sel_attn_fwd_rows_per_tile() { return kSelConsumers * 16; }
+
+size_t sel_attn_fwd_lds_bytes(int D, int T, int topk, int ring) {
+    return D == 64 ? SelLds<64>::bytes(T, topk, ring) : SelLds<128>::bytes(T, topk, ring);
+}
+
+int sel_attn_fwd_ring(int D, int T, int topk) {
+    for (int ring = kSelRingMax; ring > kSelDepth; --ring)
+        if (sel_attn_fwd_lds_bytes(D, T, topk, ring) <= (size_t)kLdsBytes) return ring;
+    return kSelDepth;
 }
 
 }  // namespace fsa
