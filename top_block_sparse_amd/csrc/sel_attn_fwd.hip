@@ -52,24 +52,26 @@ constexpr int kSelRingMax = 4;                     // LDS slots of K/V blocks (3
 constexpr int kSelDepth = 3;                       // blocks in flight per producer (<= slots)
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kSpinLimit = 1 << 22;                // bounded waits (normal waits are ~1e3)
+constexpr float kLazy = 8.f;                       // lazy-rescale threshold (log2 units)
 
-// LDS layout (bytes) for head dim D.  A slot holds one 64-key block: the K tile
-// then the V tile, both row-major with padded rows.  K rows are 16 bytes longer
-// than d bf16 values, so the 16 keys a lane group reads at one 16-byte column
-// fall on 16 distinct bank groups; V rows are 32 bytes longer, so the 8
-// consecutive keys two lane groups gather with transposing reads (32 bytes
-// per key) fall on disjoint banks.  Every fragment address is then one per-lane
-// base plus a compile-time offset.  Both tiles are whole KiBs; each
-// buffer->LDS load fills 1 KiB of a tile contiguously (lane i -> bytes 16i),
-// its padding lanes reading out of range (zeros).
+// LDS layout (bytes) for head dim D.  A slot holds one 64-key block in
+// "fragment-major" order: every MFMA operand fragment a consumer wave reads is
+// a contiguous run in lane order, so each fragment read is one conflict-free
+// contiguous wave read and every address is one per-lane base plus a
+// compile-time offset.
+//   K part: fragment (kt, s) = 1 KiB at (kt*KS + s) * 1024; lane l's 16 bytes
+//           are K[kt*16 + l%16][(4s + l/16)*8 .. +8] (the A operand of S^T).
+//   V part: fragment (ks, h, dt) = 512 bytes at kVOff + ((2ks + h)*DT + dt) * 512;
+//           lane l's 8 bytes are V[32ks + 16h + 4(l/16) + (l%16)/4][dt*16 +
+//           4(l%4) .. +4], the addresses a transposing read needs (see below).
+// The producers fill a slot with buffer->LDS loads of 1 KiB each (lane m ->
+// bytes 16m); for V, load lane m supplies the 8-byte pieces of two adjacent
+// fragment lanes, which are 8 consecutive d values of one key.
 template <int D>
 struct SelLds {
-    static constexpr int kKRow = D * 2 + 16;
-    static constexpr int kVRow = D * 2 + 32;
-    static constexpr int kKTile = kBlockKeys * kKRow;
-    static constexpr int kVTile = kBlockKeys * kVRow;
-    static_assert(kKTile % 1024 == 0 && kVTile % 1024 == 0, "tiles are whole KiBs");
-    static constexpr int kSlot = kKTile + kVTile;
+    static constexpr int KS = D / 32, DT = D / 16;
+    static constexpr int kVOff = 4 * KS * 1024;            // K part: 16 KiB (d=128)
+    static constexpr int kSlot = kVOff + 4 * DT * 512;     // + V part
     // union buffers and ring flags follow the ring of `ring` slots
     __host__ __device__ static int masks(int ring) { return ring * kSlot; }                // u64 [kSelWin]
     __host__ __device__ static int umask(int ring) { return masks(ring) + kSelWin * 8; }   // u64 [kSelWin]
@@ -78,7 +80,9 @@ struct SelLds {
     __host__ __device__ static int ready(int ring) { return count(ring) + 16; }            // u32 [ring][producers]
     __host__ __device__ static int done(int ring) { return ready(ring) + kSelRingMax * kSelProducers * 4; }
     __host__ __device__ static int ent(int ring) { return done(ring) + kSelRingMax * 4; }  // i32 [T*topk]
-    __host__ __device__ static size_t bytes(int T, int topk, int ring) { return (size_t)ent(ring) + (size_t)T * topk * 4; }
+    __host__ __device__ static size_t bytes(int T, int topk, int ring) {
+        return (size_t)ent(ring) + (size_t)T * topk * 4;
+    }
 };
 
 __device__ __forceinline__ unsigned long long uniform_u64(unsigned long long x) {
@@ -145,7 +149,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     constexpr int KS = D / 32;                  // MFMA k-steps over the head dim
     constexpr int DT = D / 16;                  // 16-wide tiles of the head dim
     using L = SelLds<D>;
-    constexpr int NIK = L::kKTile / 1024, NIV = L::kVTile / 1024;
+    constexpr int NIK = L::kVOff / 1024, NIV = (L::kSlot - L::kVOff) / 1024;
     constexpr int NI = NIK + NIV;                           // 1 KiB loads per block
     constexpr int NIP0 = (NI + 1) / 2, NIP1 = NI - NIP0;    // ... per producer wave
     static_assert(kSelProducers == 2 && NIP0 * kSelDepth <= 63, "vmcnt budget");
@@ -256,11 +260,9 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         mt_tok = uniform_u64(mk);
     }
 
-    // consumer fragment addresses (bytes within a slot)
-    // K: lane (lr, lg) reads key kt*16 + lr, head-dim chunk 4s + lg
-    const int kbase = lr * L::kKRow + lg * 16;
-    // V: lane (lr, lg) points at key 32ks + 16h + 4lg + lr/4, dims dt*16 + 4(lr%4)
-    const int vbase = L::kKTile + (4 * lg + (lr >> 2)) * L::kVRow + 8 * (lr & 3);
+    // consumer fragment addresses (bytes within a slot): contiguous in lane order
+    const int kbase = lane * 16;
+    const int vbase = L::kVOff + lane * 8;
 
     // ---- one block for this consumer's m-tile
     auto compute = [&](const uint8_t* sl, int blk, unsigned long long bm) {
@@ -272,7 +274,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
             u32x4_t kf[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
-                kf[kt] = *reinterpret_cast<const u32x4_t*>(sl + kbase + kt * 16 * L::kKRow + s * 64);
+                kf[kt] = *reinterpret_cast<const u32x4_t*>(sl + kbase + (kt * KS + s) * 1024);
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) st[kt] = mfma_16x16x32(kf[kt], qf[s], st[kt]);
         }
@@ -295,9 +297,14 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
 #pragma unroll
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, x[e]);
         mx = lane_max4(mx);
-        const float m_new = sel ? fmaxf(m_run, mx * c_log2) : m_run;
+        // The running max only moves when the block's max exceeds it by more
+        // than kLazy (log2 units): probabilities then stay below 2^kLazy, and
+        // most blocks need no rescale of the accumulator.
+        const float mb = mx * c_log2;
+        const bool bump = sel && mb > m_run + kLazy;
+        const float m_new = bump ? mb : m_run;
         const float msub = sel ? m_new : INFINITY;
-        const float alpha = sel ? fast_exp2(m_run - m_new) : 1.f;
+        const float alpha = bump ? fast_exp2(m_run - m_new) : 1.f;
         m_run = m_new;
         float ls = 0.f;
 #pragma unroll
@@ -323,9 +330,9 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const uint8_t* p0 = sl + vbase + 32 * ks * L::kVRow + dt * 32;
-                const u32x2_t lo = lds_read_tr16(p0);
-                const u32x2_t hi = lds_read_tr16(p0 + 16 * L::kVRow);
+                const uint8_t* p0 = sl + vbase + ((2 * ks) * DT + dt) * 512;
+                const u32x2_t lo = lds_read_tr16(p0);                  // keys 32ks + 4lg + ..
+                const u32x2_t hi = lds_read_tr16(p0 + DT * 512);       // keys 32ks + 16 + 4lg + ..
                 acc[dt] = mfma_16x16x32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb[ks], acc[dt]);
             }
         }
@@ -348,14 +355,22 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
 #pragma unroll
         for (int x = 0; x < NIPW; ++x) {
             const int inst = first + x;                     // which 1 KiB of the slot
-            const bool isv = inst >= NIK;
-            const int rowb = isv ? L::kVRow : L::kKRow;
-            const int byte = (inst - (isv ? NIK : 0)) * 1024 + lane * 16;   // within the tile
-            const int row = byte / rowb, col = byte - row * rowb;
-            // padding bytes (col >= 2D) read out of range, i.e. zeros
-            const uint32_t goff = col < D * 2 ? (uint32_t)(row * row_bytes + col) : 0xfffffff0u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? vr : kr, (lds_void_t*)(sl + inst * 1024),
-                                                     16, goff, 0, 0, 0);
+            int row, col;                                   // source key row, byte column
+            if (inst < NIK) {                               // K fragment (kt, s)
+                const int kt = inst / KS, s = inst % KS;
+                row = kt * 16 + (lane & 15);
+                col = (4 * s + (lane >> 4)) * 16;
+            } else {                                        // V fragments 2q, 2q+1
+                const int f = 2 * (inst - NIK) + (lane >> 5);   // (2ks + h)*DT + dt
+                const int dt = f % DT, kh = f / DT;             // kh = 2ks + h
+                const int fl = 2 * (lane & 31);                 // first fragment lane served
+                const int flr = fl & 15, flg = fl >> 4;
+                row = 16 * kh + 4 * flg + (flr >> 2);
+                col = (dt * 16 + 4 * (flr & 3)) * 2;
+            }
+            const uint32_t goff = (uint32_t)(row * row_bytes + col);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(inst < NIK ? kr : vr,
+                                                     (lds_void_t*)(sl + inst * 1024), 16, goff, 0, 0, 0);
         }
     };
     auto publish = [&](int slot, uint32_t seq_plus1) {
