@@ -112,15 +112,18 @@ fsa_status_t fsa_selected_attn_fwd(const void* q, const void* k, const void* v,
                                    size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
- * Bytes of device workspace fsa_topk_decode needs (never 0 for valid
- * arguments: the normalised index lists live there).  num_splits = 0 prices
- * the automatic choice.  Returns 0 for arguments fsa_topk_decode rejects.
+ * Bytes of device workspace fsa_topk_decode needs: the split partials, so 0
+ * when the lists are not split (num_splits = 1, or an automatic choice of 1).
+ * num_splits = 0 prices the automatic choice.  Returns 0 as well for
+ * arguments fsa_topk_decode rejects.
  */
 size_t fsa_topk_decode_workspace_size(int32_t batch, int32_t num_heads_q, int32_t num_heads_kv,
                                       int32_t head_dim, int32_t topk, int32_t num_splits);
 
-/* The split count fsa_topk_decode uses for num_splits = 0. */
-int32_t fsa_topk_decode_auto_splits(int32_t batch, int32_t num_heads_kv, int32_t topk);
+/* The split count fsa_topk_decode uses for num_splits = 0 (0 for arguments
+ * it rejects). */
+int32_t fsa_topk_decode_auto_splits(int32_t batch, int32_t num_heads_q, int32_t num_heads_kv,
+                                    int32_t topk);
 
 /*
  * Top-k gathered decode over a paged KV cache: one query token per sequence
@@ -141,7 +144,8 @@ int32_t fsa_topk_decode_auto_splits(int32_t batch, int32_t num_heads_kv, int32_t
  *   num_splits 0 = automatic (fsa_topk_decode_auto_splits), else 1..64: each
  *              (sequence, kv head) list is cut into that many parts whose
  *              partial results are merged by logsumexp
- *   workspace  at least fsa_topk_decode_workspace_size(...) bytes
+ *   workspace  at least fsa_topk_decode_workspace_size(...) bytes, 256-byte
+ *              aligned; may be NULL when that size is 0
  *   out        bf16 [batch, num_heads_q, head_dim]
  *   lse        fp32 [batch, num_heads_q], or NULL
  * The query sits after every cache position, so the bottom-right causal rule

@@ -124,22 +124,26 @@ def decode(lib, **kw):
     (dict(bt=None), INVALID),
     (dict(cs=None), INVALID),
     (dict(vc=FAKE + 8), INVALID),
-    (dict(ws=None), WORKSPACE),
-    (dict(ws_bytes=100), WORKSPACE),
-    (dict(ws=FAKE + 16), WORKSPACE),          # workspace must be 256-byte aligned
+    (dict(ws=None, splits=2), WORKSPACE),
+    (dict(ws_bytes=100, splits=2), WORKSPACE),
+    (dict(ws=FAKE + 16, splits=2), WORKSPACE),   # workspace must be 256-byte aligned
 ])
 def test_decode_argument_errors(lib, kw, code):
     assert decode(lib, **kw) == code
 
 
 def test_decode_workspace_and_splits(lib):
-    assert lib.fsa_topk_decode_auto_splits(32, 8, 2048) >= 1
-    s = lib.fsa_topk_decode_auto_splits(32, 8, 2048)
+    s = lib.fsa_topk_decode_auto_splits(32, 32, 8, 2048)
+    assert 1 <= s <= 64
     ws = lib.fsa_topk_decode_workspace_size(32, 32, 8, 128, 2048, 0)
     assert ws == lib.fsa_topk_decode_workspace_size(32, 32, 8, 128, 2048, s)
-    assert ws >= 32 * 8 * 2048 * 4 + 32 * 8 * 4 + s * 4 * 32 * 32 * 129 * 4
+    assert (ws == 0) == (s == 1)
+    assert lib.fsa_topk_decode_workspace_size(32, 32, 8, 128, 2048, 1) == 0
+    assert lib.fsa_topk_decode_workspace_size(32, 32, 8, 128, 2048, 3) >= 3 * 32 * 32 * 129 * 4
     assert lib.fsa_topk_decode_workspace_size(32, 32, 8, 128, 9000, 0) == 0
-    assert lib.fsa_topk_decode_auto_splits(1, 1, 10) == 1
+    assert lib.fsa_topk_decode_auto_splits(1, 1, 1, 10) == 1
+    assert lib.fsa_topk_decode_auto_splits(1, 8, 1, 8192) > 1      # one list: split it
+    assert lib.fsa_topk_decode_auto_splits(1, 6, 4, 100) == 0      # rejected shape
     assert decode(lib, batch=0, q=None) == 0
 
 

@@ -60,7 +60,7 @@ def load() -> ctypes.CDLL:
     lib.fsa_topk_decode_workspace_size.restype = sz
     lib.fsa_topk_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.fsa_topk_decode_auto_splits.restype = i32
-    lib.fsa_topk_decode_auto_splits.argtypes = [i32, i32, i32]
+    lib.fsa_topk_decode_auto_splits.argtypes = [i32, i32, i32, i32]
     lib.fsa_topk_decode.restype = ctypes.c_int
     lib.fsa_topk_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f32,
                                     i32, P, sz, P, P, P]
@@ -111,8 +111,8 @@ def fsa_topk_decode_workspace_size(batch: int, num_heads_q: int, num_heads_kv: i
                                                      topk, num_splits))
 
 
-def fsa_topk_decode_auto_splits(batch: int, num_heads_kv: int, topk: int) -> int:
-    return int(load().fsa_topk_decode_auto_splits(batch, num_heads_kv, topk))
+def fsa_topk_decode_auto_splits(batch: int, num_heads_q: int, num_heads_kv: int, topk: int) -> int:
+    return int(load().fsa_topk_decode_auto_splits(batch, num_heads_q, num_heads_kv, topk))
 
 
 def fsa_selected_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

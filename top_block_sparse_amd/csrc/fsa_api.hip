@@ -70,22 +70,17 @@ PrefillPlan plan_prefill(int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_
     return pl;
 }
 
-int decode_auto_splits(int32_t batch, int32_t Hkv, int32_t topk) {
+// Enough waves to give every CU about 16, with at least 32 rows per wave.
+int decode_auto_splits(int32_t batch, int32_t Hq, int32_t Hkv, int32_t topk) {
     const long long units = (long long)batch * Hkv;
-    if (units <= 0) return 1;
-    const int waves = fsa::decode_waves_per_split();
-    long long s = (2048 + units * waves - 1) / (units * waves);
-    const long long cap = topk / (waves * 32) > 1 ? topk / (waves * 32) : 1;   // >= 32 rows per wave
+    if (units <= 0 || Hkv <= 0) return 1;
+    const int waves = fsa::decode_waves_per_workgroup(Hq / Hkv);
+    long long s = (4096 + units * waves - 1) / (units * waves);
+    const long long cap = topk / (waves * 32) > 1 ? topk / (waves * 32) : 1;
     if (s > cap) s = cap;
     if (s > kMaxSplitsDecode) s = kMaxSplitsDecode;
     if (s < 1) s = 1;
     return (int)s;
-}
-
-int next_pow2(int x) {
-    int n = 1;
-    while (n < x) n <<= 1;
-    return n;
 }
 
 fsa_status_t check_decode_shape(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int32_t topk,
@@ -100,25 +95,22 @@ fsa_status_t check_decode_shape(int32_t batch, int32_t Hq, int32_t Hkv, int32_t 
     return FSA_SUCCESS;
 }
 
+// Decode workspace: split partials only (none when the lists are not split).
 struct DecodeLayout {
-    size_t rows, counts, part_o, part_lse, total;
-    int splits, nparts;
+    size_t part_o, part_lse, total;
+    int splits;
 };
 
 DecodeLayout decode_layout(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int32_t topk,
                            int32_t num_splits) {
     DecodeLayout l{};
-    l.splits = num_splits == 0 ? decode_auto_splits(batch, Hkv, topk) : num_splits;
-    l.nparts = l.splits * fsa::decode_waves_per_split();
+    l.splits = num_splits == 0 ? decode_auto_splits(batch, Hq, Hkv, topk) : num_splits;
+    if (l.splits <= 1) return l;
     size_t off = 0;
-    l.rows = off;
-    off = align_up(off + (size_t)batch * Hkv * topk * 4);
-    l.counts = off;
-    off = align_up(off + (size_t)batch * Hkv * 4);
     l.part_o = off;
-    off = align_up(off + (size_t)l.nparts * batch * Hq * D * 4);
+    off = align_up(off + (size_t)l.splits * batch * Hq * D * 4);
     l.part_lse = off;
-    off = align_up(off + (size_t)l.nparts * batch * Hq * 4);
+    off = align_up(off + (size_t)l.splits * batch * Hq * 4);
     l.total = off;
     return l;
 }
@@ -237,8 +229,10 @@ fsa_status_t fsa_selected_attn_fwd(const void* q, const void* k, const void* v,
     return FSA_SUCCESS;
 }
 
-int32_t fsa_topk_decode_auto_splits(int32_t batch, int32_t num_heads_kv, int32_t topk) {
-    return decode_auto_splits(batch, num_heads_kv, topk);
+int32_t fsa_topk_decode_auto_splits(int32_t batch, int32_t num_heads_q, int32_t num_heads_kv,
+                                    int32_t topk) {
+    if (check_decode_shape(batch, num_heads_q, num_heads_kv, 64, topk, 0) != FSA_SUCCESS) return 0;
+    return decode_auto_splits(batch, num_heads_q, num_heads_kv, topk);
 }
 
 size_t fsa_topk_decode_workspace_size(int32_t batch, int32_t num_heads_q, int32_t num_heads_kv,
@@ -268,11 +262,10 @@ fsa_status_t fsa_topk_decode(const void* q, const void* k_cache, const void* v_c
         return FSA_ERROR_INVALID_VALUE;
     const DecodeLayout lay = decode_layout(batch, num_heads_q, num_heads_kv, head_dim, topk,
                                            num_splits);
-    if (workspace == nullptr || workspace_bytes < lay.total ||
-        (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+    if (lay.total > 0 && (workspace == nullptr || workspace_bytes < lay.total ||
+                          (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
         return FSA_ERROR_WORKSPACE;
 
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
     fsa::DecodeParams p{};
     p.q = static_cast<const uint16_t*>(q);
     p.kc = static_cast<const uint16_t*>(k_cache);
@@ -280,10 +273,13 @@ fsa_status_t fsa_topk_decode(const void* q, const void* k_cache, const void* v_c
     p.tok_idx = tok_idx;
     p.block_table = block_table;
     p.cache_seqlens = cache_seqlens;
-    p.rows = reinterpret_cast<int32_t*>(ws + lay.rows);
-    p.counts = reinterpret_cast<int32_t*>(ws + lay.counts);
-    p.part_o = reinterpret_cast<float*>(ws + lay.part_o);
-    p.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
+    p.out = static_cast<uint16_t*>(out);
+    p.lse = lse;
+    if (lay.splits > 1) {
+        uint8_t* ws = static_cast<uint8_t*>(workspace);
+        p.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+        p.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
+    }
     p.batch = batch;
     p.Hq = num_heads_q;
     p.Hkv = num_heads_kv;
@@ -293,24 +289,27 @@ fsa_status_t fsa_topk_decode(const void* q, const void* k_cache, const void* v_c
     p.num_pages = num_pages;
     p.topk = topk;
     p.splits = lay.splits;
-    p.sort_n = next_pow2(topk);
+    p.ts = fsa::decode_table_slots(head_dim, p.G, topk);
     p.scale_log2 = resolve_scale(softmax_scale, head_dim) * fsa::kLog2e;
+    if (fsa::decode_lds_bytes(head_dim, p.G, p.ts, topk) > 160 * 1024)
+        return FSA_ERROR_NOT_SUPPORTED;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
-    if (fsa::launch_decode_prepass(p, s) != hipSuccess) return FSA_ERROR_LAUNCH;
-    if (fsa::launch_decode_split(p, head_dim, s) != hipSuccess) return FSA_ERROR_LAUNCH;
-    fsa::MergeParams m{};
-    m.part_o = p.part_o;
-    m.part_lse = p.part_lse;
-    m.out = static_cast<uint16_t*>(out);
-    m.lse = lse;
-    m.nrows = (int64_t)batch * num_heads_q;
-    m.nparts = lay.nparts;
-    m.lse_mode = 1;
-    m.Hq = num_heads_q;
-    m.ntok = batch;
-    if (fsa::launch_lse_merge(m, head_dim, s) != hipSuccess) return FSA_ERROR_LAUNCH;
+    if (fsa::launch_decode(p, head_dim, s) != hipSuccess) return FSA_ERROR_LAUNCH;
+    if (lay.splits > 1) {
+        fsa::MergeParams m{};
+        m.part_o = p.part_o;
+        m.part_lse = p.part_lse;
+        m.out = p.out;
+        m.lse = lse;
+        m.nrows = (int64_t)batch * num_heads_q;
+        m.nparts = lay.splits;
+        m.lse_mode = 1;
+        m.Hq = num_heads_q;
+        m.ntok = batch;
+        if (fsa::launch_lse_merge(m, head_dim, s) != hipSuccess) return FSA_ERROR_LAUNCH;
+    }
     return FSA_SUCCESS;
 }
 

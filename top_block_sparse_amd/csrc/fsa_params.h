@@ -38,12 +38,12 @@ struct DecodeParams {
     const int32_t* tok_idx;
     const int32_t* block_table;
     const int32_t* cache_seqlens;
-    int32_t* rows;          // workspace: [batch*Hkv][topk] physical cache rows
-    int32_t* counts;        // workspace: [batch*Hkv]
-    float* part_o;          // workspace: [nparts][batch*Hq][D]
-    float* part_lse;        // workspace: [nparts][batch*Hq]
+    uint16_t* out;          // [batch*Hq][D] bf16 (splits == 1)
+    float* lse;             // optional [batch*Hq] (splits == 1)
+    float* part_o;          // workspace: [splits][batch*Hq][D] (splits > 1)
+    float* part_lse;        // workspace: [splits][batch*Hq]
     int batch, Hq, Hkv, G, page_size, max_pages, num_pages, topk, splits;
-    int sort_n;             // power of two >= topk
+    int ts;                 // hash table slots (> topk)
     float scale_log2;
 };
 
@@ -66,9 +66,10 @@ hipError_t launch_sel_attn_fwd(const SelFwdParams& p, hipStream_t stream);
 size_t sel_attn_fwd_lds_bytes(int D, int T, int topk, int ring);
 int sel_attn_fwd_ring(int D, int T, int topk);   // ring slots that fit in LDS
 int sel_attn_fwd_rows_per_tile();   // query rows (T*G) one workgroup covers
-hipError_t launch_decode_prepass(const DecodeParams& p, hipStream_t stream);
-hipError_t launch_decode_split(const DecodeParams& p, int D, hipStream_t stream);
-int decode_waves_per_split();
+hipError_t launch_decode(const DecodeParams& p, int D, hipStream_t stream);
+int decode_waves_per_workgroup(int G);
+size_t decode_lds_bytes(int D, int G, int ts, int topk);
+int decode_table_slots(int D, int G, int topk);
 hipError_t launch_lse_merge(const MergeParams& p, int D, hipStream_t stream);
 
 }  // namespace fsa

@@ -8,110 +8,101 @@
 // sequence b, q head h, attends to the cache positions listed in
 // tok_idx[b, h / G, :], read as a set.
 //
-// Work is memory bound (each selected position costs one 2*d-byte K row and
-// one V row read from HBM and about 4*d*G flops), so the kernels are built
-// for many independent row loads in flight, not for the matrix cores:
-//   1. decode_prepass: one workgroup per (sequence, kv head) sorts the list in
-//      LDS, drops invalid positions and repeats, translates each position
-//      through the block table once and writes the compact list of physical
-//      cache rows (ascending) plus its length.
-//   2. decode_split: each wave takes a contiguous part of one compact list.
-//      Sixteen lanes cover one d-wide row (16 bytes each), so a wave works on
-//      four rows at a time and keeps 8 rows per lane group in flight.  Each
-//      lane group runs its own online softmax over its rows; the four groups
-//      are merged by cross-lane exchanges and the wave writes one partial
-//      (normalised O, LSE) per query head.
-//   3. lse_merge (lse_merge.hip) combines the partials.
+// The work is memory bound: each selected position costs one 2*d-byte K row
+// and one V row from HBM against about 4*d*G flops.  So the kernel is built
+// for many independent 256-byte row loads in flight, and the arithmetic stays
+// on the vector ALUs (bf16 dot2 for the scores).  One workgroup handles one
+// (sequence, kv head) list, or one part of it when the list is split:
+//   1. validate and translate: every list entry is checked (0 <= t <
+//      cache_seqlens[b], page slot and page id in range) and translated
+//      through the block table to a physical cache row, all in LDS;
+//   2. set semantics: an LDS hash table keyed by position keeps, for every
+//      distinct valid position, its first list entry (open addressing with
+//      linear probing, at most a quarter full when LDS allows); the kept rows
+//      are compacted in list order, so every workgroup of a split list derives
+//      the same compact list;
+//   3. each wave streams a contiguous share of the compact rows: sixteen
+//      lanes cover one row (16 or 8 bytes each), so a wave loads four rows per
+//      instruction and keeps kDecUnroll such groups of K and V in flight;
+//      each lane group runs its own online softmax;
+//   4. the lane groups, then the waves, are merged by logsumexp in LDS, and
+//      the workgroup writes O and LSE (or, for a split list, its normalised
+//      partial, combined afterwards by lse_merge.hip).
 #include "fsa_common.h"
 #include "fsa_params.h"
 
 namespace fsa {
 
-constexpr int kDecPrepassThreads = 1024;
-constexpr int kDecThreads = 256;
-constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kDecUnroll = 8;            // rows in flight per lane group
+constexpr int kDecUnroll = 8;            // row groups per batch (halved for G > 4)
+constexpr bool kDecDouble = false;       // two register batches in flight per wave
+constexpr int kDecWavesSmallG = 8;       // waves per workgroup for G <= 4
+constexpr int kDecMaxTopk = 8192;
+constexpr unsigned long long kDecEmpty = ~0ull;
 
+__host__ __device__ constexpr int dec_waves(int GM) { return GM <= 4 ? kDecWavesSmallG : (GM == 8 ? 8 : 4); }
 
-__global__ void __launch_bounds__(kDecPrepassThreads)
-decode_prepass_kernel(const DecodeParams p) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    int* key = reinterpret_cast<int*>(smem);                    // [sort_n]
-    int* wsum = key + p.sort_n;                                 // [32]
-    const int unit = blockIdx.x;                                // b * Hkv + g
-    const int b = unit / p.Hkv;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n = p.sort_n;
-    const int L = p.cache_seqlens[b];
-    const int32_t* lst = p.tok_idx + (int64_t)unit * p.topk;
-    const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
-    constexpr int kInvalid = 0x7fffffff;
+// LDS layout (bytes) of the decode workgroup for a hash table of ts slots.
+//   region 0: u64 table[ts] (steps 1-2): slot = position << 32 | list entry,
+//             reused for the wave partials (step 4): NW * GM records of D
+//             accumulator values + max + sum (fp32)
+//   i32 rows[topk]          compact physical cache rows
+//   i32 cnt[KMAX][NW]       kept entries per (chunk of NW*64 entries, wave)
+template <int D, int GM>
+struct DecLds {
+    static constexpr int NW = dec_waves(GM);
+    static constexpr int KMAX = kDecMaxTopk / (NW * 64);
+    static constexpr int kRec = D + 2;
+    __host__ __device__ static int region0(int ts) {
+        const int a = ts * 8, b = NW * GM * kRec * 4;
+        return ((a > b ? a : b) + 15) & ~15;
+    }
+    __host__ __device__ static int rows(int ts) { return region0(ts); }
+    __host__ __device__ static int cnt(int ts, int topk) { return rows(ts) + ((topk * 4 + 15) & ~15); }
+    __host__ __device__ static int bytes(int ts, int topk) { return cnt(ts, topk) + KMAX * NW * 4; }
+};
 
-    for (int e = tid; e < n; e += kDecPrepassThreads) {
-        int t = kInvalid;
-        if (e < p.topk) {
-            const int x = lst[e];
-            if (x >= 0 && x < L && x / p.page_size < p.max_pages) {
-                const int page = bt[x / p.page_size];
-                if (page >= 0 && page < p.num_pages) t = x;
-            }
-        }
-        key[e] = t;
-    }
-    __syncthreads();
-    // bitonic sort, ascending
-    for (int kk = 2; kk <= n; kk <<= 1) {
-        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-            for (int i = tid; i < n; i += kDecPrepassThreads) {
-                const int ixj = i ^ jj;
-                if (ixj > i) {
-                    const int a = key[i], c = key[ixj];
-                    const bool up = (i & kk) == 0;
-                    if ((a > c) == up) {
-                        key[i] = c;
-                        key[ixj] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-    // keep the first of each run of equal valid positions; compact in order
-    const int per = (n + kDecPrepassThreads - 1) / kDecPrepassThreads;
-    const int beg = tid * per;
-    int cnt = 0;
-    for (int i = beg; i < beg + per && i < n; ++i) {
-        const int t = key[i];
-        if (t != kInvalid && (i == 0 || key[i - 1] != t)) ++cnt;
-    }
-    // block exclusive scan of cnt
-    int incl = cnt;
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int wbase = 0;
-    for (int x = 0; x < wave; ++x) wbase += wsum[x];
-    int pos = wbase + incl - cnt;
-    int32_t* out = p.rows + (int64_t)unit * p.topk;
-    for (int i = beg; i < beg + per && i < n; ++i) {
-        const int t = key[i];
-        if (t != kInvalid && (i == 0 || key[i - 1] != t)) {
-            const int page = bt[t / p.page_size];
-            out[pos++] = page * p.page_size + (t % p.page_size);
-        }
-    }
-    if (tid == kDecPrepassThreads - 1) p.counts[unit] = wbase + incl;
+// Slot where the probe sequence of position x starts (multiplicative hash
+// scaled to [0, ts)).
+__device__ __forceinline__ int dec_hash(int x, int ts) {
+    return (int)(((unsigned long long)((uint32_t)x * 0x9E3779B1u) * (uint32_t)ts) >> 32);
+}
+
+// Sum over the 16 lanes of a row of the wave (every lane gets the total):
+// swap neighbours, swap pairs, mirror within 8, mirror within 16.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+    return x;
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
 // D: head dim (64 or 128); GM: query heads handled per kv head (>= G).
 template <int D, int GM>
-__global__ void __launch_bounds__(kDecThreads)
-decode_split_kernel(const DecodeParams p) {
+__global__ void __launch_bounds__(dec_waves(GM) * 64)
+decode_kernel(const DecodeParams p) {
+    using L = DecLds<D, GM>;
+    constexpr int NW = L::NW;
+    constexpr int NT = NW * 64;
     constexpr int DPL = D / 16;              // dims per lane (8 or 4)
     constexpr int WPL = DPL / 2;             // 32-bit words per lane
+    constexpr int U = GM > 4 ? kDecUnroll / 2 : kDecUnroll;
+
+    constexpr int KMAX = L::KMAX;            // list entries per thread, at most
+
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int ts = p.ts;
+    const int topk = p.topk;
+    unsigned long long* table = reinterpret_cast<unsigned long long*>(smem);
+    int* rows = reinterpret_cast<int*>(smem + L::rows(ts));
+    int* cnt = reinterpret_cast<int*>(smem + L::cnt(ts, topk));
+    float* mrg = reinterpret_cast<float*>(smem);
+
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15;                // 16 lanes share one cache row
     const int lg = lane >> 4;                // which of the wave's 4 rows
@@ -120,38 +111,115 @@ decode_split_kernel(const DecodeParams p) {
     const int b = unit / p.Hkv;
     const int g = unit % p.Hkv;
     const int G = p.G;
+    const int cs = p.cache_seqlens[b];
+    const int32_t* lst = p.tok_idx + (int64_t)unit * topk;
+    const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
+    const int nchunk = (topk + NT - 1) / NT;     // <= KMAX
 
-    const int n = p.counts[unit];
-    const int nparts = p.splits * kDecWaves;
-    const int part = split * kDecWaves + wave;
-    const int r_beg = (int)(((long long)n * part) / nparts);
-    const int r_end = (int)(((long long)n * (part + 1)) / nparts);
-    const int32_t* rows = p.rows + (int64_t)unit * p.topk;
+    // ---- 1. validate and translate this thread's entries e = k*NT + tid
+    for (int i = tid; i < ts; i += NT) table[i] = kDecEmpty;
+    int key[KMAX], phys[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const int e = k * NT + tid;
+        key[k] = -1;
+        phys[k] = 0;
+        if (k < nchunk && e < topk) {
+            const int x = lst[e];
+            if (x >= 0 && x < cs) {
+                const int slot = x / p.page_size;
+                if (slot < p.max_pages) {
+                    const int page = bt[slot];
+                    if (page >= 0 && page < p.num_pages) {
+                        key[k] = x;
+                        phys[k] = page * p.page_size + (x - slot * p.page_size);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
 
-    // the G query rows (fp32), this lane's DPL dims
-    float qv[GM][DPL];
+    // ---- 2. hash table: position -> (position, smallest list entry holding
+    // it).  A slot's position never changes once claimed, so all entries of
+    // one position meet in the same slot; probes are bounded by the table
+    // size (which exceeds topk).  Each entry remembers its slot.
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const int x = key[k];
+        int h = -1;
+        if (x >= 0) {
+            const unsigned long long mine =
+                ((unsigned long long)(uint32_t)x << 32) | (uint32_t)(k * NT + tid);
+            h = dec_hash(x, ts);
+            for (int probe = 0; probe < ts; ++probe) {
+                const unsigned long long old = atomicCAS(&table[h], kDecEmpty, mine);
+                if (old == kDecEmpty) break;
+                if ((uint32_t)(old >> 32) == (uint32_t)x) {
+                    atomicMin(&table[h], mine);
+                    break;
+                }
+                h = h + 1 == ts ? 0 : h + 1;
+            }
+        }
+        key[k] = h;                              // now: the entry's slot, or -1
+    }
+    __syncthreads();
+
+    // ---- keep each position's first entry; compact the rows in list order
+    unsigned long long kept = 0ull;              // bit k: this thread's entry k is kept
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        bool keep = false;
+        if (key[k] >= 0) keep = (uint32_t)table[key[k]] == (uint32_t)(k * NT + tid);
+        kept |= (unsigned long long)keep << k;
+        const unsigned long long bal = __ballot(keep);
+        if (k < nchunk && lane == 0) cnt[k * NW + wave] = __popcll(bal);
+    }
+    __syncthreads();
+    int n = 0;
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        if (k < nchunk) {
+            const bool keep = (kept >> k) & 1ull;
+            const int rank = __popcll(__ballot(keep) & below);
+            int wbase = 0, ctot = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int cw = cnt[k * NW + w];
+                wbase += w < wave ? cw : 0;
+                ctot += cw;
+            }
+            if (keep) rows[n + wbase + rank] = phys[k];
+            n += ctot;
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. this wave's share of this workgroup's part of the compact list
+    const int r_lo = (int)(((long long)n * split) / p.splits);
+    const int r_hi = (int)(((long long)n * (split + 1)) / p.splits);
+    const int wb = r_lo + (int)(((long long)(r_hi - r_lo) * wave) / NW);
+    const int we = r_lo + (int)(((long long)(r_hi - r_lo) * (wave + 1)) / NW);
+
+    uint32_t qw[GM][WPL];                    // this lane's dims of the G query rows (bf16 pairs)
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
         if (h < G) {
             const uint16_t* qr = p.q + ((int64_t)b * p.Hq + g * G + h) * D + lr * DPL;
-            if constexpr (DPL == 8) {
+            if constexpr (WPL == 4) {
                 const u32x4_t w = *reinterpret_cast<const u32x4_t*>(qr);
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    qv[h][2 * x] = bf16_lo(w[x]);
-                    qv[h][2 * x + 1] = bf16_hi(w[x]);
-                }
+                for (int x = 0; x < 4; ++x) qw[h][x] = w[x];
             } else {
                 const u32x2_t w = *reinterpret_cast<const u32x2_t*>(qr);
 #pragma unroll
-                for (int x = 0; x < 2; ++x) {
-                    qv[h][2 * x] = bf16_lo(w[x]);
-                    qv[h][2 * x + 1] = bf16_hi(w[x]);
-                }
+                for (int x = 0; x < 2; ++x) qw[h][x] = w[x];
             }
         } else {
 #pragma unroll
-            for (int x = 0; x < DPL; ++x) qv[h][x] = 0.f;
+            for (int x = 0; x < WPL; ++x) qw[h][x] = 0u;
         }
     }
 
@@ -168,52 +236,48 @@ decode_split_kernel(const DecodeParams p) {
     const uint16_t* kbase = p.kc + (int64_t)g * D + lr * DPL;
     const uint16_t* vbase = p.vc + (int64_t)g * D + lr * DPL;
 
-    for (int r0 = r_beg; r0 < r_end; r0 += 4 * kDecUnroll) {
-        uint32_t kw[kDecUnroll][WPL], vw[kDecUnroll][WPL];
-        bool ok[kDecUnroll];
+    // Rows r0 + 4u + lg, u < U, are one batch; two batches alternate in
+    // registers so the next batch's loads are in flight while one is computed.
+    auto issue = [&](uint32_t (&kw)[U][WPL], uint32_t (&vw)[U][WPL], int r0) {
 #pragma unroll
-        for (int u = 0; u < kDecUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int r = r0 + u * 4 + lg;
-            ok[u] = r < r_end;
-            const int64_t cr = ok[u] ? rows[r] : 0;
+            const int64_t cr = r < we ? rows[r] : 0;     // past the share: row 0, ignored
             const uint16_t* kp = kbase + cr * row_stride;
             const uint16_t* vp = vbase + cr * row_stride;
             if constexpr (WPL == 4) {
-                u32x4_t a = ok[u] ? *reinterpret_cast<const u32x4_t*>(kp) : u32x4_t{0u, 0u, 0u, 0u};
-                u32x4_t c = ok[u] ? *reinterpret_cast<const u32x4_t*>(vp) : u32x4_t{0u, 0u, 0u, 0u};
+                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kp);
+                const u32x4_t c = *reinterpret_cast<const u32x4_t*>(vp);
 #pragma unroll
                 for (int x = 0; x < 4; ++x) { kw[u][x] = a[x]; vw[u][x] = c[x]; }
             } else {
-                u32x2_t a = ok[u] ? *reinterpret_cast<const u32x2_t*>(kp) : u32x2_t{0u, 0u};
-                u32x2_t c = ok[u] ? *reinterpret_cast<const u32x2_t*>(vp) : u32x2_t{0u, 0u};
+                const u32x2_t a = *reinterpret_cast<const u32x2_t*>(kp);
+                const u32x2_t c = *reinterpret_cast<const u32x2_t*>(vp);
 #pragma unroll
                 for (int x = 0; x < 2; ++x) { kw[u][x] = a[x]; vw[u][x] = c[x]; }
             }
         }
-        // scores of the lane group's rows, one per query head
-        float s[kDecUnroll][GM];
+    };
+    auto consume = [&](const uint32_t (&kw)[U][WPL], const uint32_t (&vw)[U][WPL], int r0) {
+        // scores (log2 units) of the lane group's rows, one per query head
+        float s[U][GM];
 #pragma unroll
-        for (int u = 0; u < kDecUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
+            const bool ok = r0 + u * 4 + lg < we;
 #pragma unroll
             for (int h = 0; h < GM; ++h) {
                 float d = 0.f;
 #pragma unroll
-                for (int x = 0; x < WPL; ++x) {
-                    d = fmaf(qv[h][2 * x], bf16_lo(kw[u][x]), d);
-                    d = fmaf(qv[h][2 * x + 1], bf16_hi(kw[u][x]), d);
-                }
-                d += __shfl_xor(d, 1);
-                d += __shfl_xor(d, 2);
-                d += __shfl_xor(d, 4);
-                d += __shfl_xor(d, 8);
-                s[u][h] = ok[u] ? d * p.scale_log2 : -INFINITY;
+                for (int x = 0; x < WPL; ++x) d = dot2_bf16(qw[h][x], kw[u][x], d);
+                d = row16_sum(d);
+                s[u][h] = ok ? d * p.scale_log2 : -INFINITY;
             }
         }
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
             float mb = s[0][h];
 #pragma unroll
-            for (int u = 1; u < kDecUnroll; ++u) mb = fmaxf(mb, s[u][h]);
+            for (int u = 1; u < U; ++u) mb = fmaxf(mb, s[u][h]);
             const float m_new = fmaxf(m_run[h], mb);
             const float msub = m_new == -INFINITY ? 0.f : m_new;
             const float alpha = fast_exp2(m_run[h] - msub);
@@ -222,7 +286,7 @@ decode_split_kernel(const DecodeParams p) {
 #pragma unroll
             for (int x = 0; x < DPL; ++x) acc[h][x] *= alpha;
 #pragma unroll
-            for (int u = 0; u < kDecUnroll; ++u) {
+            for (int u = 0; u < U; ++u) {
                 const float pr = fast_exp2(s[u][h] - msub);
                 ls += pr;
 #pragma unroll
@@ -233,9 +297,29 @@ decode_split_kernel(const DecodeParams p) {
             }
             l_run[h] = l_run[h] * alpha + ls;
         }
+    };
+    constexpr int B = 4 * U;                 // rows per batch
+    if constexpr (kDecDouble) {
+        uint32_t ka[U][WPL], va[U][WPL], kb2[U][WPL], vb2[U][WPL];
+        if (wb < we) issue(ka, va, wb);
+        for (int r0 = wb; r0 < we; r0 += 2 * B) {
+            if (r0 + B < we) issue(kb2, vb2, r0 + B);
+            consume(ka, va, r0);
+            if (r0 + B >= we) break;
+            if (r0 + 2 * B < we) issue(ka, va, r0 + 2 * B);
+            consume(kb2, vb2, r0 + B);
+        }
+    } else {
+        for (int r0 = wb; r0 < we; r0 += B) {
+            uint32_t ka[U][WPL], va[U][WPL];
+            issue(ka, va, r0);
+            consume(ka, va, r0);
+        }
     }
 
-    // merge the four lane groups of the wave, then write this wave's partial
+    // ---- 4. merge the wave's four lane groups, then the workgroup's waves.
+    // Region 0 (the hash table) is free: its last reads precede the barrier
+    // that ended step 2's compaction.
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
         float m = m_run[h];
@@ -246,65 +330,99 @@ decode_split_kernel(const DecodeParams p) {
         float l = l_run[h] * sc;
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
+        float* rec = mrg + (wave * GM + h) * L::kRec;
 #pragma unroll
         for (int x = 0; x < DPL; ++x) {
             float a = acc[h][x] * sc;
             a += __shfl_xor(a, 16);
             a += __shfl_xor(a, 32);
-            acc[h][x] = a;
+            if (lg == 0) rec[lr * DPL + x] = a;
         }
-        if (h < G) {
-            const float inv = l > 0.f ? 1.f / l : 0.f;
-            const float lse_v = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
-            const int64_t prow = (int64_t)part * p.batch * p.Hq + (int64_t)b * p.Hq + g * G + h;
-            if (lg == 0) {
-                float* o = p.part_o + prow * D + lr * DPL;
+        if (lane == 0) {
+            rec[D] = m;
+            rec[D + 1] = l;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < G * (D / 2); i += NT) {
+        const int h = i / (D / 2);
+        const int d = 2 * (i - h * (D / 2));
+        float M = -INFINITY;
 #pragma unroll
-                for (int x = 0; x < DPL; x += 4) {
-                    *reinterpret_cast<f32x4_t*>(o + x) =
-                        f32x4_t{acc[h][x] * inv, acc[h][x + 1] * inv, acc[h][x + 2] * inv,
-                                acc[h][x + 3] * inv};
-                }
-                if (lr == 0) p.part_lse[prow] = lse_v;
-            }
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, mrg[(w * GM + h) * L::kRec + D]);
+        const float msub = M == -INFINITY ? 0.f : M;
+        float Ls = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float* rec = mrg + (w * GM + h) * L::kRec;
+            const float sc = fast_exp2(rec[D] - msub);
+            Ls = fmaf(rec[D + 1], sc, Ls);
+            o0 = fmaf(rec[d], sc, o0);
+            o1 = fmaf(rec[d + 1], sc, o1);
+        }
+        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+        const float lse_v = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+        const int64_t row = (int64_t)b * p.Hq + g * G + h;
+        if (p.splits == 1) {
+            *reinterpret_cast<uint32_t*>(p.out + row * D + d) = pack_bf16x2(o0 * inv, o1 * inv);
+            if (p.lse != nullptr && d == 0) p.lse[row] = lse_v;
+        } else {
+            const int64_t prow = (int64_t)split * p.batch * p.Hq + row;
+            *reinterpret_cast<f32x2_t*>(p.part_o + prow * D + d) = f32x2_t{o0 * inv, o1 * inv};
+            if (d == 0) p.part_lse[prow] = lse_v;
         }
     }
 }
 
-hipError_t launch_decode_prepass(const DecodeParams& p, hipStream_t stream) {
-    const size_t lds = (size_t)p.sort_n * 4 + 32 * 4;
-    static bool attr_set = false;
+template <int D, int GM>
+static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
+    static bool attr_set = false;   // idempotent; racing threads set the same value
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_prepass_kernel),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, GM>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(decode_prepass_kernel, dim3(p.batch * p.Hkv), dim3(kDecPrepassThreads), lds,
-                       stream, p);
-    return hipGetLastError();
-}
-
-template <int D, int GM>
-static hipError_t launch_split_t(const DecodeParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_split_kernel<D, GM>), dim3(p.batch * p.Hkv * p.splits),
-                       dim3(kDecThreads), 0, stream, p);
+    const size_t lds = DecLds<D, GM>::bytes(p.ts, p.topk);
+    hipLaunchKernelGGL((decode_kernel<D, GM>), dim3(p.batch * p.Hkv * p.splits),
+                       dim3(DecLds<D, GM>::NW * 64), lds, stream, p);
     return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_split_d(const DecodeParams& p, hipStream_t stream) {
-    if (p.G <= 1) return launch_split_t<D, 1>(p, stream);
-    if (p.G <= 2) return launch_split_t<D, 2>(p, stream);
-    if (p.G <= 4) return launch_split_t<D, 4>(p, stream);
-    if (p.G <= 8) return launch_split_t<D, 8>(p, stream);
-    return launch_split_t<D, 16>(p, stream);
+static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
+    if (p.G <= 1) return launch_decode_t<D, 1>(p, stream);
+    if (p.G <= 2) return launch_decode_t<D, 2>(p, stream);
+    if (p.G <= 4) return launch_decode_t<D, 4>(p, stream);
+    if (p.G <= 8) return launch_decode_t<D, 8>(p, stream);
+    return launch_decode_t<D, 16>(p, stream);
 }
 
-hipError_t launch_decode_split(const DecodeParams& p, int D, hipStream_t stream) {
-    return D == 64 ? launch_split_d<64>(p, stream) : launch_split_d<128>(p, stream);
+hipError_t launch_decode(const DecodeParams& p, int D, hipStream_t stream) {
+    return D == 64 ? launch_decode_d<64>(p, stream) : launch_decode_d<128>(p, stream);
 }
 
-int decode_waves_per_split() { return kDecWaves; }
+static int group_bucket(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16; }
+
+int decode_waves_per_workgroup(int G) { return dec_waves(group_bucket(G)); }
+
+size_t decode_lds_bytes(int D, int G, int ts, int topk) {
+    switch (group_bucket(G)) {
+        case 1: return D == 64 ? DecLds<64, 1>::bytes(ts, topk) : DecLds<128, 1>::bytes(ts, topk);
+        case 2: return D == 64 ? DecLds<64, 2>::bytes(ts, topk) : DecLds<128, 2>::bytes(ts, topk);
+        case 4: return D == 64 ? DecLds<64, 4>::bytes(ts, topk) : DecLds<128, 4>::bytes(ts, topk);
+        case 8: return D == 64 ? DecLds<64, 8>::bytes(ts, topk) : DecLds<128, 8>::bytes(ts, topk);
+        default: return D == 64 ? DecLds<64, 16>::bytes(ts, topk) : DecLds<128, 16>::bytes(ts, topk);
+    }
+}
+
+// Hash table slots: 4 per list entry (short probe chains), fewer when LDS is
+// short; always more than topk.
+int decode_table_slots(int D, int G, int topk) {
+    int ts = 4 * topk;
+    if (ts < 64) ts = 64;
+    while (ts > topk + 64 && decode_lds_bytes(D, G, ts, topk) > 160 * 1024) ts -= 64;
+    return ts;
+}
 
 }  // namespace fsa
