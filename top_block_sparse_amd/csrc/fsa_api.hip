@@ -70,12 +70,14 @@ PrefillPlan plan_prefill(int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_
     return pl;
 }
 
-// Enough waves to give every CU about 16, with at least 32 rows per wave.
+// Enough workgroups to give every CU one (each splits list entries among
+// its waves; a split list repeats the set computation in every part), with
+// at least 32 entries per wave.
 int decode_auto_splits(int32_t batch, int32_t Hq, int32_t Hkv, int32_t topk) {
     const long long units = (long long)batch * Hkv;
     if (units <= 0 || Hkv <= 0) return 1;
     const int waves = fsa::decode_waves_per_workgroup(Hq / Hkv);
-    long long s = (4096 + units * waves - 1) / (units * waves);
+    long long s = (256 * 8 + units * waves - 1) / (units * waves);
     const long long cap = topk / (waves * 32) > 1 ? topk / (waves * 32) : 1;
     if (s > cap) s = cap;
     if (s > kMaxSplitsDecode) s = kMaxSplitsDecode;

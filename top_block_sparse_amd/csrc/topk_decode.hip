@@ -18,13 +18,16 @@
 //      through the block table to a physical cache row, all in LDS;
 //   2. set semantics: an LDS hash table keyed by position keeps, for every
 //      distinct valid position, its first list entry (open addressing with
-//      linear probing, at most a quarter full when LDS allows); the kept rows
-//      are compacted in list order, so every workgroup of a split list derives
-//      the same compact list;
-//   3. each wave streams a contiguous share of the compact rows: sixteen
-//      lanes cover one row (16 or 8 bytes each), so a wave loads four rows per
-//      instruction and keeps kDecUnroll such groups of K and V in flight;
-//      each lane group runs its own online softmax;
+//      linear probing, at most a quarter full when LDS allows); every other
+//      entry is marked skipped.  A split list is cut by entry index, so the
+//      parts are disjoint whatever the list holds;
+//   3. the waves stream the workgroup's part in batches of 4*kDecUnroll
+//      entries taken from a shared counter (so they finish together):
+//      sixteen lanes cover one row (16 or 8 bytes each), so a wave loads four
+//      rows per instruction and keeps kDecUnroll such groups of K and V in
+//      flight; each lane group runs its own online softmax; the probabilities are
+//      rounded to bf16 for the P.V products (bf16 dot2 with fp32
+//      accumulation), the row sums stay fp32;
 //   4. the lane groups, then the waves, are merged by logsumexp in LDS, and
 //      the workgroup writes O and LSE (or, for a split list, its normalised
 //      partial, combined afterwards by lse_merge.hip).
@@ -34,9 +37,9 @@
 namespace fsa {
 
 constexpr int kDecUnroll = 8;            // row groups per batch (halved for G > 4)
-constexpr bool kDecDouble = false;       // two register batches in flight per wave
 constexpr int kDecWavesSmallG = 8;       // waves per workgroup for G <= 4
 constexpr int kDecMaxTopk = 8192;
+constexpr int kDecBtLds = 2048;          // block-table rows up to this length are staged in LDS
 constexpr unsigned long long kDecEmpty = ~0ull;
 
 __host__ __device__ constexpr int dec_waves(int GM) { return GM <= 4 ? kDecWavesSmallG : (GM == 8 ? 8 : 4); }
@@ -45,8 +48,9 @@ __host__ __device__ constexpr int dec_waves(int GM) { return GM <= 4 ? kDecWaves
 //   region 0: u64 table[ts] (steps 1-2): slot = position << 32 | list entry,
 //             reused for the wave partials (step 4): NW * GM records of D
 //             accumulator values + max + sum (fp32)
-//   i32 rows[topk]          compact physical cache rows
-//   i32 cnt[KMAX][NW]       kept entries per (chunk of NW*64 entries, wave)
+//   i32 rows[topk]          physical cache row of each entry (-1: skipped)
+//   i32 next                next batch of entries to stream
+//   i32 btl[kDecBtLds]      the sequence's block-table row (when it fits)
 template <int D, int GM>
 struct DecLds {
     static constexpr int NW = dec_waves(GM);
@@ -57,8 +61,9 @@ struct DecLds {
         return ((a > b ? a : b) + 15) & ~15;
     }
     __host__ __device__ static int rows(int ts) { return region0(ts); }
-    __host__ __device__ static int cnt(int ts, int topk) { return rows(ts) + ((topk * 4 + 15) & ~15); }
-    __host__ __device__ static int bytes(int ts, int topk) { return cnt(ts, topk) + KMAX * NW * 4; }
+    __host__ __device__ static int next(int ts, int topk) { return rows(ts) + ((topk * 4 + 15) & ~15); }
+    __host__ __device__ static int btl(int ts, int topk) { return next(ts, topk) + 16; }
+    __host__ __device__ static int bytes(int ts, int topk) { return btl(ts, topk) + kDecBtLds * 4; }
 };
 
 // Slot where the probe sequence of position x starts (multiplicative hash
@@ -100,7 +105,8 @@ decode_kernel(const DecodeParams p) {
     const int topk = p.topk;
     unsigned long long* table = reinterpret_cast<unsigned long long*>(smem);
     int* rows = reinterpret_cast<int*>(smem + L::rows(ts));
-    int* cnt = reinterpret_cast<int*>(smem + L::cnt(ts, topk));
+    int* next = reinterpret_cast<int*>(smem + L::next(ts, topk));
+    int* btl = reinterpret_cast<int*>(smem + L::btl(ts, topk));
     float* mrg = reinterpret_cast<float*>(smem);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -116,29 +122,96 @@ decode_kernel(const DecodeParams p) {
     const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
     const int nchunk = (topk + NT - 1) / NT;     // <= KMAX
 
-    // ---- 1. validate and translate this thread's entries e = k*NT + tid
+    // ---- 1. validate and translate this thread's entries e = k*NT + tid.
+    // Straight-line passes (all list loads together with the block-table row,
+    // then the lookups) so the loads of different entries are in flight
+    // together.
     for (int i = tid; i < ts; i += NT) table[i] = kDecEmpty;
     int key[KMAX], phys[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         const int e = k * NT + tid;
-        key[k] = -1;
-        phys[k] = 0;
-        if (k < nchunk && e < topk) {
-            const int x = lst[e];
-            if (x >= 0 && x < cs) {
-                const int slot = x / p.page_size;
-                if (slot < p.max_pages) {
-                    const int page = bt[slot];
-                    if (page >= 0 && page < p.num_pages) {
-                        key[k] = x;
-                        phys[k] = page * p.page_size + (x - slot * p.page_size);
-                    }
-                }
+        key[k] = lst[e < topk ? e : topk - 1];
+    }
+    const bool bt_in_lds = p.max_pages <= kDecBtLds;
+    if (bt_in_lds)
+        for (int i = tid; i < p.max_pages; i += NT) btl[i] = bt[i];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const int x = key[k];
+        const int slot = x / p.page_size;
+        const bool ok = k * NT + tid < topk && x >= 0 && x < cs && slot < p.max_pages;
+        key[k] = ok ? x : -1;
+        phys[k] = ok ? slot : 0;
+    }
+    if (bt_in_lds) {
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) phys[k] = btl[phys[k]];   // page id, checked below
+    } else {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) phys[k] = bt[phys[k]];
+    }
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const int x = key[k];
+        const int page = phys[k];
+        const bool ok = x >= 0 && page >= 0 && page < p.num_pages;
+        const int slot = x / p.page_size;
+        phys[k] = ok ? page * p.page_size + (x - slot * p.page_size) : 0;
+        key[k] = ok ? x : -1;
+        const int e = k * NT + tid;
+        if (k < nchunk && e < topk) rows[e] = ok ? phys[k] : -1;
+    }
+    if (tid == 0) *next = NW;                    // batches 0..NW-1: each wave's first
+    __syncthreads();
+
+    // ---- 3 (start). The waves stream the workgroup's part of the list in
+    // batches of 4*U entries taken from a shared counter, so they finish
+    // together.  Each wave's first batch is loaded now, so its loads are in
+    // flight during the set computation; its repeats are masked afterwards.
+    const int r_lo = (int)(((long long)topk * split) / p.splits);
+    const int r_hi = (int)(((long long)topk * (split + 1)) / p.splits);
+    constexpr int B = 4 * U;                 // entries per batch
+    const int nbatch = (r_hi - r_lo + B - 1) / B;
+    const int64_t row_stride = (int64_t)p.Hkv * D;   // elements between cache rows
+    const uint16_t* kbase = p.kc + (int64_t)g * D + lr * DPL;
+    const uint16_t* vbase = p.vc + (int64_t)g * D + lr * DPL;
+    // Entries r0 + 4u + lg, u < U, are one batch.  Bit u of the mask: that
+    // entry is a row to attend to (inside the part, valid and not a repeat).
+    auto okmask = [&](int r0) {
+        uint32_t okm = 0u;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = r0 + u * 4 + lg;
+            okm |= (uint32_t)(r < r_hi && rows[r] >= 0) << u;
+        }
+        return okm;
+    };
+    auto issue = [&](uint32_t (&kw)[U][WPL], uint32_t (&vw)[U][WPL], int r0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = r0 + u * 4 + lg;
+            const int row = r < r_hi ? rows[r] : -1;
+            const int64_t cr = row >= 0 ? row : 0;     // skipped entries read row 0, ignored
+            const uint16_t* kp = kbase + cr * row_stride;
+            const uint16_t* vp = vbase + cr * row_stride;
+            if constexpr (WPL == 4) {
+                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kp);
+                const u32x4_t c = *reinterpret_cast<const u32x4_t*>(vp);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) { kw[u][x] = a[x]; vw[u][x] = c[x]; }
+            } else {
+                const u32x2_t a = *reinterpret_cast<const u32x2_t*>(kp);
+                const u32x2_t c = *reinterpret_cast<const u32x2_t*>(vp);
+#pragma unroll
+                for (int x = 0; x < 2; ++x) { kw[u][x] = a[x]; vw[u][x] = c[x]; }
             }
         }
-    }
-    __syncthreads();
+    };
+    uint32_t ka[U][WPL], va[U][WPL];
+    int bi = wave;
+    if (bi < nbatch) issue(ka, va, r_lo + bi * B);
 
     // ---- 2. hash table: position -> (position, smallest list entry holding
     // it).  A slot's position never changes once claimed, so all entries of
@@ -166,42 +239,14 @@ decode_kernel(const DecodeParams p) {
     }
     __syncthreads();
 
-    // ---- keep each position's first entry; compact the rows in list order
-    unsigned long long kept = 0ull;              // bit k: this thread's entry k is kept
+    // ---- keep each position's first entry: a valid entry that repeats an
+    // earlier one is marked skipped (rows[e] = -1)
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-        bool keep = false;
-        if (key[k] >= 0) keep = (uint32_t)table[key[k]] == (uint32_t)(k * NT + tid);
-        kept |= (unsigned long long)keep << k;
-        const unsigned long long bal = __ballot(keep);
-        if (k < nchunk && lane == 0) cnt[k * NW + wave] = __popcll(bal);
+        const int e = k * NT + tid;
+        if (key[k] >= 0 && (uint32_t)table[key[k]] != (uint32_t)e) rows[e] = -1;
     }
     __syncthreads();
-    int n = 0;
-    const unsigned long long below = (1ull << lane) - 1ull;
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        if (k < nchunk) {
-            const bool keep = (kept >> k) & 1ull;
-            const int rank = __popcll(__ballot(keep) & below);
-            int wbase = 0, ctot = 0;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const int cw = cnt[k * NW + w];
-                wbase += w < wave ? cw : 0;
-                ctot += cw;
-            }
-            if (keep) rows[n + wbase + rank] = phys[k];
-            n += ctot;
-        }
-    }
-    __syncthreads();
-
-    // ---- 3. this wave's share of this workgroup's part of the compact list
-    const int r_lo = (int)(((long long)n * split) / p.splits);
-    const int r_hi = (int)(((long long)n * (split + 1)) / p.splits);
-    const int wb = r_lo + (int)(((long long)(r_hi - r_lo) * wave) / NW);
-    const int we = r_lo + (int)(((long long)(r_hi - r_lo) * (wave + 1)) / NW);
 
     uint32_t qw[GM][WPL];                    // this lane's dims of the G query rows (bf16 pairs)
 #pragma unroll
@@ -232,53 +277,44 @@ decode_kernel(const DecodeParams p) {
         for (int x = 0; x < DPL; ++x) acc[h][x] = 0.f;
     }
 
-    const int64_t row_stride = (int64_t)p.Hkv * D;   // elements between cache rows
-    const uint16_t* kbase = p.kc + (int64_t)g * D + lr * DPL;
-    const uint16_t* vbase = p.vc + (int64_t)g * D + lr * DPL;
-
-    // Rows r0 + 4u + lg, u < U, are one batch; two batches alternate in
-    // registers so the next batch's loads are in flight while one is computed.
-    auto issue = [&](uint32_t (&kw)[U][WPL], uint32_t (&vw)[U][WPL], int r0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int r = r0 + u * 4 + lg;
-            const int64_t cr = r < we ? rows[r] : 0;     // past the share: row 0, ignored
-            const uint16_t* kp = kbase + cr * row_stride;
-            const uint16_t* vp = vbase + cr * row_stride;
-            if constexpr (WPL == 4) {
-                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kp);
-                const u32x4_t c = *reinterpret_cast<const u32x4_t*>(vp);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) { kw[u][x] = a[x]; vw[u][x] = c[x]; }
-            } else {
-                const u32x2_t a = *reinterpret_cast<const u32x2_t*>(kp);
-                const u32x2_t c = *reinterpret_cast<const u32x2_t*>(vp);
-#pragma unroll
-                for (int x = 0; x < 2; ++x) { kw[u][x] = a[x]; vw[u][x] = c[x]; }
-            }
-        }
-    };
-    auto consume = [&](const uint32_t (&kw)[U][WPL], const uint32_t (&vw)[U][WPL], int r0) {
-        // scores (log2 units) of the lane group's rows, one per query head
+    auto consume = [&](const uint32_t (&kw)[U][WPL], const uint32_t (&vw)[U][WPL], uint32_t okm) {
+        // raw scores q.k of the lane group's rows, one per query head
         float s[U][GM];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const bool ok = r0 + u * 4 + lg < we;
 #pragma unroll
             for (int h = 0; h < GM; ++h) {
                 float d = 0.f;
 #pragma unroll
                 for (int x = 0; x < WPL; ++x) d = dot2_bf16(qw[h][x], kw[u][x], d);
-                d = row16_sum(d);
-                s[u][h] = ok ? d * p.scale_log2 : -INFINITY;
+                s[u][h] = row16_sum(d);
             }
         }
+        if (__builtin_amdgcn_ballot_w64(okm != (1u << U) - 1u) != 0ull) {   // skipped entries
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (((okm >> u) & 1u) == 0u) {
+#pragma unroll
+                    for (int h = 0; h < GM; ++h) s[u][h] = -INFINITY;
+                }
+        }
+        // V of rows 2j and 2j+1 interleaved per dim: bf16 pairs for dot2
+        uint32_t vlo[U / 2][WPL], vhi[U / 2][WPL];
+#pragma unroll
+        for (int j = 0; j < U / 2; ++j) {
+#pragma unroll
+            for (int x = 0; x < WPL; ++x) {
+                vlo[j][x] = __builtin_amdgcn_perm(vw[2 * j + 1][x], vw[2 * j][x], 0x05040100u);
+                vhi[j][x] = __builtin_amdgcn_perm(vw[2 * j + 1][x], vw[2 * j][x], 0x07060302u);
+            }
+        }
+        const float c = p.scale_log2;            // > 0: the max commutes with the scaling
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
             float mb = s[0][h];
 #pragma unroll
             for (int u = 1; u < U; ++u) mb = fmaxf(mb, s[u][h]);
-            const float m_new = fmaxf(m_run[h], mb);
+            const float m_new = fmaxf(m_run[h], mb * c);
             const float msub = m_new == -INFINITY ? 0.f : m_new;
             const float alpha = fast_exp2(m_run[h] - msub);
             m_run[h] = m_new;
@@ -286,35 +322,31 @@ decode_kernel(const DecodeParams p) {
 #pragma unroll
             for (int x = 0; x < DPL; ++x) acc[h][x] *= alpha;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float pr = fast_exp2(s[u][h] - msub);
-                ls += pr;
+            for (int j = 0; j < U / 2; ++j) {
+                const float p0 = fast_exp2(fmaf(s[2 * j][h], c, -msub));
+                const float p1 = fast_exp2(fmaf(s[2 * j + 1][h], c, -msub));
+                ls += p0 + p1;
+                const uint32_t pp = pack_bf16x2(p0, p1);
 #pragma unroll
                 for (int x = 0; x < WPL; ++x) {
-                    acc[h][2 * x] = fmaf(pr, bf16_lo(vw[u][x]), acc[h][2 * x]);
-                    acc[h][2 * x + 1] = fmaf(pr, bf16_hi(vw[u][x]), acc[h][2 * x + 1]);
+                    acc[h][2 * x] = dot2_bf16(pp, vlo[j][x], acc[h][2 * x]);
+                    acc[h][2 * x + 1] = dot2_bf16(pp, vhi[j][x], acc[h][2 * x + 1]);
                 }
             }
             l_run[h] = l_run[h] * alpha + ls;
         }
     };
-    constexpr int B = 4 * U;                 // rows per batch
-    if constexpr (kDecDouble) {
-        uint32_t ka[U][WPL], va[U][WPL], kb2[U][WPL], vb2[U][WPL];
-        if (wb < we) issue(ka, va, wb);
-        for (int r0 = wb; r0 < we; r0 += 2 * B) {
-            if (r0 + B < we) issue(kb2, vb2, r0 + B);
-            consume(ka, va, r0);
-            if (r0 + B >= we) break;
-            if (r0 + 2 * B < we) issue(ka, va, r0 + 2 * B);
-            consume(kb2, vb2, r0 + B);
-        }
-    } else {
-        for (int r0 = wb; r0 < we; r0 += B) {
-            uint32_t ka[U][WPL], va[U][WPL];
-            issue(ka, va, r0);
-            consume(ka, va, r0);
-        }
+    auto grab = [&]() {
+        int t = 0;
+        if (lane == 0) t = __hip_atomic_fetch_add(next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return __builtin_amdgcn_readfirstlane(t);
+    };
+    while (bi < nbatch) {
+        const uint32_t okm = okmask(r_lo + bi * B);
+        const int bn = grab();                   // next batch, fetched while the loads fly
+        consume(ka, va, okm);
+        bi = bn;
+        if (bi < nbatch) issue(ka, va, r_lo + bi * B);
     }
 
     // ---- 4. merge the wave's four lane groups, then the workgroup's waves.
