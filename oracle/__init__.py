@@ -51,6 +51,11 @@ def _load():
         lib.oracle_topk_decode.restype = ctypes.c_int
         lib.oracle_topk_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
                                            i32, f64, P, i64, P, P]
+        lib.oracle_topk_decode_fp8.restype = ctypes.c_int
+        lib.oracle_topk_decode_fp8.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                               i32, i32, i32, f64, P, i64, P, P]
+        lib.oracle_e4m3_value.restype = f64
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
         lib.oracle_lse_merge.restype = None
         lib.oracle_lse_merge.argtypes = [i64, i32, P, P, P, P]
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -133,6 +138,56 @@ def topk_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, t
                                 lse.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_topk_decode rejected its arguments")
+    return out, lse
+
+
+def e4m3_value(byte: int) -> float:
+    """The value an FP8 E4M3 byte stands for (NaN for the two NaN codes)."""
+    return float(_load().oracle_e4m3_value(int(byte) & 0xFF))
+
+
+def topk_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, k_descale,
+                    v_descale, tok_idx, block_table, cache_seqlens,
+                    softmax_scale: Optional[float] = None, seqs=None):
+    """Top-k decode over an FP8 E4M3 paged cache (uint8 bytes) with per
+    (sequence, kv head) dequantisation factors (float [batch, Hkv] or None).
+    Returns ``(out [n,Hq,d], lse [n,Hq])`` float64."""
+    lib = _load()
+    batch, Hq, d = q.shape
+    num_pages, page_size, Hkv, _ = k_cache.shape
+    assert k_cache.dtype == torch.uint8 and v_cache.dtype == torch.uint8
+    tok = _i32(tok_idx)
+    bt = _i32(block_table)
+    cs = _i32(cache_seqlens)
+    topk = tok.shape[-1]
+    max_pages = bt.shape[1]
+    scale = (1.0 / np.sqrt(d)) if softmax_scale is None else float(softmax_scale)
+    qb = _bits(q)
+    kb, vb = k_cache.contiguous(), v_cache.contiguous()
+
+    def f32(x):
+        if x is None:
+            return None
+        if isinstance(x, torch.Tensor):
+            x = x.cpu().numpy()
+        return np.ascontiguousarray(np.asarray(x, dtype=np.float32).reshape(batch * Hkv))
+
+    kd, vd = f32(k_descale), f32(v_descale)
+    if seqs is None:
+        sp, n = None, batch
+    else:
+        sarr = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        sp, n = sarr.ctypes.data, sarr.size
+    out = np.zeros((n, Hq, d), dtype=np.float64)
+    lse = np.zeros((n, Hq), dtype=np.float64)
+    rc = lib.oracle_topk_decode_fp8(qb.data_ptr(), kb.data_ptr(), vb.data_ptr(),
+                                    None if kd is None else kd.ctypes.data,
+                                    None if vd is None else vd.ctypes.data, tok.ctypes.data,
+                                    bt.ctypes.data, cs.ctypes.data, batch, Hq, Hkv, d, page_size,
+                                    max_pages, num_pages, topk, scale, sp, n, out.ctypes.data,
+                                    lse.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_topk_decode_fp8 rejected its arguments")
     return out, lse
 
 

@@ -247,6 +247,118 @@ int oracle_topk_decode(const uint16_t* q, const uint16_t* k_cache, const uint16_
 }
 
 /*
+ * FP8 E4M3 byte -> value, exactly (the torch.float8_e4m3fn format the
+ * FlashAttention tutorial page lists among its dtypes: 1 sign bit, 4
+ * exponent bits with bias 7, 3 mantissa bits; exponent 0 holds the
+ * subnormals m * 2^-9; no infinities; S.1111.111 is NaN).
+ */
+static double widen_e4m3(uint8_t bits) {
+    const int sgn = bits >> 7, e = (bits >> 3) & 15, m = bits & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+double oracle_e4m3_value(uint8_t bits) { return widen_e4m3(bits); }
+
+/*
+ * Top-k decode over an FP8 (E4M3) paged cache with dequantisation factors
+ * (the q_descale / k_descale / v_descale arguments of the FP8 path in the
+ * flash-attention-npu page's v3 docstrings; the flash-sparse-attn page's
+ * fused-quant decode).  The stored byte x of K (or V) of sequence b, kv head
+ * g stands for e4m3(x) * k_descale[b * Hkv + g] (NULL: factor 1); q stays
+ * bf16.  Everything else is the bf16 decode above: the list is a set of
+ * valid positions, scores s_j = scale * <q, k_j>, LSE = ln sum exp s_j,
+ * O = sum exp(s_j - LSE) v_j.
+ */
+int oracle_topk_decode_fp8(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                           const float* k_descale, const float* v_descale,
+                           const int32_t* tok_idx, const int32_t* block_table,
+                           const int32_t* cache_seqlens, int32_t batch, int32_t Hq, int32_t Hkv,
+                           int32_t d, int32_t page_size, int32_t max_pages, int32_t num_pages,
+                           int32_t topk, double scale, const int64_t* seqs, int64_t nseq,
+                           double* out, double* lse) {
+    if (batch < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || page_size <= 0 ||
+        max_pages < 0 || topk < 0)
+        return -1;
+    if (seqs == NULL && nseq != batch) return -1;
+    const int G = Hq / Hkv;
+    int bad = 0;
+#pragma omp parallel
+    {
+        int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)(topk > 0 ? topk : 1));
+        double* s = (double*)malloc(sizeof(double) * (size_t)(topk > 0 ? topk : 1));
+#pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int64_t r = 0; r < nseq; ++r) {
+            for (int g = 0; g < Hkv; ++g) {
+                int64_t b = seqs ? seqs[r] : r;
+                if (b < 0 || b >= batch) {
+#pragma omp atomic write
+                    bad = 1;
+                    continue;
+                }
+                const double kd = k_descale ? (double)k_descale[b * Hkv + g] : 1.0;
+                const double vd = v_descale ? (double)v_descale[b * Hkv + g] : 1.0;
+                const int64_t L = cache_seqlens[b];
+                const int32_t* lst = tok_idx + (b * Hkv + g) * (int64_t)topk;
+                int64_t n = 0;
+                for (int e = 0; e < topk; ++e) {
+                    int64_t t = lst[e];
+                    if (t < 0 || t >= L) continue;
+                    if (t / page_size >= max_pages) continue;
+                    int64_t page = block_table[b * max_pages + t / page_size];
+                    if (page < 0 || page >= num_pages) continue;
+                    pos[n++] = t;
+                }
+                n = sort_unique(pos, n);
+                for (int hh = 0; hh < G; ++hh) {
+                    const int h = g * G + hh;
+                    const uint16_t* qrow = q + (b * Hq + h) * (int64_t)d;
+                    double* o = out + (r * Hq + h) * (int64_t)d;
+                    double* l = lse + r * Hq + h;
+                    for (int c = 0; c < d; ++c) o[c] = 0.0;
+                    if (n == 0) {
+                        *l = -INFINITY;
+                        continue;
+                    }
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < n; ++j) {
+                        const int64_t t = pos[j];
+                        const int64_t page = block_table[b * max_pages + t / page_size];
+                        const uint8_t* kr =
+                            k_cache + ((page * page_size + t % page_size) * Hkv + g) * (int64_t)d;
+                        double dot = 0.0;
+                        for (int c = 0; c < d; ++c) dot += widen_bf16(qrow[c]) * (widen_e4m3(kr[c]) * kd);
+                        s[j] = scale * dot;
+                        if (s[j] > m) m = s[j];
+                    }
+                    double sum = 0.0;
+                    for (int64_t j = 0; j < n; ++j) sum += exp(s[j] - m);
+                    const double L2 = m + log(sum);
+                    for (int64_t j = 0; j < n; ++j) {
+                        const int64_t t = pos[j];
+                        const int64_t page = block_table[b * max_pages + t / page_size];
+                        const uint8_t* vr =
+                            v_cache + ((page * page_size + t % page_size) * Hkv + g) * (int64_t)d;
+                        const double p = exp(s[j] - L2);
+                        for (int c = 0; c < d; ++c) o[c] += p * (widen_e4m3(vr[c]) * vd);
+                    }
+                    *l = L2;
+                }
+            }
+        }
+        free(pos);
+        free(s);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
  * Merge n partial results (lse_parts[n], o_parts[n, d]) of one row computed on
  * disjoint key subsets.  An empty part carries LSE = -inf and adds nothing.
  */

@@ -435,3 +435,85 @@ def test_oracle_rejects_bad_arguments():
     with pytest.raises(ValueError):          # token id out of range
         oracle.selected_attn_fwd(q, k, k, np.zeros((4, 2, 1), np.int32), [0, 4], [0, 4], 4,
                                  tokens=[5])
+
+
+# ------------------------------------------------------------------ FP8 decode
+
+def test_e4m3_decoder_matches_torch_float8():
+    """Every byte against torch's float8_e4m3fn widening (an independent decoder)."""
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(
+        torch.float64).numpy()
+    mine = np.array([oracle.e4m3_value(b) for b in range(256)])
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.isnan(mine).sum() == 2                       # 0x7F and 0xFF
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert mine[0x38] == 1.0 and mine[0x7E] == 448.0 and mine[0x01] == 2.0 ** -9
+
+
+def _fp8_case(seed, batch=3, hq=8, hkv=2, d=32, L=300, P=32, topk=64):
+    rng = np.random.default_rng(seed)
+    pages = -(-L // P)
+    num_pages = batch * pages
+    kb = rng.integers(0, 256, size=(num_pages, P, hkv, d), dtype=np.uint8)
+    vb = rng.integers(0, 256, size=(num_pages, P, hkv, d), dtype=np.uint8)
+    for x in (kb, vb):                                     # no NaN codes
+        x[(x & 0x7F) == 0x7F] = 0x3C
+    q = rand_bf16((batch, hq, d), seed + 7)
+    bt = rng.permutation(num_pages).astype(np.int32).reshape(batch, pages)
+    tok = rng.integers(-2, L + 3, size=(batch, hkv, topk)).astype(np.int32)
+    tok[:, :, 1] = tok[:, :, 0]                            # a repeat in every list
+    seqlens = np.array([L] + [L // 2] * (batch - 1), np.int32)
+    return q, torch.from_numpy(kb), torch.from_numpy(vb), tok, bt, seqlens
+
+
+def _as_bf16(kb, factor=None):
+    """The bf16 cache holding exactly the values the E4M3 bytes stand for."""
+    vals = kb.view(torch.float8_e4m3fn).to(torch.float32)
+    if factor is not None:
+        vals = vals * factor
+    out = vals.to(torch.bfloat16)
+    assert torch.equal(out.to(torch.float32), vals)       # exact in bf16
+    return out
+
+
+def test_fp8_decode_equals_bf16_decode_on_the_same_values():
+    q, kb, vb, tok, bt, seqlens = _fp8_case(301)
+    o8, l8 = oracle.topk_decode_fp8(q, kb, vb, None, None, tok, bt, seqlens)
+    o16, l16 = oracle.topk_decode(q, _as_bf16(kb), _as_bf16(vb), tok, bt, seqlens)
+    assert np.allclose(o8, o16, atol=1e-12, rtol=1e-12)
+    assert np.allclose(l8, l16, atol=1e-12, rtol=1e-12)
+
+
+def test_fp8_descale_per_sequence_and_head():
+    """Factors that are powers of two give exactly the bf16 decode of the scaled
+    values, each (sequence, kv head) with its own factor."""
+    q, kb, vb, tok, bt, seqlens = _fp8_case(302)
+    batch, hkv = 3, 2
+    kd = np.array([[0.5, 2.0], [0.25, 1.0], [4.0, 0.125]], np.float32)
+    vd = np.array([[2.0, 0.5], [1.0, 8.0], [0.25, 0.5]], np.float32)
+    o8, l8 = oracle.topk_decode_fp8(q, kb, vb, kd, vd, tok, bt, seqlens)
+    for b in range(batch):
+        for g in range(hkv):
+            # a cache scaled by this sequence's factors, read only for (b, g)
+            kf = torch.full((hkv,), float(kd[b, g]))
+            vf = torch.full((hkv,), float(vd[b, g]))
+            k16 = _as_bf16(kb, kf[None, None, :, None])
+            v16 = _as_bf16(vb, vf[None, None, :, None])
+            o, l = oracle.topk_decode(q, k16, v16, tok, bt, seqlens)
+            G = 4
+            hs = slice(g * G, (g + 1) * G)
+            assert np.allclose(o8[b, hs], o[b, hs], atol=1e-12, rtol=1e-12)
+            assert np.allclose(l8[b, hs], l[b, hs], atol=1e-12, rtol=1e-12)
+
+
+def test_fp8_v_descale_scales_output_k_descale_scales_scores():
+    q, kb, vb, tok, bt, seqlens = _fp8_case(303)
+    ones = np.ones((3, 2), np.float32)
+    o1, l1 = oracle.topk_decode_fp8(q, kb, vb, ones, ones, tok, bt, seqlens)
+    o2, l2 = oracle.topk_decode_fp8(q, kb, vb, ones, 3.0 * ones, tok, bt, seqlens)
+    assert np.allclose(o2, 3.0 * o1, atol=1e-12, rtol=1e-12) and np.array_equal(l1, l2)
+    o3, l3 = oracle.topk_decode_fp8(q, kb, vb, 0.5 * ones, ones, tok, bt, seqlens)
+    o4, l4 = oracle.topk_decode_fp8(q, kb, vb, ones, ones, tok, bt, seqlens,
+                                    softmax_scale=0.5 / math.sqrt(32))
+    assert np.allclose(o3, o4, atol=1e-12) and np.allclose(l3, l4, atol=1e-12)

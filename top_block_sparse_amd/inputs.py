@@ -254,6 +254,49 @@ def make_decode(spec: DecodeSpec, with_cache: bool = True, cache_sets: int = 1) 
     return d
 
 
+def quantize_e4m3(x: torch.Tensor, descale: torch.Tensor, block_table: torch.Tensor) -> torch.Tensor:
+    """FP8 E4M3 bytes (uint8) of a paged cache ``x`` [num_pages, page, Hkv, d]
+    for per (sequence, kv head) dequantisation factors ``descale`` [batch, Hkv]:
+    page ``block_table[b, i]`` of sequence b stores round(x / descale[b, g]),
+    clamped to +-448 (the E4M3 range), rounded to nearest even by torch's
+    float8_e4m3fn cast.  Pages no sequence uses get factor 1.
+    """
+    num_pages, _, hkv, _ = x.shape
+    per_page = torch.ones((num_pages, hkv), dtype=torch.float32)
+    bt = block_table.to(torch.int64)
+    for b in range(bt.shape[0]):
+        ids = bt[b][(bt[b] >= 0) & (bt[b] < num_pages)]
+        per_page[ids] = descale[b].to(torch.float32)
+    out = torch.empty(x.shape, dtype=torch.uint8)
+    step = max(1, (1 << 24) // max(1, x[0].numel()))
+    for p0 in range(0, num_pages, step):
+        xs = x[p0:p0 + step].to(torch.float32) / per_page[p0:p0 + step, None, :, None]
+        out[p0:p0 + step] = xs.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return out
+
+
+def make_decode_fp8(spec: DecodeSpec, unit_factors: bool = False) -> dict:
+    """The decode workload with an FP8 E4M3 cache: the same q, lists, tables
+    and N(0,1) cache values as ``make_decode``, stored as bytes with seeded
+    per (sequence, kv head) dequantisation factors 5/448 * U(0.8, 1.25), so the
+    largest |x| about 5 lands near the top of the E4M3 range (or with all
+    factors 1: the values themselves rounded to E4M3)."""
+    d = make_decode(spec)
+    rng = np.random.Generator(np.random.PCG64(6000 + spec.seed))
+    shape = (spec.batch, spec.num_heads_kv)
+    kd = torch.from_numpy((5.0 / 448.0 * rng.uniform(0.8, 1.25, shape)).astype(np.float32))
+    vd = torch.from_numpy((5.0 / 448.0 * rng.uniform(0.8, 1.25, shape)).astype(np.float32))
+    if unit_factors:
+        kd = torch.ones(shape, dtype=torch.float32)
+        vd = torch.ones(shape, dtype=torch.float32)
+    d["k_cache"] = quantize_e4m3(d["k_cache"], kd, d["block_table"])
+    d["v_cache"] = quantize_e4m3(d["v_cache"], vd, d["block_table"])
+    d["k_descale"] = kd
+    d["v_descale"] = vd
+    d["sets"] = [dict(d["sets"][0], k_cache=d["k_cache"], v_cache=d["v_cache"])]
+    return d
+
+
 def count_valid_pairs(blk_idx: np.ndarray, cu_q: np.ndarray, cu_k: np.ndarray,
                       block_size: int, causal: bool = True) -> int:
     """Number of distinct (token, kv head, block) selections whose block has a visible key.
