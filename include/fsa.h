@@ -159,6 +159,34 @@ fsa_status_t fsa_topk_decode(const void* q, const void* k_cache, const void* v_c
                              float softmax_scale, int32_t num_splits, void* workspace,
                              size_t workspace_bytes, void* out, float* lse, void* stream);
 
+/*
+ * Top-k gathered decode over an FP8 paged KV cache: fsa_topk_decode with K
+ * and V stored as FP8 E4M3 bytes (the torch.float8_e4m3fn format the
+ * FlashAttention tutorial page lists; the flash-sparse-attn page's fused-quant
+ * decode) and dequantisation factors as in the FP8 path of the
+ * flash-attention-npu page's v3 docstrings (k_descale, v_descale).
+ *
+ *   k_cache, v_cache  uint8 [num_pages, page_size, num_heads_kv, head_dim]:
+ *              the byte x of sequence b, kv head g stands for
+ *              e4m3(x) * k_descale[b * num_heads_kv + g] (V: v_descale);
+ *              16-byte aligned
+ *   k_descale, v_descale  fp32 [batch, num_heads_kv] device arrays, or NULL
+ *              for a factor of 1
+ * All other arguments, the limits, the workspace
+ * (fsa_topk_decode_workspace_size with the same arguments) and the error
+ * behaviour are those of fsa_topk_decode; q, out and lse stay bf16 / fp32.
+ * The two NaN codes (S.1111.111) are not meaningful cache contents: the
+ * outputs of a list that reaches one are unspecified.
+ */
+fsa_status_t fsa_topk_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                 const float* k_descale, const float* v_descale,
+                                 const int32_t* tok_idx, const int32_t* block_table,
+                                 const int32_t* cache_seqlens, int32_t batch, int32_t num_heads_q,
+                                 int32_t num_heads_kv, int32_t head_dim, int32_t page_size,
+                                 int32_t max_pages_per_seq, int32_t num_pages, int32_t topk,
+                                 float softmax_scale, int32_t num_splits, void* workspace,
+                                 size_t workspace_bytes, void* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

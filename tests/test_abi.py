@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 7
+    assert len(names) == 8
     assert sorted(names) == sorted(_lib.EXPORTS)
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
@@ -130,6 +130,36 @@ def decode(lib, **kw):
 ])
 def test_decode_argument_errors(lib, kw, code):
     assert decode(lib, **kw) == code
+
+
+def decode_fp8(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, kd=None, vd=None, tok=FAKE, bt=FAKE, cs=FAKE, batch=4,
+             hq=8, hkv=2, d=128, page=256, maxp=8, npages=32, topk=100, scale=0.0, splits=2,
+             ws=None, ws_bytes=0, out=FAKE, lse=None, stream=None)
+    a.update(kw)
+    return lib.fsa_topk_decode_fp8(a["q"], a["kc"], a["vc"], a["kd"], a["vd"], a["tok"], a["bt"],
+                                   a["cs"], a["batch"], a["hq"], a["hkv"], a["d"], a["page"],
+                                   a["maxp"], a["npages"], a["topk"], a["scale"], a["splits"],
+                                   a["ws"], a["ws_bytes"], a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=6, hkv=4), INVALID),
+    (dict(d=96), NOT_SUPPORTED),
+    (dict(topk=0), INVALID),
+    (dict(topk=8193), NOT_SUPPORTED),
+    (dict(kc=None), INVALID),
+    (dict(vc=FAKE + 4), INVALID),              # caches must be 16-byte aligned
+    (dict(page=0), INVALID),
+    (dict(ws=None), WORKSPACE),                # two splits need the partial workspace
+    (dict(ws=FAKE, ws_bytes=64), WORKSPACE),
+])
+def test_decode_fp8_argument_errors(lib, kw, code):
+    assert decode_fp8(lib, **kw) == code
+
+
+def test_decode_fp8_empty_batch_is_a_no_op(lib):
+    assert decode_fp8(lib, batch=0, q=None, splits=0) == 0
 
 
 def test_decode_workspace_and_splits(lib):

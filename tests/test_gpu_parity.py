@@ -343,3 +343,66 @@ def test_decode_full_size_workload():
     print("[gpu] decode workload: HIP path + oracle", flush=True)
     o, l, ro, rl = run_decode(dd)
     compare_decode(o, l, ro, rl, what=spec.name)
+
+
+# ------------------------------------------------------------------ FP8 decode
+
+def run_decode_fp8(dd, tok=None, num_splits=0, cache_seqlens=None, block_table=None,
+                   descale=True):
+    tok = dd["tok_idx"] if tok is None else tok
+    cs = dd["cache_seqlens"] if cache_seqlens is None else cache_seqlens
+    bt = dd["block_table"] if block_table is None else block_table
+    kd = dd["k_descale"] if descale else None
+    vd = dd["v_descale"] if descale else None
+    o, l = fsa.fsa_topk_decode_fp8(dd["q"].to(DEV), dd["k_cache"].to(DEV), dd["v_cache"].to(DEV),
+                                   None if kd is None else kd.to(DEV),
+                                   None if vd is None else vd.to(DEV), tok.to(DEV), bt.to(DEV),
+                                   cs.to(DEV), num_splits=num_splits)
+    torch.cuda.synchronize()
+    ro, rl = oracle.topk_decode_fp8(dd["q"], dd["k_cache"], dd["v_cache"], kd, vd, tok, bt, cs)
+    return o.float().cpu().numpy(), l.cpu().numpy(), ro, rl
+
+
+@pytest.mark.parametrize("case", DECODE_SHAPES[:5], ids=lambda c: "_".join(map(str, c)))
+def test_decode_fp8_shapes_with_index_edge_cases(case):
+    batch, hq, hkv, d, L, P, topk = case
+    print(f"[gpu] decode fp8 {case}", flush=True)
+    spec = inputs.DecodeSpec("t", batch, hq, hkv, d, L, P, topk, recent=min(64, topk), seed=L + P)
+    dd = inputs.make_decode_fp8(spec)
+    rng = np.random.default_rng(L + 1)
+    tok = mutate_tok(dd["tok_idx"], rng, L)
+    cs = dd["cache_seqlens"].clone()
+    cs[0] = L // 2 + 1
+    bt = dd["block_table"].clone()
+    if bt.shape[1] > 2:
+        bt[-1, 1] = -3
+    o, l, ro, rl = run_decode_fp8(dd, tok=tok, cache_seqlens=cs, block_table=bt)
+    compare_decode(o, l, ro, rl, what=f"fp8 {case}")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 16])
+def test_decode_fp8_split_counts_and_unit_factors(splits):
+    spec = inputs.DecodeSpec("t", 3, 8, 2, 128, 4000, 256, 1500, seed=40 + splits)
+    dd = inputs.make_decode_fp8(spec, unit_factors=splits == 3)
+    o, l, ro, rl = run_decode_fp8(dd, num_splits=splits, descale=splits != 3)   # None = factor 1
+    compare_decode(o, l, ro, rl, what=f"fp8 splits={splits}")
+
+
+def test_decode_fp8_visible_set_exact():
+    spec = inputs.DecodeSpec("t", 4, 8, 2, 128, 2500, 128, 900, seed=13)
+    dd = inputs.make_decode_fp8(spec)
+    dd["q"] = torch.zeros_like(dd["q"])
+    tok = mutate_tok(dd["tok_idx"], np.random.default_rng(2), 2500)
+    o, l, ro, rl = run_decode_fp8(dd, tok=tok)
+    assert np.abs(l - rl).max() <= 1e-5
+    compare_decode(o, l, ro, rl)
+
+
+def test_decode_fp8_full_size_workload():
+    """The decode workload with its cache stored as FP8, every (sequence, head)."""
+    spec = inputs.DECODE_WORKLOADS["decode_b32_h32_kv8_d128_L32768_p256_top2048"]
+    print("[gpu] decode fp8 workload: generating inputs", flush=True)
+    dd = inputs.make_decode_fp8(spec)
+    print("[gpu] decode fp8 workload: HIP path + oracle", flush=True)
+    o, l, ro, rl = run_decode_fp8(dd)
+    compare_decode(o, l, ro, rl, what=spec.name + " fp8")

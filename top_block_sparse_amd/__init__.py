@@ -15,11 +15,12 @@ from ._lib import (  # noqa: F401
     fsa_status_string,
     fsa_topk_decode,
     fsa_topk_decode_auto_splits,
+    fsa_topk_decode_fp8,
     fsa_topk_decode_workspace_size,
 )
 
 __all__ = [
     "FsaError", "fsa_abi_version", "fsa_selected_attn_fwd",
     "fsa_selected_attn_fwd_workspace_size", "fsa_status_string", "fsa_topk_decode",
-    "fsa_topk_decode_auto_splits", "fsa_topk_decode_workspace_size",
+    "fsa_topk_decode_auto_splits", "fsa_topk_decode_fp8", "fsa_topk_decode_workspace_size",
 ]

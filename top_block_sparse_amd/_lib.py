@@ -26,7 +26,7 @@ _STATUS = {0: "FSA_SUCCESS", 1: "FSA_ERROR_INVALID_VALUE", 2: "FSA_ERROR_NOT_SUP
 # Every symbol include/fsa.h declares.
 EXPORTS = ("fsa_status_string", "fsa_abi_version", "fsa_selected_attn_fwd_workspace_size",
            "fsa_selected_attn_fwd", "fsa_topk_decode_workspace_size",
-           "fsa_topk_decode_auto_splits", "fsa_topk_decode")
+           "fsa_topk_decode_auto_splits", "fsa_topk_decode", "fsa_topk_decode_fp8")
 
 _lib = None
 
@@ -57,6 +57,9 @@ def load() -> ctypes.CDLL:
     lib.fsa_selected_attn_fwd.restype = ctypes.c_int
     lib.fsa_selected_attn_fwd.argtypes = [P, P, P, P, P, P, i32, i64, i64, i32, i32, i32, i32, i32,
                                           i32, i32, f32, i32, i32, P, sz, P, P, P]
+    lib.fsa_topk_decode_fp8.restype = ctypes.c_int
+    lib.fsa_topk_decode_fp8.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                        i32, f32, i32, P, sz, P, P, P]
     lib.fsa_topk_decode_workspace_size.restype = sz
     lib.fsa_topk_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.fsa_topk_decode_auto_splits.restype = i32
@@ -163,17 +166,13 @@ def fsa_selected_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out, lse
 
 
-def fsa_topk_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                    tok_idx: torch.Tensor, block_table: torch.Tensor, cache_seqlens: torch.Tensor,
-                    softmax_scale: Optional[float] = None, num_splits: int = 0,
-                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, return_lse: bool = True
-                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Top-k gathered paged decode; returns ``(out [B,Hq,d], lse [B,Hq])``."""
+def _decode(q, k_cache, v_cache, k_descale, v_descale, tok_idx, block_table, cache_seqlens,
+            softmax_scale, num_splits, out, lse, workspace, return_lse, fp8: bool):
     lib = load()
+    cache_dtype = torch.uint8 if fp8 else torch.bfloat16
     _check_dev("q", q, torch.bfloat16, 3)
-    _check_dev("k_cache", k_cache, torch.bfloat16, 4)
-    _check_dev("v_cache", v_cache, torch.bfloat16, 4)
+    _check_dev("k_cache", k_cache, cache_dtype, 4)
+    _check_dev("v_cache", v_cache, cache_dtype, 4)
     _check_dev("tok_idx", tok_idx, torch.int32, 3)
     _check_dev("block_table", block_table, torch.int32, 2)
     _check_dev("cache_seqlens", cache_seqlens, torch.int32, 1)
@@ -185,6 +184,11 @@ def fsa_topk_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     if tuple(tok_idx.shape[:2]) != (batch, hkv) or block_table.shape[0] != batch \
             or cache_seqlens.numel() != batch:
         raise ValueError("tok_idx [B,Hkv,topk], block_table [B,max_pages], cache_seqlens [B]")
+    for nm, t in (("k_descale", k_descale), ("v_descale", v_descale)):
+        if t is not None:
+            _check_dev(nm, t, torch.float32, 2)
+            if tuple(t.shape) != (batch, hkv):
+                raise ValueError(f"{nm} must be [batch, Hkv]")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
@@ -194,13 +198,43 @@ def fsa_topk_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
-    st = lib.fsa_topk_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(tok_idx),
-                             _ptr(block_table), _ptr(cache_seqlens), batch, hq, hkv, d, page_size,
-                             block_table.shape[1], num_pages, topk, scale, num_splits,
-                             _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(q.device))
+    tail = (_ptr(tok_idx), _ptr(block_table), _ptr(cache_seqlens), batch, hq, hkv, d, page_size,
+            block_table.shape[1], num_pages, topk, scale, num_splits, _ptr(workspace), ws_bytes,
+            _ptr(out), _ptr(lse), _stream(q.device))
+    if fp8:
+        st = lib.fsa_topk_decode_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_descale),
+                                     _ptr(v_descale), *tail)
+    else:
+        st = lib.fsa_topk_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), *tail)
     if st != FSA_SUCCESS:
-        raise FsaError(st, "fsa_topk_decode")
+        raise FsaError(st, "fsa_topk_decode_fp8" if fp8 else "fsa_topk_decode")
     return out, lse
+
+
+def fsa_topk_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    tok_idx: torch.Tensor, block_table: torch.Tensor, cache_seqlens: torch.Tensor,
+                    softmax_scale: Optional[float] = None, num_splits: int = 0,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, return_lse: bool = True
+                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Top-k gathered paged decode; returns ``(out [B,Hq,d], lse [B,Hq])``."""
+    return _decode(q, k_cache, v_cache, None, None, tok_idx, block_table, cache_seqlens,
+                   softmax_scale, num_splits, out, lse, workspace, return_lse, fp8=False)
+
+
+def fsa_topk_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        k_descale: Optional[torch.Tensor], v_descale: Optional[torch.Tensor],
+                        tok_idx: torch.Tensor, block_table: torch.Tensor,
+                        cache_seqlens: torch.Tensor, softmax_scale: Optional[float] = None,
+                        num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, return_lse: bool = True
+                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Top-k gathered paged decode over an FP8 E4M3 cache (uint8 bytes) with
+    fp32 [B, Hkv] dequantisation factors (None: 1); returns ``(out, lse)``."""
+    return _decode(q, k_cache, v_cache, k_descale, v_descale, tok_idx, block_table,
+                   cache_seqlens, softmax_scale, num_splits, out, lse, workspace, return_lse,
+                   fp8=True)
 
 
 def default_scale(head_dim: int) -> float:

@@ -121,6 +121,80 @@ float resolve_scale(float s, int D) { return s > 0.f ? s : 1.0f / std::sqrt((flo
 
 }  // namespace
 
+static fsa_status_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                               bool kv_fp8, const float* k_descale, const float* v_descale,
+                             const int32_t* tok_idx, const int32_t* block_table,
+                             const int32_t* cache_seqlens, int32_t batch, int32_t num_heads_q,
+                             int32_t num_heads_kv, int32_t head_dim, int32_t page_size,
+                             int32_t max_pages_per_seq, int32_t num_pages, int32_t topk,
+                             float softmax_scale, int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, void* out, float* lse, void* stream) {
+    fsa_status_t st = check_decode_shape(batch, num_heads_q, num_heads_kv, head_dim, topk,
+                                         num_splits);
+    if (st != FSA_SUCCESS) return st;
+    if (page_size <= 0 || max_pages_per_seq < 0 || num_pages < 0) return FSA_ERROR_INVALID_VALUE;
+    if ((int64_t)num_pages * page_size >= (int64_t)INT32_MAX) return FSA_ERROR_NOT_SUPPORTED;
+    if (batch == 0) return FSA_SUCCESS;
+    if (!q || !k_cache || !v_cache || !tok_idx || !block_table || !cache_seqlens || !out)
+        return FSA_ERROR_INVALID_VALUE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return FSA_ERROR_INVALID_VALUE;
+    const DecodeLayout lay = decode_layout(batch, num_heads_q, num_heads_kv, head_dim, topk,
+                                           num_splits);
+    if (lay.total > 0 && (workspace == nullptr || workspace_bytes < lay.total ||
+                          (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
+        return FSA_ERROR_WORKSPACE;
+
+    fsa::DecodeParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.kc = k_cache;
+    p.vc = v_cache;
+    p.kv_fp8 = kv_fp8 ? 1 : 0;
+    p.k_descale = k_descale;
+    p.v_descale = v_descale;
+    p.tok_idx = tok_idx;
+    p.block_table = block_table;
+    p.cache_seqlens = cache_seqlens;
+    p.out = static_cast<uint16_t*>(out);
+    p.lse = lse;
+    if (lay.splits > 1) {
+        uint8_t* ws = static_cast<uint8_t*>(workspace);
+        p.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+        p.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
+    }
+    p.batch = batch;
+    p.Hq = num_heads_q;
+    p.Hkv = num_heads_kv;
+    p.G = num_heads_q / num_heads_kv;
+    p.page_size = page_size;
+    p.max_pages = max_pages_per_seq;
+    p.num_pages = num_pages;
+    p.topk = topk;
+    p.splits = lay.splits;
+    p.ts = fsa::decode_table_slots(head_dim, p.G, topk);
+    p.scale_log2 = resolve_scale(softmax_scale, head_dim) * fsa::kLog2e;
+    if (fsa::decode_lds_bytes(head_dim, p.G, p.ts, topk) > 160 * 1024)
+        return FSA_ERROR_NOT_SUPPORTED;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (fsa::launch_decode(p, head_dim, s) != hipSuccess) return FSA_ERROR_LAUNCH;
+    if (lay.splits > 1) {
+        fsa::MergeParams m{};
+        m.part_o = p.part_o;
+        m.part_lse = p.part_lse;
+        m.out = p.out;
+        m.lse = lse;
+        m.nrows = (int64_t)batch * num_heads_q;
+        m.nparts = lay.splits;
+        m.lse_mode = 1;
+        m.Hq = num_heads_q;
+        m.ntok = batch;
+        if (fsa::launch_lse_merge(m, head_dim, s) != hipSuccess) return FSA_ERROR_LAUNCH;
+    }
+    return FSA_SUCCESS;
+}
+
 extern "C" {
 
 const char* fsa_status_string(fsa_status_t status) {
@@ -252,67 +326,24 @@ fsa_status_t fsa_topk_decode(const void* q, const void* k_cache, const void* v_c
                              int32_t max_pages_per_seq, int32_t num_pages, int32_t topk,
                              float softmax_scale, int32_t num_splits, void* workspace,
                              size_t workspace_bytes, void* out, float* lse, void* stream) {
-    fsa_status_t st = check_decode_shape(batch, num_heads_q, num_heads_kv, head_dim, topk,
-                                         num_splits);
-    if (st != FSA_SUCCESS) return st;
-    if (page_size <= 0 || max_pages_per_seq < 0 || num_pages < 0) return FSA_ERROR_INVALID_VALUE;
-    if ((int64_t)num_pages * page_size >= (int64_t)INT32_MAX) return FSA_ERROR_NOT_SUPPORTED;
-    if (batch == 0) return FSA_SUCCESS;
-    if (!q || !k_cache || !v_cache || !tok_idx || !block_table || !cache_seqlens || !out)
-        return FSA_ERROR_INVALID_VALUE;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
-        return FSA_ERROR_INVALID_VALUE;
-    const DecodeLayout lay = decode_layout(batch, num_heads_q, num_heads_kv, head_dim, topk,
-                                           num_splits);
-    if (lay.total > 0 && (workspace == nullptr || workspace_bytes < lay.total ||
-                          (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
-        return FSA_ERROR_WORKSPACE;
+    return decode_impl(q, k_cache, v_cache, false, nullptr, nullptr, tok_idx, block_table,
+                       cache_seqlens, batch, num_heads_q, num_heads_kv, head_dim, page_size,
+                       max_pages_per_seq, num_pages, topk, softmax_scale, num_splits, workspace,
+                       workspace_bytes, out, lse, stream);
+}
 
-    fsa::DecodeParams p{};
-    p.q = static_cast<const uint16_t*>(q);
-    p.kc = static_cast<const uint16_t*>(k_cache);
-    p.vc = static_cast<const uint16_t*>(v_cache);
-    p.tok_idx = tok_idx;
-    p.block_table = block_table;
-    p.cache_seqlens = cache_seqlens;
-    p.out = static_cast<uint16_t*>(out);
-    p.lse = lse;
-    if (lay.splits > 1) {
-        uint8_t* ws = static_cast<uint8_t*>(workspace);
-        p.part_o = reinterpret_cast<float*>(ws + lay.part_o);
-        p.part_lse = reinterpret_cast<float*>(ws + lay.part_lse);
-    }
-    p.batch = batch;
-    p.Hq = num_heads_q;
-    p.Hkv = num_heads_kv;
-    p.G = num_heads_q / num_heads_kv;
-    p.page_size = page_size;
-    p.max_pages = max_pages_per_seq;
-    p.num_pages = num_pages;
-    p.topk = topk;
-    p.splits = lay.splits;
-    p.ts = fsa::decode_table_slots(head_dim, p.G, topk);
-    p.scale_log2 = resolve_scale(softmax_scale, head_dim) * fsa::kLog2e;
-    if (fsa::decode_lds_bytes(head_dim, p.G, p.ts, topk) > 160 * 1024)
-        return FSA_ERROR_NOT_SUPPORTED;
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();
-    if (fsa::launch_decode(p, head_dim, s) != hipSuccess) return FSA_ERROR_LAUNCH;
-    if (lay.splits > 1) {
-        fsa::MergeParams m{};
-        m.part_o = p.part_o;
-        m.part_lse = p.part_lse;
-        m.out = p.out;
-        m.lse = lse;
-        m.nrows = (int64_t)batch * num_heads_q;
-        m.nparts = lay.splits;
-        m.lse_mode = 1;
-        m.Hq = num_heads_q;
-        m.ntok = batch;
-        if (fsa::launch_lse_merge(m, head_dim, s) != hipSuccess) return FSA_ERROR_LAUNCH;
-    }
-    return FSA_SUCCESS;
+fsa_status_t fsa_topk_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                                 const float* k_descale, const float* v_descale,
+                                 const int32_t* tok_idx, const int32_t* block_table,
+                                 const int32_t* cache_seqlens, int32_t batch, int32_t num_heads_q,
+                                 int32_t num_heads_kv, int32_t head_dim, int32_t page_size,
+                                 int32_t max_pages_per_seq, int32_t num_pages, int32_t topk,
+                                 float softmax_scale, int32_t num_splits, void* workspace,
+                                 size_t workspace_bytes, void* out, float* lse, void* stream) {
+    return decode_impl(q, k_cache, v_cache, true, k_descale, v_descale, tok_idx, block_table,
+                       cache_seqlens, batch, num_heads_q, num_heads_kv, head_dim, page_size,
+                       max_pages_per_seq, num_pages, topk, softmax_scale, num_splits, workspace,
+                       workspace_bytes, out, lse, stream);
 }
 
 }  // extern "C"

@@ -33,8 +33,10 @@ struct SelFwdParams {
 // Top-k paged decode (topk_decode.hip).
 struct DecodeParams {
     const uint16_t* q;
-    const uint16_t* kc;
-    const uint16_t* vc;
+    const void* kc;         // bf16, or FP8 E4M3 bytes when kv_fp8
+    const void* vc;
+    const float* k_descale; // [batch*Hkv] or null (kv_fp8 only)
+    const float* v_descale;
     const int32_t* tok_idx;
     const int32_t* block_table;
     const int32_t* cache_seqlens;
@@ -44,6 +46,7 @@ struct DecodeParams {
     float* part_lse;        // workspace: [splits][batch*Hq]
     int batch, Hq, Hkv, G, page_size, max_pages, num_pages, topk, splits;
     int ts;                 // hash table slots (> topk)
+    int kv_fp8;
     float scale_log2;
 };
 

@@ -87,15 +87,18 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// D: head dim (64 or 128); GM: query heads handled per kv head (>= G).
-template <int D, int GM>
+// D: head dim (64 or 128); GM: query heads handled per kv head (>= G);
+// F8: the cache holds FP8 E4M3 bytes with dequantisation factors (else bf16).
+template <int D, int GM, bool F8>
 __global__ void __launch_bounds__(dec_waves(GM) * 64)
 decode_kernel(const DecodeParams p) {
     using L = DecLds<D, GM>;
     constexpr int NW = L::NW;
     constexpr int NT = NW * 64;
     constexpr int DPL = D / 16;              // dims per lane (8 or 4)
-    constexpr int WPL = DPL / 2;             // 32-bit words per lane
+    constexpr int WPL = DPL / 2;             // bf16 pairs per lane and row
+    constexpr int EB = F8 ? 1 : 2;           // bytes per cache element
+    constexpr int RW = DPL * EB / 4;         // raw 32-bit words per lane and row
     constexpr int U = GM > 4 ? kDecUnroll / 2 : kDecUnroll;
 
     constexpr int KMAX = L::KMAX;            // list entries per thread, at most
@@ -174,9 +177,9 @@ decode_kernel(const DecodeParams p) {
     const int r_hi = (int)(((long long)topk * (split + 1)) / p.splits);
     constexpr int B = 4 * U;                 // entries per batch
     const int nbatch = (r_hi - r_lo + B - 1) / B;
-    const int64_t row_stride = (int64_t)p.Hkv * D;   // elements between cache rows
-    const uint16_t* kbase = p.kc + (int64_t)g * D + lr * DPL;
-    const uint16_t* vbase = p.vc + (int64_t)g * D + lr * DPL;
+    const int64_t row_stride = (int64_t)p.Hkv * D * EB;   // bytes between cache rows
+    const uint8_t* kbase = static_cast<const uint8_t*>(p.kc) + ((int64_t)g * D + lr * DPL) * EB;
+    const uint8_t* vbase = static_cast<const uint8_t*>(p.vc) + ((int64_t)g * D + lr * DPL) * EB;
     // Entries r0 + 4u + lg, u < U, are one batch.  Bit u of the mask: that
     // entry is a row to attend to (inside the part, valid and not a repeat).
     auto okmask = [&](int r0) {
@@ -188,28 +191,32 @@ decode_kernel(const DecodeParams p) {
         }
         return okm;
     };
-    auto issue = [&](uint32_t (&kw)[U][WPL], uint32_t (&vw)[U][WPL], int r0) {
+    // Raw cache words of a batch (bf16 pairs, or four E4M3 bytes per word).
+    auto issue = [&](uint32_t (&kw)[U][RW], uint32_t (&vw)[U][RW], int r0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int r = r0 + u * 4 + lg;
             const int row = r < r_hi ? rows[r] : -1;
             const int64_t cr = row >= 0 ? row : 0;     // skipped entries read row 0, ignored
-            const uint16_t* kp = kbase + cr * row_stride;
-            const uint16_t* vp = vbase + cr * row_stride;
-            if constexpr (WPL == 4) {
+            const uint8_t* kp = kbase + cr * row_stride;
+            const uint8_t* vp = vbase + cr * row_stride;
+            if constexpr (RW == 4) {
                 const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kp);
                 const u32x4_t c = *reinterpret_cast<const u32x4_t*>(vp);
 #pragma unroll
                 for (int x = 0; x < 4; ++x) { kw[u][x] = a[x]; vw[u][x] = c[x]; }
-            } else {
+            } else if constexpr (RW == 2) {
                 const u32x2_t a = *reinterpret_cast<const u32x2_t*>(kp);
                 const u32x2_t c = *reinterpret_cast<const u32x2_t*>(vp);
 #pragma unroll
                 for (int x = 0; x < 2; ++x) { kw[u][x] = a[x]; vw[u][x] = c[x]; }
+            } else {
+                kw[u][0] = *reinterpret_cast<const uint32_t*>(kp);
+                vw[u][0] = *reinterpret_cast<const uint32_t*>(vp);
             }
         }
     };
-    uint32_t ka[U][WPL], va[U][WPL];
+    uint32_t ka[U][RW], va[U][RW];
     int bi = wave;
     if (bi < nbatch) issue(ka, va, r_lo + bi * B);
 
@@ -248,6 +255,14 @@ decode_kernel(const DecodeParams p) {
     }
     __syncthreads();
 
+    // scale (log2 units) including the K dequantisation factor; V's factor
+    // scales the output
+    float c_log2 = p.scale_log2, v_scale = 1.f;
+    if constexpr (F8) {
+        if (p.k_descale != nullptr) c_log2 *= p.k_descale[unit];
+        if (p.v_descale != nullptr) v_scale = p.v_descale[unit];
+    }
+
     uint32_t qw[GM][WPL];                    // this lane's dims of the G query rows (bf16 pairs)
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
@@ -277,7 +292,24 @@ decode_kernel(const DecodeParams p) {
         for (int x = 0; x < DPL; ++x) acc[h][x] = 0.f;
     }
 
-    auto consume = [&](const uint32_t (&kw)[U][WPL], const uint32_t (&vw)[U][WPL], uint32_t okm) {
+    auto consume = [&](const uint32_t (&kr)[U][RW], const uint32_t (&vr)[U][RW], uint32_t okm) {
+        // bf16 pairs of the rows (E4M3 -> bf16 is exact)
+        uint32_t kw[U][WPL], vw[U][WPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int x = 0; x < RW; ++x) {
+                if constexpr (F8) {
+                    kw[u][2 * x] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[u][x], 1.f, false));
+                    kw[u][2 * x + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[u][x], 1.f, true));
+                    vw[u][2 * x] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vr[u][x], 1.f, false));
+                    vw[u][2 * x + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vr[u][x], 1.f, true));
+                } else {
+                    kw[u][x] = kr[u][x];
+                    vw[u][x] = vr[u][x];
+                }
+            }
+        }
         // raw scores q.k of the lane group's rows, one per query head
         float s[U][GM];
 #pragma unroll
@@ -308,7 +340,7 @@ decode_kernel(const DecodeParams p) {
                 vhi[j][x] = __builtin_amdgcn_perm(vw[2 * j + 1][x], vw[2 * j][x], 0x07060302u);
             }
         }
-        const float c = p.scale_log2;            // > 0: the max commutes with the scaling
+        const float c = c_log2;                  // > 0: the max commutes with the scaling
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
             float mb = s[0][h];
@@ -392,7 +424,7 @@ decode_kernel(const DecodeParams p) {
             o0 = fmaf(rec[d], sc, o0);
             o1 = fmaf(rec[d + 1], sc, o1);
         }
-        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+        const float inv = Ls > 0.f ? v_scale / Ls : 0.f;
         const float lse_v = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
         const int64_t row = (int64_t)b * p.Hq + g * G + h;
         if (p.splits == 1) {
@@ -406,32 +438,34 @@ decode_kernel(const DecodeParams p) {
     }
 }
 
-template <int D, int GM>
+template <int D, int GM, bool F8>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
     static bool attr_set = false;   // idempotent; racing threads set the same value
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, GM>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, GM, F8>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const size_t lds = DecLds<D, GM>::bytes(p.ts, p.topk);
-    hipLaunchKernelGGL((decode_kernel<D, GM>), dim3(p.batch * p.Hkv * p.splits),
+    hipLaunchKernelGGL((decode_kernel<D, GM, F8>), dim3(p.batch * p.Hkv * p.splits),
                        dim3(DecLds<D, GM>::NW * 64), lds, stream, p);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool F8>
 static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
-    if (p.G <= 1) return launch_decode_t<D, 1>(p, stream);
-    if (p.G <= 2) return launch_decode_t<D, 2>(p, stream);
-    if (p.G <= 4) return launch_decode_t<D, 4>(p, stream);
-    if (p.G <= 8) return launch_decode_t<D, 8>(p, stream);
-    return launch_decode_t<D, 16>(p, stream);
+    if (p.G <= 1) return launch_decode_t<D, 1, F8>(p, stream);
+    if (p.G <= 2) return launch_decode_t<D, 2, F8>(p, stream);
+    if (p.G <= 4) return launch_decode_t<D, 4, F8>(p, stream);
+    if (p.G <= 8) return launch_decode_t<D, 8, F8>(p, stream);
+    return launch_decode_t<D, 16, F8>(p, stream);
 }
 
 hipError_t launch_decode(const DecodeParams& p, int D, hipStream_t stream) {
-    return D == 64 ? launch_decode_d<64>(p, stream) : launch_decode_d<128>(p, stream);
+    if (p.kv_fp8)
+        return D == 64 ? launch_decode_d<64, true>(p, stream) : launch_decode_d<128, true>(p, stream);
+    return D == 64 ? launch_decode_d<64, false>(p, stream) : launch_decode_d<128, false>(p, stream);
 }
 
 static int group_bucket(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16; }
