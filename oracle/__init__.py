@@ -51,6 +51,9 @@ def _load():
         lib.oracle_topk_decode.restype = ctypes.c_int
         lib.oracle_topk_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
                                            i32, f64, P, i64, P, P]
+        lib.oracle_window_attn_fwd.restype = ctypes.c_int
+        lib.oracle_window_attn_fwd.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, i64, f64,
+                                               P, i64, P, P]
         lib.oracle_topk_decode_fp8.restype = ctypes.c_int
         lib.oracle_topk_decode_fp8.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                                i32, i32, i32, f64, P, i64, P, P]
@@ -138,6 +141,36 @@ def topk_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, t
                                 lse.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_topk_decode rejected its arguments")
+    return out, lse
+
+
+def window_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q,
+                    cu_seqlens_k, window_left: int, window_right: int,
+                    softmax_scale: Optional[float] = None, tokens=None):
+    """Dense attention inside the window (left, right) (negative = unlimited)
+    for every query token (or the listed ``tokens``).
+    Returns ``(out [n, Hq, d] float64, lse [n, Hq] float64)``."""
+    lib = _load()
+    total_q, Hq, d = q.shape
+    Hkv = k.shape[1]
+    cu_q = _i32(cu_seqlens_q)
+    cu_k = _i32(cu_seqlens_k)
+    batch = cu_q.size - 1
+    scale = (1.0 / np.sqrt(d)) if softmax_scale is None else float(softmax_scale)
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    if tokens is None:
+        tp, n = None, total_q
+    else:
+        tarr = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+        tp, n = tarr.ctypes.data, tarr.size
+    out = np.zeros((n, Hq, d), dtype=np.float64)
+    lse = np.zeros((n, Hq), dtype=np.float64)
+    rc = lib.oracle_window_attn_fwd(qb.data_ptr(), kb.data_ptr(), vb.data_ptr(), cu_q.ctypes.data,
+                                    cu_k.ctypes.data, batch, Hq, Hkv, d, int(window_left),
+                                    int(window_right), scale, tp, n, out.ctypes.data,
+                                    lse.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_window_attn_fwd rejected its arguments")
     return out, lse
 
 

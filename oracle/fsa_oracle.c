@@ -184,6 +184,66 @@ int oracle_selected_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_
 }
 
 /*
+ * Local (sliding-window) attention, dense within the window.  Row i of a
+ * sequence with S_q queries and S_k keys attends to every key j with
+ *   i + S_k - S_q - left <= j <= i + S_k - S_q + right,   0 <= j < S_k,
+ * where a negative left or right leaves that side unlimited (window_size =
+ * (left, right) of the flash_attn_func docstring, flash-attention-npu page;
+ * (-1, 0) is causal attention, FlashAttention tutorial page section 4.3; the
+ * FSA page's sliding-window branch is the causal window (window - 1, 0)).
+ * Same layouts and conventions as oracle_selected_attn_fwd.
+ */
+int oracle_window_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const int32_t* cu_q, const int32_t* cu_k, int32_t batch, int32_t Hq,
+                           int32_t Hkv, int32_t d, int64_t left, int64_t right, double scale,
+                           const int64_t* tokens, int64_t ntok, double* out, double* lse) {
+    if (batch < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0) return -1;
+    const int G = Hq / Hkv;
+    const int64_t total_q = cu_q[batch];
+    if (tokens == NULL && ntok != total_q) return -1;
+    int64_t max_sk = 1;
+    for (int b = 0; b < batch; ++b)
+        if (cu_k[b + 1] - cu_k[b] > max_sk) max_sk = cu_k[b + 1] - cu_k[b];
+    int bad = 0;
+#pragma omp parallel
+    {
+        int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)max_sk);
+        double* s = (double*)malloc(sizeof(double) * (size_t)max_sk);
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < ntok; ++r) {
+            int64_t t = tokens ? tokens[r] : r;
+            if (t < 0 || t >= total_q) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            int sq_id = 0;
+            while (sq_id + 1 < batch && cu_q[sq_id + 1] <= t) ++sq_id;
+            const int64_t i = t - cu_q[sq_id];
+            const int64_t Sq = cu_q[sq_id + 1] - cu_q[sq_id];
+            const int64_t Sk = cu_k[sq_id + 1] - cu_k[sq_id];
+            const int64_t c = i + Sk - Sq;               /* the row's aligned key position */
+            for (int g = 0; g < Hkv; ++g) {
+                int64_t nk = 0;
+                for (int64_t j = 0; j < Sk; ++j) {
+                    if (left >= 0 && j < c - left) continue;
+                    if (right >= 0 && j > c + right) continue;
+                    keys[nk++] = ((cu_k[sq_id] + j) * Hkv + g) * (int64_t)d;
+                }
+                for (int hh = 0; hh < G; ++hh) {
+                    int h = g * G + hh;
+                    attend(q + (t * Hq + h) * (int64_t)d, k, v, keys, nk, d, scale, s,
+                           out + (r * Hq + h) * (int64_t)d, lse + r * Hq + h);
+                }
+            }
+        }
+        free(keys);
+        free(s);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
  * Top-k decode.  q [batch, Hq, d]; k_cache/v_cache [num_pages, page_size, Hkv, d];
  * tok_idx [batch, Hkv, topk]; block_table [batch, max_pages]; cache_seqlens [batch].
  * seqs: batch entries to evaluate (NULL: all, nseq == batch).

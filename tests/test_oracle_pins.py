@@ -517,3 +517,75 @@ def test_fp8_v_descale_scales_output_k_descale_scales_scores():
     o4, l4 = oracle.topk_decode_fp8(q, kb, vb, ones, ones, tok, bt, seqlens,
                                     softmax_scale=0.5 / math.sqrt(32))
     assert np.allclose(o3, o4, atol=1e-12) and np.allclose(l3, l4, atol=1e-12)
+
+
+# ------------------------------------------------------------------ local (sliding-window) attention
+
+def _window_case(seed, seqlens_q=(37, 64, 1), seqlens_k=None, hq=4, hkv=2, d=16):
+    seqlens_k = seqlens_k or seqlens_q
+    cu_q = np.concatenate([[0], np.cumsum(seqlens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(seqlens_k)]).astype(np.int32)
+    q = rand_bf16((int(cu_q[-1]), hq, d), seed)
+    k = rand_bf16((int(cu_k[-1]), hkv, d), seed + 1)
+    v = rand_bf16((int(cu_k[-1]), hkv, d), seed + 2)
+    return q, k, v, cu_q, cu_k
+
+
+@pytest.mark.parametrize("sk_extra", [0, 9])
+def test_window_minus1_0_is_causal_and_minus1_minus1_is_global(sk_extra):
+    """window (-1, 0) equals causal attention (FlashAttention tutorial page 4.3),
+    (-1, -1) equals unmasked attention; both against numpy brute force."""
+    sq = (37, 64, 5)
+    sk = tuple(x + sk_extra for x in sq)
+    q, k, v, cu_q, cu_k = _window_case(401, sq, sk)
+    heads = [h // 2 for h in range(4)]
+    for (left, right), causal in (((-1, 0), True), ((-1, -1), False)):
+        o, l = oracle.window_attn_fwd(q, k, v, cu_q, cu_k, left, right)
+        ro, rl = dense_reference(f64(q), f64(k), f64(v), cu_q, cu_k, 1 / 4, causal, heads)
+        assert np.allclose(o, ro, atol=1e-12) and np.allclose(l, rl, atol=1e-12)
+
+
+def test_window_zero_width_is_one_key():
+    q, k, v, cu_q, cu_k = _window_case(402, (20,), (26,))
+    o, l = oracle.window_attn_fwd(q, k, v, cu_q, cu_k, 0, 0)
+    qq, kk, vv = f64(q), f64(k), f64(v)
+    for i in range(20):
+        j = i + 6                                   # bottom-right aligned key
+        for h in range(4):
+            g = h // 2
+            assert np.allclose(o[i, h], vv[j, g], atol=0)
+            assert abs(l[i, h] - 0.25 * qq[i, h] @ kk[j, g]) < 1e-12
+
+
+@pytest.mark.parametrize("left,right", [(3, 0), (7, 2), (0, 5), (15, -1), (-1, 4), (100, 100)])
+def test_window_band_against_torch_sdpa(left, right):
+    """General windows against torch SDPA (fp64) with the band as its mask."""
+    sq, sk = 30, 41
+    q, k, v, cu_q, cu_k = _window_case(403 + left, (sq,), (sk,))
+    o, l = oracle.window_attn_fwd(q, k, v, cu_q, cu_k, left, right)
+    i = np.arange(sq)[:, None] + sk - sq
+    j = np.arange(sk)[None, :]
+    band = np.ones((sq, sk), bool)
+    if left >= 0:
+        band &= j >= i - left
+    if right >= 0:
+        band &= j <= i + right
+    qq = torch.from_numpy(f64(q)).transpose(0, 1)              # [H, S, d]
+    kk = torch.from_numpy(f64(k)).transpose(0, 1).repeat_interleave(2, 0)
+    vv = torch.from_numpy(f64(v)).transpose(0, 1).repeat_interleave(2, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qq, kk, vv, attn_mask=torch.from_numpy(band), scale=0.25).transpose(0, 1).numpy()
+    rows = band.any(1)
+    assert np.allclose(o[rows], ref[rows], atol=1e-12)
+    assert np.all(o[~rows] == 0) and np.all(l[~rows] == -np.inf)
+
+
+def test_window_uniform_scores_count_the_band():
+    q, k, v, cu_q, cu_k = _window_case(404, (50, 9), (50, 13))
+    q = torch.zeros_like(q)
+    o, l = oracle.window_attn_fwd(q, k, v, cu_q, cu_k, 6, 1)
+    for s, (sq, sk) in enumerate(((50, 50), (9, 13))):
+        for i in range(sq):
+            c = i + sk - sq
+            n = len([j for j in range(sk) if c - 6 <= j <= c + 1])
+            assert abs(l[cu_q[s] + i, 0] - math.log(n)) < 1e-12
