@@ -112,6 +112,36 @@ fsa_status_t fsa_selected_attn_fwd(const void* q, const void* k, const void* v,
                                    size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
+ * Local (sliding-window) attention forward, dense within the window, varlen
+ * layout.  Row i of a sequence with S_q queries and S_k keys attends to every
+ * key j of its sequence with
+ *     i + S_k - S_q - window_left <= j <= i + S_k - S_q + window_right
+ * (window_size = (left, right) of the flash_attn_func docstring on the
+ * flash-attention-npu page; -1 leaves that side unlimited, so (-1, 0) is
+ * causal attention, FlashAttention tutorial page section 4.3, and (-1, -1) is
+ * full attention).  The FSA page's sliding-window branch with window w is
+ * (w - 1, 0).  A row with no key in its window gets O = 0 and LSE = -inf.
+ *
+ *   q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+ *   max_seqlen_q, max_seqlen_k, head dims and groups, softmax_scale,
+ *   num_splits, workspace, out, lse: as in fsa_selected_attn_fwd (no block
+ *   lists); window_left, window_right >= -1
+ */
+size_t fsa_sliding_window_fwd_workspace_size(int32_t batch, int64_t total_q,
+                                             int32_t max_seqlen_q, int32_t num_heads_q,
+                                             int32_t num_heads_kv, int32_t head_dim,
+                                             int32_t num_splits);
+
+fsa_status_t fsa_sliding_window_fwd(const void* q, const void* k, const void* v,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int32_t batch, int64_t total_q, int64_t total_k,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                    int32_t window_left, int32_t window_right,
+                                    float softmax_scale, int32_t num_splits, void* workspace,
+                                    size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
  * Bytes of device workspace fsa_topk_decode needs: the split partials, so 0
  * when the lists are not split (num_splits = 1, or an automatic choice of 1).
  * num_splits = 0 prices the automatic choice.  Returns 0 as well for

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 10
     assert sorted(names) == sorted(_lib.EXPORTS)
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
@@ -182,3 +182,35 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load()
+
+
+def window(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cuq=FAKE, cuk=FAKE, batch=2, total_q=100, total_k=100,
+             maxq=64, maxk=64, hq=8, hkv=2, d=128, wl=511, wr=0, scale=0.0, splits=2,
+             ws=None, ws_bytes=0, out=FAKE, lse=None, stream=None)
+    a.update(kw)
+    return lib.fsa_sliding_window_fwd(a["q"], a["k"], a["v"], a["cuq"], a["cuk"], a["batch"],
+                                      a["total_q"], a["total_k"], a["maxq"], a["maxk"], a["hq"],
+                                      a["hkv"], a["d"], a["wl"], a["wr"], a["scale"], a["splits"],
+                                      a["ws"], a["ws_bytes"], a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(wl=-2), INVALID),
+    (dict(wr=-5), INVALID),
+    (dict(hq=6, hkv=4), INVALID),
+    (dict(d=96), NOT_SUPPORTED),
+    (dict(cuq=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(k=FAKE + 2), INVALID),               # 16-byte alignment
+    (dict(ws=None), WORKSPACE),                # two splits need partials
+])
+def test_sliding_window_argument_errors(lib, kw, code):
+    assert window(lib, **kw) == code
+
+
+def test_sliding_window_workspace(lib):
+    f = lib.fsa_sliding_window_fwd_workspace_size
+    assert f(2, 16384, 8192, 32, 8, 128, 1) == 0
+    assert f(2, 16384, 8192, 32, 8, 128, 4) == 4 * 16384 * 32 * 128 * 4 + 4 * 16384 * 32 * 4
+    assert window(lib, batch=0, q=None, splits=0) == 0

@@ -406,3 +406,62 @@ def test_decode_fp8_full_size_workload():
     print("[gpu] decode fp8 workload: HIP path + oracle", flush=True)
     o, l, ro, rl = run_decode_fp8(dd)
     compare_decode(o, l, ro, rl, what=spec.name + " fp8")
+
+
+# ------------------------------------------------------------------ local (sliding-window) attention
+
+def run_window(d, left, right, num_splits=0):
+    g = to_dev(d, ("q", "k", "v", "cu_seqlens_q", "cu_seqlens_k"))
+    out, l = fsa.fsa_sliding_window_fwd(g["q"], g["k"], g["v"], g["cu_seqlens_q"],
+                                        g["cu_seqlens_k"], d["max_seqlen_q"], d["max_seqlen_k"],
+                                        left, right, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), l.cpu().numpy()
+
+
+WINDOW_CASES = [
+    # seqlens_q, seqlens_k (None = same), hq, hkv, d, (left, right)
+    ((1000, 333), None, 8, 2, 128, (511, 0)),
+    ((700,), (900,), 4, 4, 64, (63, 0)),           # S_k > S_q
+    ((300, 0, 257), None, 16, 1, 128, (64, 0)),    # empty sequence, G = 16
+    ((520,), None, 6, 2, 128, (100, 30)),          # both sides, G = 3
+    ((129, 64), (100, 64), 8, 8, 128, (0, 0)),     # one key per row, S_k < S_q
+    ((600,), None, 8, 1, 64, (-1, 0)),             # causal
+    ((333,), (250,), 4, 2, 128, (-1, -1)),         # global
+    ((2000,), None, 32, 2, 128, (1023, 0)),        # G = 16 wide window
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: f"{c[0]}_{c[4]}_{c[5]}")
+def test_sliding_window_shapes(case):
+    sq, sk, hq, hkv, d, (left, right) = case
+    print(f"[gpu] window {case}", flush=True)
+    spec = inputs.PrefillSpec("w", sq, hq, hkv, d, 1, seed=sum(sq) + hq, seqlens_k=sk)
+    dd = inputs.make_prefill(spec)
+    out, lse = run_window(dd, left, right)
+    ro, rl = oracle.window_attn_fwd(dd["q"], dd["k"], dd["v"], dd["cu_seqlens_q"],
+                                    dd["cu_seqlens_k"], left, right)
+    compare(out, lse, ro, rl, what=str(case))
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_sliding_window_splits_and_exact_band(splits):
+    spec = inputs.PrefillSpec("w", (900, 140), 8, 2, 128, 1, seed=77)
+    dd = inputs.make_prefill(spec)
+    dd["q"] = torch.zeros_like(dd["q"])
+    out, lse = run_window(dd, 200, 0, num_splits=splits)
+    ro, rl = oracle.window_attn_fwd(dd["q"], dd["k"], dd["v"], dd["cu_seqlens_q"],
+                                    dd["cu_seqlens_k"], 200, 0)
+    assert np.abs(lse.T - rl).max() <= 1e-5             # ln(#keys in the band), exactly
+    compare(out, lse, ro, rl, what=f"splits={splits}")
+
+
+def test_sliding_window_512_at_the_bench_shape():
+    """The sliding-window branch (window 512) on B=2, S=8192, Hq=32, Hkv=8, d=128."""
+    spec = inputs.PrefillSpec("w512", (8192, 8192), 32, 8, 128, 1, seed=2)
+    dd = inputs.make_prefill(spec)
+    out, lse = run_window(dd, 511, 0)
+    toks = sample_tokens(dd["cu_seqlens_q"].numpy(), 600, 5)
+    ro, rl = oracle.window_attn_fwd(dd["q"], dd["k"], dd["v"], dd["cu_seqlens_q"],
+                                    dd["cu_seqlens_k"], 511, 0, tokens=toks)
+    compare(out, lse, ro, rl, tokens=toks, what="window 512")

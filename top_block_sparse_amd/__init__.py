@@ -12,6 +12,8 @@ from ._lib import (  # noqa: F401
     fsa_abi_version,
     fsa_selected_attn_fwd,
     fsa_selected_attn_fwd_workspace_size,
+    fsa_sliding_window_fwd,
+    fsa_sliding_window_fwd_workspace_size,
     fsa_status_string,
     fsa_topk_decode,
     fsa_topk_decode_auto_splits,
@@ -21,6 +23,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = [
     "FsaError", "fsa_abi_version", "fsa_selected_attn_fwd",
-    "fsa_selected_attn_fwd_workspace_size", "fsa_status_string", "fsa_topk_decode",
+    "fsa_selected_attn_fwd_workspace_size", "fsa_sliding_window_fwd",
+    "fsa_sliding_window_fwd_workspace_size", "fsa_status_string", "fsa_topk_decode",
     "fsa_topk_decode_auto_splits", "fsa_topk_decode_fp8", "fsa_topk_decode_workspace_size",
 ]

@@ -26,7 +26,8 @@ _STATUS = {0: "FSA_SUCCESS", 1: "FSA_ERROR_INVALID_VALUE", 2: "FSA_ERROR_NOT_SUP
 # Every symbol include/fsa.h declares.
 EXPORTS = ("fsa_status_string", "fsa_abi_version", "fsa_selected_attn_fwd_workspace_size",
            "fsa_selected_attn_fwd", "fsa_topk_decode_workspace_size",
-           "fsa_topk_decode_auto_splits", "fsa_topk_decode", "fsa_topk_decode_fp8")
+           "fsa_topk_decode_auto_splits", "fsa_topk_decode", "fsa_topk_decode_fp8",
+           "fsa_sliding_window_fwd_workspace_size", "fsa_sliding_window_fwd")
 
 _lib = None
 
@@ -57,6 +58,11 @@ def load() -> ctypes.CDLL:
     lib.fsa_selected_attn_fwd.restype = ctypes.c_int
     lib.fsa_selected_attn_fwd.argtypes = [P, P, P, P, P, P, i32, i64, i64, i32, i32, i32, i32, i32,
                                           i32, i32, f32, i32, i32, P, sz, P, P, P]
+    lib.fsa_sliding_window_fwd_workspace_size.restype = sz
+    lib.fsa_sliding_window_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
+    lib.fsa_sliding_window_fwd.restype = ctypes.c_int
+    lib.fsa_sliding_window_fwd.argtypes = [P, P, P, P, P, i32, i64, i64, i32, i32, i32, i32, i32,
+                                           i32, i32, f32, i32, P, sz, P, P, P]
     lib.fsa_topk_decode_fp8.restype = ctypes.c_int
     lib.fsa_topk_decode_fp8.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
                                         i32, f32, i32, P, sz, P, P, P]
@@ -106,6 +112,14 @@ def fsa_selected_attn_fwd_workspace_size(batch: int, total_q: int, max_seqlen_q:
     return int(load().fsa_selected_attn_fwd_workspace_size(batch, total_q, max_seqlen_q,
                                                             num_heads_q, num_heads_kv, head_dim,
                                                             block_size, topk, num_splits))
+
+
+def fsa_sliding_window_fwd_workspace_size(batch: int, total_q: int, max_seqlen_q: int,
+                                          num_heads_q: int, num_heads_kv: int, head_dim: int,
+                                          num_splits: int = 0) -> int:
+    return int(load().fsa_sliding_window_fwd_workspace_size(batch, total_q, max_seqlen_q,
+                                                             num_heads_q, num_heads_kv,
+                                                             head_dim, num_splits))
 
 
 def fsa_topk_decode_workspace_size(batch: int, num_heads_q: int, num_heads_kv: int,
@@ -163,6 +177,49 @@ def fsa_selected_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                    _stream(q.device))
     if st != FSA_SUCCESS:
         raise FsaError(st, "fsa_selected_attn_fwd")
+    return out, lse
+
+
+def fsa_sliding_window_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                           max_seqlen_q: int, max_seqlen_k: int, window_left: int,
+                           window_right: int = 0, softmax_scale: Optional[float] = None,
+                           num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None, return_lse: bool = True
+                           ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Dense attention inside the key window (left, right) (-1 = unlimited);
+    shapes as in ``fsa_selected_attn_fwd``; returns ``(out, lse)``."""
+    lib = load()
+    _check_dev("q", q, torch.bfloat16, 3)
+    _check_dev("k", k, torch.bfloat16, 3)
+    _check_dev("v", v, torch.bfloat16, 3)
+    _check_dev("cu_seqlens_q", cu_seqlens_q, torch.int32, 1)
+    _check_dev("cu_seqlens_k", cu_seqlens_k, torch.int32, 1)
+    total_q, hq, d = q.shape
+    total_k, hkv, _ = k.shape
+    batch = cu_seqlens_q.numel() - 1
+    if tuple(v.shape) != tuple(k.shape) or k.shape[2] != d:
+        raise ValueError("k and v must both be [total_k, Hkv, d] with q's d")
+    if cu_seqlens_k.numel() != batch + 1:
+        raise ValueError("cu_seqlens_k must match cu_seqlens_q")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, total_q), dtype=torch.float32, device=q.device)
+    need = lib.fsa_sliding_window_fwd_workspace_size(batch, total_q, max_seqlen_q, hq, hkv, d,
+                                                     num_splits)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = lib.fsa_sliding_window_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                                    _ptr(cu_seqlens_k), batch, total_q, total_k, max_seqlen_q,
+                                    max_seqlen_k, hq, hkv, d, int(window_left), int(window_right),
+                                    scale, num_splits, _ptr(workspace), ws_bytes, _ptr(out),
+                                    _ptr(lse), _stream(q.device))
+    if st != FSA_SUCCESS:
+        raise FsaError(st, "fsa_sliding_window_fwd")
     return out, lse
 
 

@@ -195,57 +195,33 @@ static fsa_status_t decode_impl(const void* q, const void* k_cache, const void* 
     return FSA_SUCCESS;
 }
 
-extern "C" {
-
-const char* fsa_status_string(fsa_status_t status) {
-    switch (status) {
-        case FSA_SUCCESS: return "FSA_SUCCESS";
-        case FSA_ERROR_INVALID_VALUE: return "FSA_ERROR_INVALID_VALUE";
-        case FSA_ERROR_NOT_SUPPORTED: return "FSA_ERROR_NOT_SUPPORTED";
-        case FSA_ERROR_WORKSPACE: return "FSA_ERROR_WORKSPACE";
-        case FSA_ERROR_LAUNCH: return "FSA_ERROR_LAUNCH";
-    }
-    return "FSA_ERROR_UNKNOWN";
-}
-
-int32_t fsa_abi_version(void) { return FSA_ABI_VERSION; }
-
-size_t fsa_selected_attn_fwd_workspace_size(int32_t batch, int64_t total_q, int32_t max_seqlen_q,
-                                             int32_t num_heads_q, int32_t num_heads_kv,
-                                             int32_t head_dim, int32_t block_size, int32_t topk,
-                                             int32_t num_splits) {
-    if (total_q < 0) return 0;
-    if (check_prefill_shape(batch, max_seqlen_q, num_heads_q, num_heads_kv, head_dim, block_size,
-                            topk, num_splits) != FSA_SUCCESS)
-        return 0;
-    const PrefillPlan pl = plan_prefill(batch, max_seqlen_q, num_heads_q, num_heads_kv, num_splits);
+size_t prefill_workspace(const PrefillPlan& pl, int64_t total_q, int32_t Hq, int32_t D) {
     if (pl.splits <= 1) return 0;
-    const size_t rows = (size_t)total_q * num_heads_q;
-    return align_up((size_t)pl.splits * rows * head_dim * 4) + align_up((size_t)pl.splits * rows * 4);
+    const size_t rows = (size_t)total_q * Hq;
+    return align_up((size_t)pl.splits * rows * D * 4) + align_up((size_t)pl.splits * rows * 4);
 }
 
-fsa_status_t fsa_selected_attn_fwd(const void* q, const void* k, const void* v,
-                                   const int32_t* blk_idx, const int32_t* cu_seqlens_q,
-                                   const int32_t* cu_seqlens_k, int32_t batch, int64_t total_q,
-                                   int64_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                                   int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
-                                   int32_t block_size, int32_t topk, float softmax_scale,
-                                   int32_t causal, int32_t num_splits, void* workspace,
-                                   size_t workspace_bytes, void* out, float* lse, void* stream) {
+static fsa_status_t prefill_impl(const void* q, const void* k, const void* v,
+                                 const int32_t* blk_idx, const int32_t* cu_seqlens_q,
+                                 const int32_t* cu_seqlens_k, int32_t batch, int64_t total_q,
+                                 int64_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                 int32_t block_size, int32_t topk, float softmax_scale,
+                                 int32_t wl, int32_t wr, bool dense, int32_t num_splits,
+                                 void* workspace, size_t workspace_bytes, void* out, float* lse,
+                                 void* stream) {
     fsa_status_t st = check_prefill_shape(batch, max_seqlen_q, num_heads_q, num_heads_kv, head_dim,
                                           block_size, topk, num_splits);
     if (st != FSA_SUCCESS) return st;
     if (total_q < 0 || total_k < 0 || max_seqlen_k < 0) return FSA_ERROR_INVALID_VALUE;
     if (total_q > INT32_MAX || total_k > INT32_MAX) return FSA_ERROR_NOT_SUPPORTED;
     if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FSA_SUCCESS;   // nothing to do
-    if (!q || !k || !v || !blk_idx || !cu_seqlens_q || !cu_seqlens_k || !out)
+    if (!q || !k || !v || (!dense && !blk_idx) || !cu_seqlens_q || !cu_seqlens_k || !out)
         return FSA_ERROR_INVALID_VALUE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return FSA_ERROR_INVALID_VALUE;
     const PrefillPlan pl = plan_prefill(batch, max_seqlen_q, num_heads_q, num_heads_kv, num_splits);
-    const size_t need = fsa_selected_attn_fwd_workspace_size(
-        batch, total_q, max_seqlen_q, num_heads_q, num_heads_kv, head_dim, block_size, topk,
-        num_splits);
+    const size_t need = prefill_workspace(pl, total_q, num_heads_q, head_dim);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
         return FSA_ERROR_WORKSPACE;
     if (pl.n_wg <= 0) return FSA_SUCCESS;
@@ -265,15 +241,17 @@ fsa_status_t fsa_selected_attn_fwd(const void* q, const void* k, const void* v,
     p.Hq = num_heads_q;
     p.Hkv = num_heads_kv;
     p.G = num_heads_q / num_heads_kv;
-    p.topk = topk;
-    p.causal = causal ? 1 : 0;
+    p.topk = dense ? 0 : topk;
+    p.wl = wl;
+    p.wr = wr;
+    p.dense = dense ? 1 : 0;
     p.num_splits = pl.splits;
     p.T = pl.T;
     p.mtiles = pl.mtiles;
     p.tiles_per_seq = pl.tiles_per_seq;
     p.n_wg = pl.n_wg;
-    p.ring = fsa::sel_attn_fwd_ring(head_dim, pl.T, topk);
-    if (fsa::sel_attn_fwd_lds_bytes(head_dim, pl.T, topk, p.ring) > 160 * 1024)
+    p.ring = fsa::sel_attn_fwd_ring(head_dim, pl.T, p.topk);
+    if (fsa::sel_attn_fwd_lds_bytes(head_dim, pl.T, p.topk, p.ring) > 160 * 1024)
         return FSA_ERROR_NOT_SUPPORTED;
     p.scale_log2 = resolve_scale(softmax_scale, head_dim) * fsa::kLog2e;
     const size_t rows = (size_t)total_q * num_heads_q;
@@ -303,6 +281,75 @@ fsa_status_t fsa_selected_attn_fwd(const void* q, const void* k, const void* v,
         if (e != hipSuccess) return FSA_ERROR_LAUNCH;
     }
     return FSA_SUCCESS;
+}
+
+
+extern "C" {
+
+const char* fsa_status_string(fsa_status_t status) {
+    switch (status) {
+        case FSA_SUCCESS: return "FSA_SUCCESS";
+        case FSA_ERROR_INVALID_VALUE: return "FSA_ERROR_INVALID_VALUE";
+        case FSA_ERROR_NOT_SUPPORTED: return "FSA_ERROR_NOT_SUPPORTED";
+        case FSA_ERROR_WORKSPACE: return "FSA_ERROR_WORKSPACE";
+        case FSA_ERROR_LAUNCH: return "FSA_ERROR_LAUNCH";
+    }
+    return "FSA_ERROR_UNKNOWN";
+}
+
+int32_t fsa_abi_version(void) { return FSA_ABI_VERSION; }
+
+size_t fsa_selected_attn_fwd_workspace_size(int32_t batch, int64_t total_q, int32_t max_seqlen_q,
+                                             int32_t num_heads_q, int32_t num_heads_kv,
+                                             int32_t head_dim, int32_t block_size, int32_t topk,
+                                             int32_t num_splits) {
+    if (total_q < 0) return 0;
+    if (check_prefill_shape(batch, max_seqlen_q, num_heads_q, num_heads_kv, head_dim, block_size,
+                            topk, num_splits) != FSA_SUCCESS)
+        return 0;
+    const PrefillPlan pl = plan_prefill(batch, max_seqlen_q, num_heads_q, num_heads_kv, num_splits);
+    return prefill_workspace(pl, total_q, num_heads_q, head_dim);
+}
+
+fsa_status_t fsa_selected_attn_fwd(const void* q, const void* k, const void* v,
+                                   const int32_t* blk_idx, const int32_t* cu_seqlens_q,
+                                   const int32_t* cu_seqlens_k, int32_t batch, int64_t total_q,
+                                   int64_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                   int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                   int32_t block_size, int32_t topk, float softmax_scale,
+                                   int32_t causal, int32_t num_splits, void* workspace,
+                                   size_t workspace_bytes, void* out, float* lse, void* stream) {
+    return prefill_impl(q, k, v, blk_idx, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                        max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim,
+                        block_size, topk, softmax_scale, -1, causal ? 0 : -1, false, num_splits,
+                        workspace, workspace_bytes, out, lse, stream);
+}
+
+size_t fsa_sliding_window_fwd_workspace_size(int32_t batch, int64_t total_q,
+                                             int32_t max_seqlen_q, int32_t num_heads_q,
+                                             int32_t num_heads_kv, int32_t head_dim,
+                                             int32_t num_splits) {
+    return fsa_selected_attn_fwd_workspace_size(batch, total_q, max_seqlen_q, num_heads_q,
+                                                num_heads_kv, head_dim, fsa::kBlockKeys, 1,
+                                                num_splits);
+}
+
+fsa_status_t fsa_sliding_window_fwd(const void* q, const void* k, const void* v,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int32_t batch, int64_t total_q, int64_t total_k,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                    int32_t window_left, int32_t window_right,
+                                    float softmax_scale, int32_t num_splits, void* workspace,
+                                    size_t workspace_bytes, void* out, float* lse, void* stream) {
+    if (window_left < -1 || window_right < -1 || max_seqlen_k < 0) return FSA_ERROR_INVALID_VALUE;
+    // a window at least as long as every sequence is the same as no limit
+    const int32_t wl = window_left > max_seqlen_k ? max_seqlen_k : window_left;
+    const int32_t wr = window_right > max_seqlen_k ? max_seqlen_k : window_right;
+    return prefill_impl(q, k, v, nullptr, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                        max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim,
+                        fsa::kBlockKeys, 1, softmax_scale, wl, wr, true, num_splits, workspace,
+                        workspace_bytes, out, lse, stream);
 }
 
 int32_t fsa_topk_decode_auto_splits(int32_t batch, int32_t num_heads_q, int32_t num_heads_kv,

@@ -21,7 +21,9 @@ struct SelFwdParams {
     float* part_lse;    // [num_splits][total_q*Hq]
     int64_t total_q;
     int64_t total_k;
-    int batch, Hq, Hkv, G, topk, causal, num_splits;
+    int batch, Hq, Hkv, G, topk, num_splits;
+    int wl, wr;         // key window of row i: [i + off - wl, i + off + wr], -1 = unlimited
+    int dense;          // 1: every key of the window (no block lists; blk_idx unused)
     int T;              // query tokens per tile (<= 64)
     int mtiles;         // ceil(T*G/16) 16-row MFMA tiles per tile
     int tiles_per_seq;

@@ -192,11 +192,17 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     const int ntok = (Sq - tok0) < p.T ? (Sq - tok0) : p.T;
     const int off = Sk - Sq;                    // bottom-right alignment shift
     const int nblk = (Sk + kBlockKeys - 1) / kBlockKeys;
-    int nb_range = nblk;                        // blocks that can hold a visible key
-    if (p.causal) {
-        const int last_key = tok0 + ntok - 1 + off;
-        nb_range = last_key < 0 ? 0 : (last_key / kBlockKeys + 1);
-        nb_range = nb_range < nblk ? nb_range : nblk;
+    // Row i sees keys j with i + off - wl <= j <= i + off + wr (a negative
+    // bound is unlimited; causal is wr = 0).  Blocks [nb_lo, nb_range) can
+    // hold a key visible to some row of the tile.
+    int nb_range = nblk, nb_lo = 0;
+    if (p.wr >= 0) {
+        const long long last_key = (long long)tok0 + ntok - 1 + off + p.wr;
+        nb_range = last_key < 0 ? 0 : (int)(last_key / kBlockKeys + 1 < nblk ? last_key / kBlockKeys + 1 : nblk);
+    }
+    if (p.wl >= 0) {
+        const long long first_key = (long long)tok0 + off - p.wl;
+        nb_lo = first_key <= 0 ? 0 : (int)(first_key / kBlockKeys);
     }
     const int topk = p.topk;
     const int G = p.G;
@@ -208,8 +214,10 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         const int tl = e / topk;
         const int slot = e - tl * topk;
         int id = p.blk_idx[((q0 + tok0 + tl) * p.Hkv + g) * (int64_t)topk + slot];
-        bool ok = id >= 0 && id < nb_range;
-        if (ok && p.causal) ok = id * kBlockKeys <= tok0 + tl + off;
+        bool ok = id >= nb_lo && id < nb_range;
+        const long long c = (long long)tok0 + tl + off;
+        if (ok && p.wr >= 0) ok = (long long)id * kBlockKeys <= c + p.wr;
+        if (ok && p.wl >= 0) ok = (long long)id * kBlockKeys + kBlockKeys - 1 >= c - p.wl;
         s_ent[e] = ok ? id : -1;
     }
     if (tid < kSelRingMax * (kSelProducers + 1)) s_ready[tid] = 0u;   // s_ready and s_done
@@ -224,26 +232,33 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     u32x4_t qf[KS];
     unsigned long long mt_tok = 0ull;           // tokens covered by the m-tile (wave-uniform)
-    int row_tok = 64, row_lim = 0, lo_lim = 0x7fffffff;
+    // row_lim: first key past the row's window; row_lo: its first key.
+    // lo_lim / hi_lo: the smallest row_lim / largest row_lo of the m-tile.
+    int row_tok = 64, row_lim = 0, lo_lim = 0x7fffffff, row_lo = 0, hi_lo = 0;
     {
         const int row = mt * 16 + lr;
         const int tl = row / G;
         const int hh = row - tl * G;
         const bool valid = consumer && mt < p.mtiles && tl < ntok;
         row_tok = valid ? tl : 64;
-        int lim = Sk;
-        if (p.causal) {
-            const int c = tok0 + tl + off + 1;
-            lim = c < lim ? c : lim;
-        }
-        row_lim = lim;
-        int lo = valid ? lim : 0x7fffffff;
+        const long long c = (long long)tok0 + tl + off;
+        long long lim = Sk;
+        if (p.wr >= 0 && c + p.wr + 1 < lim) lim = c + p.wr + 1;
+        row_lim = (int)(lim < -1 ? -1 : lim);
+        long long lo_k = 0;
+        if (p.wl >= 0 && c - p.wl > 0) lo_k = c - p.wl;
+        row_lo = (int)lo_k;
+        int lo = valid ? row_lim : 0x7fffffff;
+        int hl = valid ? row_lo : 0;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const int y = __shfl_xor(lo, o);
             lo = y < lo ? y : lo;
+            const int z = __shfl_xor(hl, o);
+            hl = z > hl ? z : hl;
         }
         lo_lim = __builtin_amdgcn_readfirstlane(lo);
+        hi_lo = __builtin_amdgcn_readfirstlane(hl);
         const uint16_t* qrow = p.q + ((q0 + tok0 + tl) * p.Hq + g * G + hh) * (int64_t)D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -285,13 +300,21 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[kt * 4 + i] = st[kt][i];
-        if (blk * kBlockKeys + kBlockKeys > lo_lim) {           // causal edge / sequence end
+        if (blk * kBlockKeys + kBlockKeys > lo_lim) {           // window end / sequence end
             const int lim = row_lim - blk * kBlockKeys;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (kt * 16 + lg * 4 + i >= lim) x[kt * 4 + i] = -INFINITY;
+        }
+        if (blk * kBlockKeys < hi_lo) {                          // window start
+            const int lo = row_lo - blk * kBlockKeys;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (kt * 16 + lg * 4 + i < lo) x[kt * 4 + i] = -INFINITY;
         }
         float mx = x[0];
 #pragma unroll
@@ -386,13 +409,33 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     lds_barrier();   // s_ent and ring flags ready
 
     uint32_t seq0 = 0;    // ring sequence number of the window's first block
-    for (int win_lo = 0; win_lo < nb_range; win_lo += kSelWin) {
+    for (int win_lo = nb_lo; win_lo < nb_range; win_lo += kSelWin) {
         const int win_n = (nb_range - win_lo) < kSelWin ? (nb_range - win_lo) : kSelWin;
-        for (int x = tid; x < kSelWin; x += kSelThreads) s_masks[x] = 0ull;
-        lds_barrier();
-        for (int e = tid; e < nent; e += kSelThreads) {
-            const int id = s_ent[e];
-            if (id >= win_lo && id < win_lo + win_n) atomicOr(&s_masks[id - win_lo], 1ull << (e / topk));
+        if (p.dense) {
+            // every block of the window: the tokens whose key range meets it
+            for (int x = tid; x < kSelWin; x += kSelThreads) {
+                unsigned long long mk = 0ull;
+                if (x < win_n) {
+                    const long long bk = (long long)(win_lo + x) * kBlockKeys;
+                    long long t_lo = 0, t_hi = ntok - 1;
+                    if (p.wr >= 0 && bk - p.wr - tok0 - off > t_lo) t_lo = bk - p.wr - tok0 - off;
+                    if (p.wl >= 0 && bk + kBlockKeys - 1 + p.wl - tok0 - off < t_hi)
+                        t_hi = bk + kBlockKeys - 1 + p.wl - tok0 - off;
+                    if (t_lo <= t_hi) {
+                        const int nbits = (int)(t_hi - t_lo + 1);
+                        mk = (nbits >= 64 ? ~0ull : ((1ull << nbits) - 1ull)) << t_lo;
+                    }
+                }
+                s_masks[x] = mk;
+            }
+            lds_barrier();
+        } else {
+            for (int x = tid; x < kSelWin; x += kSelThreads) s_masks[x] = 0ull;
+            lds_barrier();
+            for (int e = tid; e < nent; e += kSelThreads) {
+                const int id = s_ent[e];
+                if (id >= win_lo && id < win_lo + win_n) atomicOr(&s_masks[id - win_lo], 1ull << (e / topk));
+            }
         }
         lds_barrier();
         if (wave == 0) {      // ascending compaction of the non-empty blocks

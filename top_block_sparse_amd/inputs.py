@@ -275,13 +275,13 @@ def quantize_e4m3(x: torch.Tensor, descale: torch.Tensor, block_table: torch.Ten
     return out
 
 
-def make_decode_fp8(spec: DecodeSpec, unit_factors: bool = False) -> dict:
-    """The decode workload with an FP8 E4M3 cache: the same q, lists, tables
-    and N(0,1) cache values as ``make_decode``, stored as bytes with seeded
-    per (sequence, kv head) dequantisation factors 5/448 * U(0.8, 1.25), so the
-    largest |x| about 5 lands near the top of the E4M3 range (or with all
-    factors 1: the values themselves rounded to E4M3)."""
-    d = make_decode(spec)
+def fp8_from_decode(d: dict, unit_factors: bool = False) -> dict:
+    """The FP8 form of a ``make_decode`` workload: the same q, lists, tables and
+    N(0,1) cache values, stored as E4M3 bytes with seeded per (sequence, kv
+    head) dequantisation factors 5/448 * U(0.8, 1.25), so the largest |x|
+    about 5 lands near the top of the E4M3 range (or with all factors 1: the
+    values themselves rounded to E4M3)."""
+    spec = d["spec"]
     rng = np.random.Generator(np.random.PCG64(6000 + spec.seed))
     shape = (spec.batch, spec.num_heads_kv)
     kd = torch.from_numpy((5.0 / 448.0 * rng.uniform(0.8, 1.25, shape)).astype(np.float32))
@@ -289,12 +289,18 @@ def make_decode_fp8(spec: DecodeSpec, unit_factors: bool = False) -> dict:
     if unit_factors:
         kd = torch.ones(shape, dtype=torch.float32)
         vd = torch.ones(shape, dtype=torch.float32)
-    d["k_cache"] = quantize_e4m3(d["k_cache"], kd, d["block_table"])
-    d["v_cache"] = quantize_e4m3(d["v_cache"], vd, d["block_table"])
-    d["k_descale"] = kd
-    d["v_descale"] = vd
-    d["sets"] = [dict(d["sets"][0], k_cache=d["k_cache"], v_cache=d["v_cache"])]
-    return d
+    e = dict(d)
+    e["k_cache"] = quantize_e4m3(d["k_cache"], kd, d["block_table"])
+    e["v_cache"] = quantize_e4m3(d["v_cache"], vd, d["block_table"])
+    e["k_descale"] = kd
+    e["v_descale"] = vd
+    e["sets"] = [dict(d["sets"][0], k_cache=e["k_cache"], v_cache=e["v_cache"])]
+    return e
+
+
+def make_decode_fp8(spec: DecodeSpec, unit_factors: bool = False) -> dict:
+    """``fp8_from_decode(make_decode(spec))``."""
+    return fp8_from_decode(make_decode(spec), unit_factors)
 
 
 def count_valid_pairs(blk_idx: np.ndarray, cu_q: np.ndarray, cu_k: np.ndarray,
