@@ -69,7 +69,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("full", "prefill", "decode", "copy"), default="full",
+    ap.add_argument("--mode", choices=("full", "prefill", "decode", "decode_fp8", "window", "copy"),
+                    default="full",
                     help="profiling runs: launch only one kernel family (or a plain 1 GiB "
                          "device copy used to calibrate HBM byte counters) --steps times, "
                          "print timings, no JSON line")
@@ -104,8 +105,9 @@ def main():
         return
 
     # ---------------- inputs (generated on the host, then resident in HBM)
-    want_p = args.mode in ("full", "prefill")
-    want_d = args.mode in ("full", "decode")
+    want_p = args.mode in ("full", "prefill", "window")
+    want_d = args.mode in ("full", "decode", "decode_fp8")
+    want_f8 = args.mode in ("full", "decode_fp8")
     pspec = inputs.PREFILL_WORKLOADS[PREFILL]
     dspec = inputs.DECODE_WORKLOADS[DECODE]
     if want_p:
@@ -142,9 +144,32 @@ def main():
             dspec.batch, dspec.num_heads_q, dspec.num_heads_kv, dspec.head_dim, dspec.topk, 0),
             dtype=torch.uint8, device=dev)
         n_sel = dspec.batch * dspec.num_heads_kv * dspec.topk      # lists hold distinct positions
-        d_bytes = (n_sel * 2 * dspec.head_dim * 2                  # selected K and V rows
-                   + dtok.numel() * 4 + dbt.numel() * 4 + dcs.numel() * 4
-                   + dq.numel() * 2 + d_out.numel() * 2 + d_lse.numel() * 4)
+        small = (dtok.numel() * 4 + dbt.numel() * 4 + dcs.numel() * 4
+                 + dq.numel() * 2 + d_out.numel() * 2 + d_lse.numel() * 4)
+        d_bytes = n_sel * 2 * dspec.head_dim * 2 + small           # selected bf16 K and V rows
+        if want_f8:
+            log("quantising the decode cache to FP8 E4M3")
+            f8 = inputs.fp8_from_decode(dd)
+            k8 = f8["k_cache"].to(dev)
+            v8 = f8["v_cache"].to(dev)
+            sets8 = [(k8, v8), (k8.clone(), v8.clone())]
+            kd8 = f8["k_descale"].to(dev)
+            vd8 = f8["v_descale"].to(dev)
+            del f8
+            f8_bytes = n_sel * 2 * dspec.head_dim * 1 + small + 2 * kd8.numel() * 4
+        if args.mode == "decode_fp8":
+            del sets
+
+    WINDOW = 512
+    # keys visible to each row under the causal window (WINDOW - 1, 0)
+    w_keys = sum(min(WINDOW, i + 1) for s_len in pspec.seqlens for i in range(s_len))
+    w_flops = 4.0 * pspec.head_dim * pspec.num_heads_q * w_keys
+    w_out = torch.empty_like(pg["q"]) if want_p else None
+
+    def window():
+        fsa.fsa_sliding_window_fwd(pg["q"], pg["k"], pg["v"], pg["cu_seqlens_q"],
+                                   pg["cu_seqlens_k"], pd["max_seqlen_q"], pd["max_seqlen_k"],
+                                   WINDOW - 1, 0, out=w_out, lse=p_lse)
 
     def prefill():
         fsa.fsa_selected_attn_fwd(pg["q"], pg["k"], pg["v"], pg["blk_idx"], pg["cu_seqlens_q"],
@@ -155,9 +180,16 @@ def main():
         k_, v_ = sets[i % 2]
         fsa.fsa_topk_decode(dq, k_, v_, dtok, dbt, dcs, out=d_out, lse=d_lse, workspace=d_ws)
 
-    if args.mode in ("prefill", "decode"):
+    def decode_fp8(i):
+        k_, v_ = sets8[i % 2]
+        fsa.fsa_topk_decode_fp8(dq, k_, v_, kd8, vd8, dtok, dbt, dcs, out=d_out, lse=d_lse,
+                                workspace=d_ws)
+
+    if args.mode in ("prefill", "decode", "decode_fp8"):
+        step = {"prefill": lambda i: prefill(), "decode": decode, "decode_fp8": decode_fp8,
+                "window": lambda i: window()}[args.mode]
         for i in range(args.warmup + args.steps):
-            prefill() if args.mode == "prefill" else decode(i)
+            step(i)
         torch.cuda.synchronize()
         log(f"{args.mode}: {args.warmup + args.steps} launches")
         return
@@ -166,6 +198,8 @@ def main():
     for i in range(args.warmup):
         prefill()
         decode(i)
+        decode_fp8(i)
+        window()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -193,7 +227,30 @@ def main():
     torch.cuda.synchronize()
     t_decode = time.perf_counter() - t0
 
+    log(f"timing {K} FP8 decode calls")
+    f_ev = [(ev(), ev()) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        f_ev[i][0].record(stream)
+        decode_fp8(i)
+        f_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_f8 = time.perf_counter() - t0
+
+    log(f"timing {K} sliding-window calls")
+    w_ev = [(ev(), ev()) for _ in range(K)]
+    for i in range(K):
+        w_ev[i][0].record(stream)
+        window()
+        w_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+
     p_ms = np.array([a.elapsed_time(b) for a, b in p_ev])
+    f_ms = np.array([a.elapsed_time(b) for a, b in f_ev])
+    w_ms = np.array([a.elapsed_time(b) for a, b in w_ev])
+    w_tflops = w_flops / (w_ms.mean() * 1e-3) / 1e12
+    f_gbs_evt = f8_bytes / (f_ms.mean() * 1e-3) / 1e9
     d_ms = np.array([a.elapsed_time(b) for a, b in d_ev])
     p_tflops_wall = flops * K / t_prefill / 1e12
     p_tflops_evt = flops / (p_ms.mean() * 1e-3) / 1e12
@@ -203,6 +260,8 @@ def main():
         f"{p_tflops_evt:.1f} TFLOP/s (events), {p_tflops_wall:.1f} (wall)")
     log(f"decode : mean {d_ms.mean() * 1e3:.1f} us  min {d_ms.min() * 1e3:.1f} us  "
         f"{d_gbs_evt:.0f} GB/s (events), {d_gbs_wall:.0f} (wall)")
+    log(f"decode8: mean {f_ms.mean() * 1e3:.1f} us  min {f_ms.min() * 1e3:.1f} us  "
+        f"{f_gbs_evt:.0f} GB/s (events), {f8_bytes * K / t_f8 / 1e9:.0f} (wall)")
 
     kern_src = os.path.join(ROOT, "top_block_sparse_amd", "csrc", "sel_attn_fwd.hip")
     traffic = measured_traffic(kern_src, PREFILL)
@@ -219,6 +278,26 @@ def main():
                      "unit": "GB/s", "frac": round(d_gbs_evt / PEAK_HBM_GBS, 4),
                      "traffic": d_traffic, "bytes_per_call": d_bytes,
                      "scope": "whole call: prepass + split + merge kernels"},
+    }
+
+    log(f"window : mean {w_ms.mean():.3f} ms  {w_tflops:.1f} TFLOP/s (events)")
+    window_obj = {
+        "value": round(w_tflops, 2), "unit": "TFLOP/s",
+        "workload": f"sliding_window_{WINDOW}_b2_s8192_h32_kv8_d128",
+        "ms_per_call": round(float(w_ms.mean()), 4),
+        "roofline": {"bound": "mfma", "achieved": round(w_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(w_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "flops_per_call": w_flops},
+    }
+    decode_fp8_obj = {
+        "value": round(f_gbs_evt, 1), "unit": "GB/s", "workload": DECODE + "_fp8_e4m3",
+        "us_per_call": round(float(f_ms.mean()) * 1e3, 2),
+        "gbs_wall": round(f8_bytes * K / t_f8 / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(f_gbs_evt, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(f_gbs_evt / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(dec_src, DECODE + "_fp8"),
+                     "bytes_per_call": f8_bytes,
+                     "scope": "whole call; K/V rows 1 byte per element"},
     }
 
     result = {
@@ -242,6 +321,8 @@ def main():
                    "decode_bytes_per_call": d_bytes},
         "roofline": roofline,
         "decode": decode_obj,
+        "decode_fp8": decode_fp8_obj,
+        "sliding_window": window_obj,
     }
 
     if not args.no_cpu_baseline:
