@@ -51,6 +51,9 @@ def _load():
         lib.oracle_topk_decode.restype = ctypes.c_int
         lib.oracle_topk_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
                                            i32, f64, P, i64, P, P]
+        lib.oracle_selected_attn_bwd.restype = ctypes.c_int
+        lib.oracle_selected_attn_bwd.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                                 i32, f64, i32, P, P, P]
         lib.oracle_window_attn_fwd.restype = ctypes.c_int
         lib.oracle_window_attn_fwd.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, i64, f64,
                                                P, i64, P, P]
@@ -142,6 +145,33 @@ def topk_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, t
     if rc != 0:
         raise ValueError("oracle_topk_decode rejected its arguments")
     return out, lse
+
+
+def selected_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
+                      blk_idx, cu_seqlens_q, cu_seqlens_k, block_size: int,
+                      softmax_scale: Optional[float] = None, causal: bool = True):
+    """Gradients of sum(dout * O) for the selected-attention forward.
+    Returns ``(dq [total_q,Hq,d], dk [total_k,Hkv,d], dv [total_k,Hkv,d])`` float64."""
+    lib = _load()
+    total_q, Hq, d = q.shape
+    total_k, Hkv, _ = k.shape
+    blk = _i32(blk_idx)
+    cu_q = _i32(cu_seqlens_q)
+    cu_k = _i32(cu_seqlens_k)
+    batch = cu_q.size - 1
+    topk = blk.shape[-1] if blk.ndim == 3 else 0
+    scale = (1.0 / np.sqrt(d)) if softmax_scale is None else float(softmax_scale)
+    qb, kb, vb, db = _bits(q), _bits(k), _bits(v), _bits(dout)
+    dq = np.zeros((total_q, Hq, d), dtype=np.float64)
+    dk = np.zeros((total_k, Hkv, d), dtype=np.float64)
+    dv = np.zeros((total_k, Hkv, d), dtype=np.float64)
+    rc = lib.oracle_selected_attn_bwd(qb.data_ptr(), kb.data_ptr(), vb.data_ptr(), db.data_ptr(),
+                                      blk.ctypes.data, cu_q.ctypes.data, cu_k.ctypes.data, batch,
+                                      Hq, Hkv, d, block_size, topk, scale, int(causal),
+                                      dq.ctypes.data, dk.ctypes.data, dv.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_selected_attn_bwd rejected its arguments")
+    return dq, dk, dv
 
 
 def window_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q,

@@ -184,6 +184,110 @@ int oracle_selected_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_
 }
 
 /*
+ * Backward of selected attention: the gradients of sum(dO * O) with respect to
+ * q, k and v, O being the forward above (the training use of selected
+ * attention on the FSA page).  For each row (token i, q head h) with visible
+ * key set J (exactly the forward's), P_j = exp(s_j - LSE), O = sum_j P_j v_j
+ * and, by the chain rule through the softmax,
+ *   D = sum_c dO_c O_c,  dP_j = <dO, v_j>,  dS_j = P_j (dP_j - D),
+ *   dq = scale * sum_j dS_j k_j,  dk_j += scale * dS_j q,  dv_j += P_j dO.
+ * Inputs as in oracle_selected_attn_fwd plus dout [total_q, Hq, d] (bf16
+ * bits); outputs dq [total_q, Hq, d], dk and dv [total_k, Hkv, d] (fp64),
+ * every element written (keys no row sees get 0).  Work is split over
+ * (sequence, kv head) pairs, whose dk / dv rows are disjoint.
+ */
+int oracle_selected_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const uint16_t* dout, const int32_t* blk_idx, const int32_t* cu_q,
+                             const int32_t* cu_k, int32_t batch, int32_t Hq, int32_t Hkv,
+                             int32_t d, int32_t block_size, int32_t topk, double scale,
+                             int32_t causal, double* dq, double* dk, double* dv) {
+    if (batch < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || block_size <= 0 ||
+        topk < 0)
+        return -1;
+    const int G = Hq / Hkv;
+    const int64_t total_q = cu_q[batch], total_k = cu_k[batch];
+    memset(dq, 0, sizeof(double) * (size_t)total_q * Hq * d);
+    memset(dk, 0, sizeof(double) * (size_t)total_k * Hkv * d);
+    memset(dv, 0, sizeof(double) * (size_t)total_k * Hkv * d);
+    const int64_t cap = (int64_t)(topk > 0 ? topk : 1) * block_size;
+#pragma omp parallel
+    {
+        int64_t* blocks = (int64_t*)malloc(sizeof(int64_t) * (size_t)(topk > 0 ? topk : 1));
+        int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
+        double* p = (double*)malloc(sizeof(double) * (size_t)cap);
+        double* o = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int sq_id = 0; sq_id < batch; ++sq_id) {
+            for (int g = 0; g < Hkv; ++g) {
+                const int64_t Sq = cu_q[sq_id + 1] - cu_q[sq_id];
+                const int64_t Sk = cu_k[sq_id + 1] - cu_k[sq_id];
+                const int64_t nblk = (Sk + block_size - 1) / block_size;
+                for (int64_t i = 0; i < Sq; ++i) {
+                    const int64_t t = cu_q[sq_id] + i;
+                    int64_t nb = 0;
+                    const int32_t* lst = blk_idx + (t * Hkv + g) * (int64_t)topk;
+                    for (int e = 0; e < topk; ++e)
+                        if (lst[e] >= 0 && lst[e] < nblk) blocks[nb++] = lst[e];
+                    nb = sort_unique(blocks, nb);
+                    int64_t nk = 0;
+                    for (int64_t bi = 0; bi < nb; ++bi)
+                        for (int64_t j = blocks[bi] * block_size;
+                             j < (blocks[bi] + 1) * block_size && j < Sk; ++j) {
+                            if (causal && j > i + Sk - Sq) continue;
+                            keys[nk++] = (cu_k[sq_id] + j) * Hkv + g;     /* key row */
+                        }
+                    if (nk == 0) continue;
+                    for (int hh = 0; hh < G; ++hh) {
+                        const int h = g * G + hh;
+                        const uint16_t* qr = q + (t * Hq + h) * (int64_t)d;
+                        const uint16_t* dor = dout + (t * Hq + h) * (int64_t)d;
+                        double m = -INFINITY;
+                        for (int64_t j = 0; j < nk; ++j) {
+                            const uint16_t* kr = k + keys[j] * d;
+                            double dot = 0.0;
+                            for (int c = 0; c < d; ++c) dot += widen_bf16(qr[c]) * widen_bf16(kr[c]);
+                            p[j] = scale * dot;
+                            if (p[j] > m) m = p[j];
+                        }
+                        double sum = 0.0;
+                        for (int64_t j = 0; j < nk; ++j) sum += exp(p[j] - m);
+                        const double lse = m + log(sum);
+                        for (int c = 0; c < d; ++c) o[c] = 0.0;
+                        for (int64_t j = 0; j < nk; ++j) {
+                            p[j] = exp(p[j] - lse);
+                            const uint16_t* vr = v + keys[j] * d;
+                            for (int c = 0; c < d; ++c) o[c] += p[j] * widen_bf16(vr[c]);
+                        }
+                        double D = 0.0;
+                        for (int c = 0; c < d; ++c) D += widen_bf16(dor[c]) * o[c];
+                        double* dqr = dq + (t * Hq + h) * (int64_t)d;
+                        for (int64_t j = 0; j < nk; ++j) {
+                            const uint16_t* kr = k + keys[j] * d;
+                            const uint16_t* vr = v + keys[j] * d;
+                            double dp = 0.0;
+                            for (int c = 0; c < d; ++c) dp += widen_bf16(dor[c]) * widen_bf16(vr[c]);
+                            const double ds = p[j] * (dp - D);
+                            double* dkr = dk + keys[j] * d;
+                            double* dvr = dv + keys[j] * d;
+                            for (int c = 0; c < d; ++c) {
+                                dqr[c] += scale * ds * widen_bf16(kr[c]);
+                                dkr[c] += scale * ds * widen_bf16(qr[c]);
+                                dvr[c] += p[j] * widen_bf16(dor[c]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        free(blocks);
+        free(keys);
+        free(p);
+        free(o);
+    }
+    return 0;
+}
+
+/*
  * Local (sliding-window) attention, dense within the window.  Row i of a
  * sequence with S_q queries and S_k keys attends to every key j with
  *   i + S_k - S_q - left <= j <= i + S_k - S_q + right,   0 <= j < S_k,

@@ -589,3 +589,99 @@ def test_window_uniform_scores_count_the_band():
             c = i + sk - sq
             n = len([j for j in range(sk) if c - 6 <= j <= c + 1])
             assert abs(l[cu_q[s] + i, 0] - math.log(n)) < 1e-12
+
+
+# ------------------------------------------------------------------ backward
+
+def _autograd_dense(q, k, v, dout, cu, causal, scale, G):
+    """torch autograd (fp64, CPU) of masked softmax attention per sequence; K/V
+    expanded over each GQA group, their gradients summed back."""
+    dq = torch.zeros(q.shape, dtype=torch.float64)
+    dk = torch.zeros(k.shape, dtype=torch.float64)
+    dv = torch.zeros(v.shape, dtype=torch.float64)
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b == a:
+            continue
+        qq = torch.from_numpy(f64(q[a:b])).transpose(0, 1).clone().requires_grad_(True)
+        kk = torch.from_numpy(f64(k[a:b])).transpose(0, 1).clone().requires_grad_(True)
+        vv = torch.from_numpy(f64(v[a:b])).transpose(0, 1).clone().requires_grad_(True)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qq, kk.repeat_interleave(G, 0), vv.repeat_interleave(G, 0), is_causal=causal,
+            scale=scale)
+        (o * torch.from_numpy(f64(dout[a:b])).transpose(0, 1)).sum().backward()
+        dq[a:b] = qq.grad.transpose(0, 1)
+        dk[a:b] = kk.grad.transpose(0, 1)
+        dv[a:b] = vv.grad.transpose(0, 1)
+    return dq.numpy(), dk.numpy(), dv.numpy()
+
+
+@pytest.mark.parametrize("G", [1, 3])
+def test_bwd_all_blocks_equals_torch_autograd(G):
+    seqlens = (37, 64, 9)
+    hkv, d, bs = 2, 16, 8
+    hq = G * hkv
+    cu = np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32)
+    total = int(cu[-1])
+    q = rand_bf16((total, hq, d), 501)
+    k = rand_bf16((total, hkv, d), 502)
+    v = rand_bf16((total, hkv, d), 503)
+    do = rand_bf16((total, hq, d), 504)
+    nb = -(-max(seqlens) // bs)
+    blk = np.tile(np.arange(nb, dtype=np.int32), (total, hkv, 1))   # every block (future ones skipped)
+    dq, dk, dv = oracle.selected_attn_bwd(q, k, v, do, blk, cu, cu, bs)
+    rq, rk, rv = _autograd_dense(q, k, v, do, cu, True, 1 / 4, G)
+    assert np.allclose(dq, rq, atol=1e-11) and np.allclose(dk, rk, atol=1e-11)
+    assert np.allclose(dv, rv, atol=1e-11)
+
+
+def test_bwd_finite_differences_with_noisy_lists():
+    """Central differences of sum(dO * O) through the (pinned) forward oracle, on
+    inputs whose +-1/64 steps are exact in bf16; lists hold repeats, -1,
+    out-of-range and future ids."""
+    rng = np.random.default_rng(7)
+    S, hq, hkv, d, bs, topk = 12, 4, 2, 4, 2, 5
+    grid = lambda shape: torch.from_numpy(rng.integers(-12, 13, size=shape) / 16.0).to(torch.bfloat16)
+    q, k, v, do = grid((S, hq, d)), grid((S, hkv, d)), grid((S, hkv, d)), grid((S, hq, d))
+    blk = rng.integers(-1, 8, size=(S, hkv, topk)).astype(np.int32)
+    blk[:, :, 1] = blk[:, :, 0]
+    cu = np.array([0, S], np.int32)
+    dq, dk, dv = oracle.selected_attn_bwd(q, k, v, do, blk, cu, cu, bs)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.selected_attn_fwd(qq, kk, vv, blk, cu, cu, bs)
+        return float((o * f64(do)).sum())
+
+    eps = 1.0 / 64
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in [tuple(rng.integers(0, n) for n in x.shape) for _ in range(12)]:
+            xp, xm = x.clone(), x.clone()
+            xp[idx] = float(x[idx]) + eps
+            xm[idx] = float(x[idx]) - eps
+            assert float(xp[idx]) - float(xm[idx]) == 2 * eps      # exact in bf16
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - g[idx]) <= 2e-3 * (1 + abs(g[idx])), (name, idx, fd, g[idx])
+
+
+def test_bwd_gqa_equals_summed_mha():
+    """GQA gradients of a kv head equal the sum over its query heads of the
+    gradients with K/V expanded to one kv head per query head."""
+    S, hkv, G, d, bs, topk = 40, 2, 3, 16, 8, 3
+    hq = hkv * G
+    q = rand_bf16((S, hq, d), 511)
+    k = rand_bf16((S, hkv, d), 512)
+    v = rand_bf16((S, hkv, d), 513)
+    do = rand_bf16((S, hq, d), 514)
+    rng = np.random.default_rng(5)
+    blk = rng.integers(-1, 5, size=(S, hkv, topk)).astype(np.int32)
+    cu = np.array([0, S], np.int32)
+    dq, dk, dv = oracle.selected_attn_bwd(q, k, v, do, blk, cu, cu, bs)
+    ke = k.repeat_interleave(G, 1)
+    ve = v.repeat_interleave(G, 1)
+    be = np.repeat(blk, G, axis=1)
+    dq2, dk2, dv2 = oracle.selected_attn_bwd(q, ke, ve, do, be, cu, cu, bs)
+    assert np.allclose(dq, dq2, atol=1e-12)
+    assert np.allclose(dk, dk2.reshape(S, hkv, G, d).sum(2), atol=1e-12)
+    assert np.allclose(dv, dv2.reshape(S, hkv, G, d).sum(2), atol=1e-12)
