@@ -112,6 +112,40 @@ fsa_status_t fsa_selected_attn_fwd(const void* q, const void* k, const void* v,
                                    size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
+ * Backward of fsa_selected_attn_fwd (the training use of selected attention
+ * on the FSA page): the gradients of sum(dout * out) with respect to q, k and
+ * v, for the same lists, causal flag and scale as the forward call.
+ *
+ *   q, k, v, blk_idx, cu_seqlens_q/k, batch, total_q, total_k, max_seqlen_q,
+ *            max_seqlen_k, head counts, head_dim, block_size, topk,
+ *            softmax_scale, causal: as in fsa_selected_attn_fwd (head groups
+ *            num_heads_q / num_heads_kv <= 32)
+ *   out      bf16 [total_q, num_heads_q, head_dim]: the forward's output
+ *   lse      fp32 [num_heads_q, total_q]: the forward's LSE
+ *   dout     bf16 [total_q, num_heads_q, head_dim]: gradient of the output
+ *   workspace at least fsa_selected_attn_bwd_workspace_size(...) bytes,
+ *            256-byte aligned
+ *   dq       bf16 [total_q, num_heads_q, head_dim]
+ *   dk, dv   bf16 [total_k, num_heads_kv, head_dim]; keys no row sees get 0
+ * Rows with no visible key get dq = 0.  dk and dv are summed in an order that
+ * can change between calls, so they may differ in the last bits run to run.
+ */
+size_t fsa_selected_attn_bwd_workspace_size(int32_t batch, int64_t total_q, int32_t max_seqlen_q,
+                                            int32_t max_seqlen_k, int32_t num_heads_q,
+                                            int32_t num_heads_kv, int32_t head_dim,
+                                            int32_t block_size, int32_t topk);
+
+fsa_status_t fsa_selected_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                                   const float* lse, const void* dout, const int32_t* blk_idx,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                   int32_t batch, int64_t total_q, int64_t total_k,
+                                   int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                   int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                   int32_t block_size, int32_t topk, float softmax_scale,
+                                   int32_t causal, void* workspace, size_t workspace_bytes,
+                                   void* dq, void* dk, void* dv, void* stream);
+
+/*
  * Local (sliding-window) attention forward, dense within the window, varlen
  * layout.  Row i of a sequence with S_q queries and S_k keys attends to every
  * key j of its sequence with

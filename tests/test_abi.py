@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     assert sorted(names) == sorted(_lib.EXPORTS)
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
@@ -214,3 +214,40 @@ def test_sliding_window_workspace(lib):
     assert f(2, 16384, 8192, 32, 8, 128, 1) == 0
     assert f(2, 16384, 8192, 32, 8, 128, 4) == 4 * 16384 * 32 * 128 * 4 + 4 * 16384 * 32 * 4
     assert window(lib, batch=0, q=None, splits=0) == 0
+
+
+def bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, blk=FAKE, cuq=FAKE, cuk=FAKE,
+             batch=2, total_q=100, total_k=100, maxq=64, maxk=64, hq=8, hkv=2, d=128, bs=64,
+             topk=16, scale=0.0, causal=1, ws=None, ws_bytes=0, dq=FAKE, dk=FAKE, dv=FAKE,
+             stream=None)
+    a.update(kw)
+    return lib.fsa_selected_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["blk"],
+                                     a["cuq"], a["cuk"], a["batch"], a["total_q"], a["total_k"],
+                                     a["maxq"], a["maxk"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                     a["topk"], a["scale"], a["causal"], a["ws"], a["ws_bytes"],
+                                     a["dq"], a["dk"], a["dv"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=6, hkv=4), INVALID),
+    (dict(d=96), NOT_SUPPORTED),
+    (dict(bs=32), NOT_SUPPORTED),
+    (dict(topk=65), NOT_SUPPORTED),
+    (dict(hq=128, hkv=2), NOT_SUPPORTED),      # group above 32
+    (dict(lse=None), INVALID),
+    (dict(do=None), INVALID),
+    (dict(dv=FAKE + 8), INVALID),
+    (dict(ws=None), WORKSPACE),
+    (dict(ws=FAKE, ws_bytes=1024), WORKSPACE),
+])
+def test_bwd_argument_errors(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_bwd_workspace(lib):
+    f = lib.fsa_selected_attn_bwd_workspace_size
+    n = f(2, 16384, 8192, 8192, 32, 8, 128, 64, 16)
+    assert n >= 32 * 16384 * 4 + 16 * 129 * 4 + 16 * 128 * 4 + 16384 * 8 * 16 * 4
+    assert f(2, 16384, 8192, 8192, 32, 8, 96, 64, 16) == 0
+    assert bwd(lib, batch=0, q=None) == 0

@@ -465,3 +465,82 @@ def test_sliding_window_512_at_the_bench_shape():
     ro, rl = oracle.window_attn_fwd(dd["q"], dd["k"], dd["v"], dd["cu_seqlens_q"],
                                     dd["cu_seqlens_k"], 511, 0, tokens=toks)
     compare(out, lse, ro, rl, tokens=toks, what="window 512")
+
+
+# ------------------------------------------------------------------ backward
+# Gradients are stored in bf16 (relative step 2^-9) and the kernels feed P and
+# dS to the MFMAs as bf16 with fp32 accumulation, so each element is held to
+# |err| <= 3e-2 * (1 + |ref|) and the mean error to 5e-3 of the mean |ref|.
+G_REL, G_MEAN = 3e-2, 5e-3
+
+
+def run_bwd(dd, do, causal=True):
+    g = to_dev(dd, ("q", "k", "v", "blk_idx", "cu_seqlens_q", "cu_seqlens_k"))
+    out, lse = fsa.fsa_selected_attn_fwd(g["q"], g["k"], g["v"], g["blk_idx"], g["cu_seqlens_q"],
+                                         g["cu_seqlens_k"], dd["max_seqlen_q"], dd["max_seqlen_k"],
+                                         causal=causal)
+    dq, dk, dv = fsa.fsa_selected_attn_bwd(g["q"], g["k"], g["v"], out, lse, do.to(DEV),
+                                           g["blk_idx"], g["cu_seqlens_q"], g["cu_seqlens_k"],
+                                           dd["max_seqlen_q"], dd["max_seqlen_k"], causal=causal)
+    torch.cuda.synchronize()
+    return [x.float().cpu().numpy() for x in (dq, dk, dv)]
+
+
+def compare_grads(got, ref, what=""):
+    for nm, a, r in zip(("dq", "dk", "dv"), got, ref):
+        assert np.isfinite(a).all(), f"{what} {nm}"
+        e = np.abs(a - r)
+        worst = (e / (1.0 + np.abs(r))).max()
+        assert worst <= G_REL, f"{what} {nm} max err/(1+|ref|) = {worst:.3e}"
+        assert e.mean() <= G_MEAN * max(np.abs(r).mean(), 1e-3), f"{what} {nm} mean err {e.mean():.3e}"
+
+
+BWD_SHAPES = [
+    # seqlens_q, seqlens_k (None = same), hq, hkv, d, topk
+    ((1024,), None, 4, 1, 64, 4),
+    ((700, 300), None, 8, 2, 128, 8),
+    ((513, 0, 200), None, 16, 1, 128, 6),          # empty sequence, G = 16
+    ((400,), (650,), 6, 2, 64, 16),                # S_k > S_q, G = 3
+    ((300,), (200,), 8, 8, 128, 8),                # S_k < S_q: early rows see nothing
+    ((900,), None, 4, 4, 128, 16),                 # G = 1
+    ((257,), None, 64, 2, 128, 5),                 # G = 32
+]
+
+
+@pytest.mark.parametrize("case", BWD_SHAPES, ids=lambda c: f"{c[0]}_{c[2]}_{c[3]}_{c[4]}_{c[5]}")
+def test_bwd_shapes_with_index_edge_cases(case):
+    sq, sk, hq, hkv, d, topk = case
+    print(f"[gpu] backward {case}", flush=True)
+    spec = inputs.PrefillSpec("b", sq, hq, hkv, d, topk, seed=sum(sq) + topk, seqlens_k=sk)
+    dd = inputs.make_prefill(spec)
+    dd["blk_idx"] = torch.from_numpy(mutate_lists(dd["blk_idx"].numpy(), dd["cu_seqlens_q"].numpy(),
+                                                  dd["cu_seqlens_k"].numpy(), 64,
+                                                  np.random.default_rng(topk)))
+    do = inputs.randn_bf16(tuple(dd["q"].shape), 9100 + topk)
+    got = run_bwd(dd, do)
+    ref = oracle.selected_attn_bwd(dd["q"], dd["k"], dd["v"], do, dd["blk_idx"],
+                                   dd["cu_seqlens_q"], dd["cu_seqlens_k"], 64)
+    compare_grads(got, ref, what=str(case))
+
+
+def test_bwd_not_causal():
+    spec = inputs.PrefillSpec("b", (600, 128), 8, 2, 128, 8, seed=31, causal=False)
+    dd = inputs.make_prefill(spec)
+    do = inputs.randn_bf16(tuple(dd["q"].shape), 9200)
+    got = run_bwd(dd, do, causal=False)
+    ref = oracle.selected_attn_bwd(dd["q"], dd["k"], dd["v"], do, dd["blk_idx"],
+                                   dd["cu_seqlens_q"], dd["cu_seqlens_k"], 64, causal=False)
+    compare_grads(got, ref, what="not causal")
+
+
+def test_bwd_medium_gqa_workload():
+    """B=1, S=4096, Hq=32, Hkv=8, d=128, topk 16 (the bench layout at half length)."""
+    spec = inputs.PrefillSpec("b", (4096,), 32, 8, 128, 16, seed=33)
+    dd = inputs.make_prefill(spec)
+    do = inputs.randn_bf16(tuple(dd["q"].shape), 9300)
+    print("[gpu] backward medium: HIP path", flush=True)
+    got = run_bwd(dd, do)
+    print("[gpu] backward medium: oracle", flush=True)
+    ref = oracle.selected_attn_bwd(dd["q"], dd["k"], dd["v"], do, dd["blk_idx"],
+                                   dd["cu_seqlens_q"], dd["cu_seqlens_k"], 64)
+    compare_grads(got, ref, what="medium")

@@ -10,6 +10,8 @@ call through the binding loads the library and raises if it is not built.
 from ._lib import (  # noqa: F401
     FsaError,
     fsa_abi_version,
+    fsa_selected_attn_bwd,
+    fsa_selected_attn_bwd_workspace_size,
     fsa_selected_attn_fwd,
     fsa_selected_attn_fwd_workspace_size,
     fsa_sliding_window_fwd,
@@ -22,7 +24,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "FsaError", "fsa_abi_version", "fsa_selected_attn_fwd",
+    "FsaError", "fsa_abi_version", "fsa_selected_attn_bwd", "fsa_selected_attn_bwd_workspace_size",
+    "fsa_selected_attn_fwd",
     "fsa_selected_attn_fwd_workspace_size", "fsa_sliding_window_fwd",
     "fsa_sliding_window_fwd_workspace_size", "fsa_status_string", "fsa_topk_decode",
     "fsa_topk_decode_auto_splits", "fsa_topk_decode_fp8", "fsa_topk_decode_workspace_size",

@@ -27,7 +27,8 @@ _STATUS = {0: "FSA_SUCCESS", 1: "FSA_ERROR_INVALID_VALUE", 2: "FSA_ERROR_NOT_SUP
 EXPORTS = ("fsa_status_string", "fsa_abi_version", "fsa_selected_attn_fwd_workspace_size",
            "fsa_selected_attn_fwd", "fsa_topk_decode_workspace_size",
            "fsa_topk_decode_auto_splits", "fsa_topk_decode", "fsa_topk_decode_fp8",
-           "fsa_sliding_window_fwd_workspace_size", "fsa_sliding_window_fwd")
+           "fsa_sliding_window_fwd_workspace_size", "fsa_sliding_window_fwd",
+           "fsa_selected_attn_bwd_workspace_size", "fsa_selected_attn_bwd")
 
 _lib = None
 
@@ -58,6 +59,12 @@ def load() -> ctypes.CDLL:
     lib.fsa_selected_attn_fwd.restype = ctypes.c_int
     lib.fsa_selected_attn_fwd.argtypes = [P, P, P, P, P, P, i32, i64, i64, i32, i32, i32, i32, i32,
                                           i32, i32, f32, i32, i32, P, sz, P, P, P]
+    lib.fsa_selected_attn_bwd_workspace_size.restype = sz
+    lib.fsa_selected_attn_bwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32,
+                                                         i32]
+    lib.fsa_selected_attn_bwd.restype = ctypes.c_int
+    lib.fsa_selected_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, i32, i64, i64, i32, i32, i32,
+                                          i32, i32, i32, i32, f32, i32, P, sz, P, P, P, P]
     lib.fsa_sliding_window_fwd_workspace_size.restype = sz
     lib.fsa_sliding_window_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32]
     lib.fsa_sliding_window_fwd.restype = ctypes.c_int
@@ -112,6 +119,15 @@ def fsa_selected_attn_fwd_workspace_size(batch: int, total_q: int, max_seqlen_q:
     return int(load().fsa_selected_attn_fwd_workspace_size(batch, total_q, max_seqlen_q,
                                                             num_heads_q, num_heads_kv, head_dim,
                                                             block_size, topk, num_splits))
+
+
+def fsa_selected_attn_bwd_workspace_size(batch: int, total_q: int, max_seqlen_q: int,
+                                         max_seqlen_k: int, num_heads_q: int, num_heads_kv: int,
+                                         head_dim: int, block_size: int, topk: int) -> int:
+    return int(load().fsa_selected_attn_bwd_workspace_size(batch, total_q, max_seqlen_q,
+                                                            max_seqlen_k, num_heads_q,
+                                                            num_heads_kv, head_dim, block_size,
+                                                            topk))
 
 
 def fsa_sliding_window_fwd_workspace_size(batch: int, total_q: int, max_seqlen_q: int,
@@ -178,6 +194,48 @@ def fsa_selected_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if st != FSA_SUCCESS:
         raise FsaError(st, "fsa_selected_attn_fwd")
     return out, lse
+
+
+def fsa_selected_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                          lse: torch.Tensor, dout: torch.Tensor, blk_idx: torch.Tensor,
+                          cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                          max_seqlen_q: int, max_seqlen_k: int, block_size: int = 64,
+                          softmax_scale: Optional[float] = None, causal: bool = True,
+                          workspace: Optional[torch.Tensor] = None
+                          ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward of ``fsa_selected_attn_fwd``: ``(dq, dk, dv)`` for the gradient
+    ``dout`` of its output ``out`` (whose LSE ``[Hq, total_q]`` it also takes)."""
+    lib = load()
+    for nm, t, nd in (("q", q, 3), ("k", k, 3), ("v", v, 3), ("out", out, 3), ("dout", dout, 3)):
+        _check_dev(nm, t, torch.bfloat16, nd)
+    _check_dev("lse", lse, torch.float32, 2)
+    _check_dev("blk_idx", blk_idx, torch.int32, 3)
+    _check_dev("cu_seqlens_q", cu_seqlens_q, torch.int32, 1)
+    _check_dev("cu_seqlens_k", cu_seqlens_k, torch.int32, 1)
+    total_q, hq, d = q.shape
+    total_k, hkv, _ = k.shape
+    topk = blk_idx.shape[2]
+    batch = cu_seqlens_q.numel() - 1
+    if tuple(out.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) \
+            or tuple(v.shape) != tuple(k.shape) or tuple(lse.shape) != (hq, total_q):
+        raise ValueError("out/dout must match q, v must match k, lse must be [Hq, total_q]")
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    need = lib.fsa_selected_attn_bwd_workspace_size(batch, total_q, max_seqlen_q, max_seqlen_k,
+                                                    hq, hkv, d, block_size, topk)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = lib.fsa_selected_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                                   _ptr(blk_idx), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch,
+                                   total_q, total_k, max_seqlen_q, max_seqlen_k, hq, hkv, d,
+                                   block_size, topk, scale, int(causal), _ptr(workspace),
+                                   ws_bytes, _ptr(dq), _ptr(dk), _ptr(dv), _stream(q.device))
+    if st != FSA_SUCCESS:
+        raise FsaError(st, "fsa_selected_attn_bwd")
+    return dq, dk, dv
 
 
 def fsa_sliding_window_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

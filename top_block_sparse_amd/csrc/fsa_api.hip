@@ -17,6 +17,7 @@ namespace {
 constexpr int kMaxTopkPrefill = 64;
 constexpr int kMaxGroupPrefill = 224;   // one tile covers at most 14 m-tiles of 16 rows
 constexpr int kMaxSplitsPrefill = 16;
+constexpr int kMaxGroupBackward = 32;   // 32 query rows per dK/dV step hold one token at least
 constexpr int kMaxTopkDecode = 8192;
 constexpr int kMaxGroupDecode = 16;
 constexpr int kMaxSplitsDecode = 64;
@@ -391,6 +392,119 @@ fsa_status_t fsa_topk_decode_fp8(const void* q, const void* k_cache, const void*
                        cache_seqlens, batch, num_heads_q, num_heads_kv, head_dim, page_size,
                        max_pages_per_seq, num_pages, topk, softmax_scale, num_splits, workspace,
                        workspace_bytes, out, lse, stream);
+}
+
+struct BwdLayout {
+    size_t dvec, counts, cursor, toks, total;
+    int nb_max;
+};
+
+static BwdLayout bwd_layout(int32_t batch, int64_t total_q, int32_t max_seqlen_k, int32_t Hq,
+                            int32_t Hkv, int32_t topk) {
+    BwdLayout l{};
+    l.nb_max = (max_seqlen_k + fsa::kBlockKeys - 1) / fsa::kBlockKeys;
+    if (l.nb_max < 1) l.nb_max = 1;
+    size_t off = 0;
+    l.dvec = off;
+    off = align_up(off + (size_t)Hq * total_q * 4);
+    l.counts = off;
+    off = align_up(off + (size_t)batch * Hkv * (l.nb_max + 1) * 4);
+    l.cursor = off;
+    off = align_up(off + (size_t)batch * Hkv * l.nb_max * 4);
+    l.toks = off;
+    off = align_up(off + (size_t)total_q * Hkv * topk * 4);
+    l.total = off;
+    return l;
+}
+
+static fsa_status_t check_bwd_shape(int32_t batch, int64_t total_q, int32_t max_seqlen_q,
+                                    int32_t max_seqlen_k, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t bs, int32_t topk) {
+    fsa_status_t st = check_prefill_shape(batch, max_seqlen_q, Hq, Hkv, D, bs, topk, 1);
+    if (st != FSA_SUCCESS) return st;
+    if (total_q < 0 || max_seqlen_k < 0) return FSA_ERROR_INVALID_VALUE;
+    if (Hq / Hkv > kMaxGroupBackward) return FSA_ERROR_NOT_SUPPORTED;
+    return FSA_SUCCESS;
+}
+
+size_t fsa_selected_attn_bwd_workspace_size(int32_t batch, int64_t total_q, int32_t max_seqlen_q,
+                                            int32_t max_seqlen_k, int32_t num_heads_q,
+                                            int32_t num_heads_kv, int32_t head_dim,
+                                            int32_t block_size, int32_t topk) {
+    if (check_bwd_shape(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv,
+                        head_dim, block_size, topk) != FSA_SUCCESS)
+        return 0;
+    return bwd_layout(batch, total_q, max_seqlen_k, num_heads_q, num_heads_kv, topk).total;
+}
+
+fsa_status_t fsa_selected_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                                   const float* lse, const void* dout, const int32_t* blk_idx,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                   int32_t batch, int64_t total_q, int64_t total_k,
+                                   int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                   int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                   int32_t block_size, int32_t topk, float softmax_scale,
+                                   int32_t causal, void* workspace, size_t workspace_bytes,
+                                   void* dq, void* dk, void* dv, void* stream) {
+    fsa_status_t st = check_bwd_shape(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q,
+                                      num_heads_kv, head_dim, block_size, topk);
+    if (st != FSA_SUCCESS) return st;
+    if (total_k < 0) return FSA_ERROR_INVALID_VALUE;
+    if (total_q > INT32_MAX || total_k > INT32_MAX) return FSA_ERROR_NOT_SUPPORTED;
+    if (batch == 0 || (total_q == 0 && total_k == 0)) return FSA_SUCCESS;
+    if (!q || !k || !v || !out || !lse || !dout || !blk_idx || !cu_seqlens_q || !cu_seqlens_k ||
+        !dq || !dk || !dv)
+        return FSA_ERROR_INVALID_VALUE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return FSA_ERROR_INVALID_VALUE;
+    const BwdLayout lay = bwd_layout(batch, total_q, max_seqlen_k, num_heads_q, num_heads_kv, topk);
+    if (workspace == nullptr || workspace_bytes < lay.total ||
+        (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return FSA_ERROR_WORKSPACE;
+    const int G = num_heads_q / num_heads_kv;
+    int T = fsa::sel_attn_bwd_rows_per_tile() / G;
+    if (T > 64) T = 64;
+    if (T < 1) T = 1;
+    if (fsa::sel_attn_bwd_dq_lds_bytes(head_dim, T, topk) > 160 * 1024) return FSA_ERROR_NOT_SUPPORTED;
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    fsa::SelBwdParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.o = static_cast<const uint16_t*>(out);
+    p.dout = static_cast<const uint16_t*>(dout);
+    p.lse = lse;
+    p.blk_idx = blk_idx;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.dq = static_cast<uint16_t*>(dq);
+    p.dk = static_cast<uint16_t*>(dk);
+    p.dv = static_cast<uint16_t*>(dv);
+    p.dvec = reinterpret_cast<float*>(ws + lay.dvec);
+    p.counts = reinterpret_cast<int32_t*>(ws + lay.counts);
+    p.cursor = reinterpret_cast<int32_t*>(ws + lay.cursor);
+    p.toks = reinterpret_cast<int32_t*>(ws + lay.toks);
+    p.total_q = total_q;
+    p.total_k = total_k;
+    p.batch = batch;
+    p.Hq = num_heads_q;
+    p.Hkv = num_heads_kv;
+    p.G = G;
+    p.topk = topk;
+    p.causal = causal ? 1 : 0;
+    p.nb_max = lay.nb_max;
+    p.T = T;
+    p.mtiles = (T * G + 15) / 16;
+    p.tiles_per_seq = (max_seqlen_q + T - 1) / T;
+    if (p.tiles_per_seq < 1) p.tiles_per_seq = 1;
+    p.scale = resolve_scale(softmax_scale, head_dim);
+    p.scale_log2 = p.scale * fsa::kLog2e;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (fsa::launch_sel_attn_bwd(p, head_dim, s) != hipSuccess) return FSA_ERROR_LAUNCH;
+    return FSA_SUCCESS;
 }
 
 }  // extern "C"

@@ -52,6 +52,30 @@ struct DecodeParams {
     float scale_log2;
 };
 
+// Selected-attention backward (sel_attn_bwd.hip).
+struct SelBwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* o;
+    const uint16_t* dout;
+    const float* lse;        // [Hq][total_q], natural log (the forward's)
+    const int32_t* blk_idx;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    uint16_t* dq;            // [total_q][Hq][D]
+    uint16_t* dk;            // [total_k][Hkv][D]
+    uint16_t* dv;
+    float* dvec;             // workspace [Hq][total_q]: rowsum(dO * O)
+    int32_t* counts;         // workspace [batch*Hkv][nb_max + 1]: counts, then offsets
+    int32_t* cursor;         // workspace [batch*Hkv][nb_max]
+    int32_t* toks;           // workspace [total_q * Hkv * topk]: token lists per block
+    int64_t total_q, total_k;
+    int batch, Hq, Hkv, G, topk, causal, nb_max;
+    int T, mtiles, tiles_per_seq;   // dq tiling
+    float scale, scale_log2;
+};
+
 // Logsumexp merge of split partials (lse_merge.hip).
 struct MergeParams {
     const float* part_o;     // [nparts][nrows][D]
@@ -76,5 +100,8 @@ int decode_waves_per_workgroup(int G);
 size_t decode_lds_bytes(int D, int G, int ts, int topk);
 int decode_table_slots(int D, int G, int topk);
 hipError_t launch_lse_merge(const MergeParams& p, int D, hipStream_t stream);
+hipError_t launch_sel_attn_bwd(const SelBwdParams& p, int D, hipStream_t stream);
+int sel_attn_bwd_rows_per_tile();   // query rows (T*G) one dq workgroup covers
+size_t sel_attn_bwd_dq_lds_bytes(int D, int T, int topk);
 
 }  // namespace fsa
