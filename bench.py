@@ -69,7 +69,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=("full", "prefill", "decode", "decode_fp8", "window", "copy"),
+    ap.add_argument("--mode", choices=("full", "prefill", "decode", "decode_fp8", "window",
+                                       "backward", "copy"),
                     default="full",
                     help="profiling runs: launch only one kernel family (or a plain 1 GiB "
                          "device copy used to calibrate HBM byte counters) --steps times, "
@@ -105,7 +106,7 @@ def main():
         return
 
     # ---------------- inputs (generated on the host, then resident in HBM)
-    want_p = args.mode in ("full", "prefill", "window")
+    want_p = args.mode in ("full", "prefill", "window", "backward")
     want_d = args.mode in ("full", "decode", "decode_fp8")
     want_f8 = args.mode in ("full", "decode_fp8")
     pspec = inputs.PREFILL_WORKLOADS[PREFILL]
@@ -171,6 +172,25 @@ def main():
                                    pg["cu_seqlens_k"], pd["max_seqlen_q"], pd["max_seqlen_k"],
                                    WINDOW - 1, 0, out=w_out, lse=p_lse)
 
+    bwd_state = {}
+
+    def backward():
+        if not bwd_state:                          # the forward's out / lse, and dO, once
+            o_, l_ = fsa.fsa_selected_attn_fwd(pg["q"], pg["k"], pg["v"], pg["blk_idx"],
+                                               pg["cu_seqlens_q"], pg["cu_seqlens_k"],
+                                               pd["max_seqlen_q"], pd["max_seqlen_k"])
+            bwd_state.update(o=o_, l=l_, do=inputs.randn_bf16(tuple(pg["q"].shape), 9999).to(dev))
+            need = fsa.fsa_selected_attn_bwd_workspace_size(
+                len(pspec.seqlens), pg["q"].shape[0], pg["k"].shape[0], pd["max_seqlen_q"],
+                pd["max_seqlen_k"],
+                pspec.num_heads_q, pspec.num_heads_kv, pspec.head_dim, pspec.block_size,
+                pspec.topk)
+            bwd_state["ws"] = torch.empty(need, dtype=torch.uint8, device=dev)
+        fsa.fsa_selected_attn_bwd(pg["q"], pg["k"], pg["v"], bwd_state["o"], bwd_state["l"],
+                                  bwd_state["do"], pg["blk_idx"], pg["cu_seqlens_q"],
+                                  pg["cu_seqlens_k"], pd["max_seqlen_q"], pd["max_seqlen_k"],
+                                  workspace=bwd_state["ws"])
+
     def prefill():
         fsa.fsa_selected_attn_fwd(pg["q"], pg["k"], pg["v"], pg["blk_idx"], pg["cu_seqlens_q"],
                                   pg["cu_seqlens_k"], pd["max_seqlen_q"], pd["max_seqlen_k"],
@@ -185,9 +205,9 @@ def main():
         fsa.fsa_topk_decode_fp8(dq, k_, v_, kd8, vd8, dtok, dbt, dcs, out=d_out, lse=d_lse,
                                 workspace=d_ws)
 
-    if args.mode in ("prefill", "decode", "decode_fp8"):
+    if args.mode != "full":
         step = {"prefill": lambda i: prefill(), "decode": decode, "decode_fp8": decode_fp8,
-                "window": lambda i: window()}[args.mode]
+                "window": lambda i: window(), "backward": lambda i: backward()}[args.mode]
         for i in range(args.warmup + args.steps):
             step(i)
         torch.cuda.synchronize()
@@ -200,6 +220,7 @@ def main():
         decode(i)
         decode_fp8(i)
         window()
+        backward()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -246,8 +267,19 @@ def main():
         w_ev[i][1].record(stream)
     torch.cuda.synchronize()
 
+    log(f"timing {K} backward calls")
+    b_ev = [(ev(), ev()) for _ in range(K)]
+    for i in range(K):
+        b_ev[i][0].record(stream)
+        backward()
+        b_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+
     p_ms = np.array([a.elapsed_time(b) for a, b in p_ev])
     f_ms = np.array([a.elapsed_time(b) for a, b in f_ev])
+    b_ms = np.array([a.elapsed_time(b) for a, b in b_ev])
+    b_flops = 2.5 * flops                    # five products per selected block against two
+    b_tflops = b_flops / (b_ms.mean() * 1e-3) / 1e12
     w_ms = np.array([a.elapsed_time(b) for a, b in w_ev])
     w_tflops = w_flops / (w_ms.mean() * 1e-3) / 1e12
     f_gbs_evt = f8_bytes / (f_ms.mean() * 1e-3) / 1e9
@@ -289,6 +321,15 @@ def main():
                      "unit": "TFLOP/s", "frac": round(w_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "flops_per_call": w_flops},
     }
+    log(f"backward: mean {b_ms.mean():.3f} ms  {b_tflops:.1f} TFLOP/s (events)")
+    backward_obj = {
+        "value": round(b_tflops, 2), "unit": "TFLOP/s", "workload": PREFILL + "_backward",
+        "ms_per_call": round(float(b_ms.mean()), 4),
+        "roofline": {"bound": "mfma", "achieved": round(b_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(b_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "flops_per_call": b_flops,
+                     "scope": "whole call: D prep, block index, dK/dV and dQ kernels"},
+    }
     decode_fp8_obj = {
         "value": round(f_gbs_evt, 1), "unit": "GB/s", "workload": DECODE + "_fp8_e4m3",
         "us_per_call": round(float(f_ms.mean()) * 1e3, 2),
@@ -323,6 +364,7 @@ def main():
         "decode": decode_obj,
         "decode_fp8": decode_fp8_obj,
         "sliding_window": window_obj,
+        "backward": backward_obj,
     }
 
     if not args.no_cpu_baseline:

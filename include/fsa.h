@@ -130,10 +130,10 @@ fsa_status_t fsa_selected_attn_fwd(const void* q, const void* k, const void* v,
  * Rows with no visible key get dq = 0.  dk and dv are summed in an order that
  * can change between calls, so they may differ in the last bits run to run.
  */
-size_t fsa_selected_attn_bwd_workspace_size(int32_t batch, int64_t total_q, int32_t max_seqlen_q,
-                                            int32_t max_seqlen_k, int32_t num_heads_q,
-                                            int32_t num_heads_kv, int32_t head_dim,
-                                            int32_t block_size, int32_t topk);
+size_t fsa_selected_attn_bwd_workspace_size(int32_t batch, int64_t total_q, int64_t total_k,
+                                            int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                            int32_t num_heads_q, int32_t num_heads_kv,
+                                            int32_t head_dim, int32_t block_size, int32_t topk);
 
 fsa_status_t fsa_selected_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                                    const float* lse, const void* dout, const int32_t* blk_idx,

@@ -247,7 +247,8 @@ def test_bwd_argument_errors(lib, kw, code):
 
 def test_bwd_workspace(lib):
     f = lib.fsa_selected_attn_bwd_workspace_size
-    n = f(2, 16384, 8192, 8192, 32, 8, 128, 64, 16)
-    assert n >= 32 * 16384 * 4 + 16 * 129 * 4 + 16 * 128 * 4 + 16384 * 8 * 16 * 4
-    assert f(2, 16384, 8192, 8192, 32, 8, 96, 64, 16) == 0
+    n = f(2, 16384, 16384, 8192, 8192, 32, 8, 128, 64, 16)
+    assert n >= (32 * 16384 * 4 + 16 * 129 * 4 + 16 * 128 * 4 + 16384 * 8 * 16 * 4
+                 + 16384 * 8 * 2 * 128 * 4)
+    assert f(2, 16384, 16384, 8192, 8192, 32, 8, 96, 64, 16) == 0
     assert bwd(lib, batch=0, q=None) == 0

@@ -60,8 +60,8 @@ def load() -> ctypes.CDLL:
     lib.fsa_selected_attn_fwd.argtypes = [P, P, P, P, P, P, i32, i64, i64, i32, i32, i32, i32, i32,
                                           i32, i32, f32, i32, i32, P, sz, P, P, P]
     lib.fsa_selected_attn_bwd_workspace_size.restype = sz
-    lib.fsa_selected_attn_bwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32,
-                                                         i32]
+    lib.fsa_selected_attn_bwd_workspace_size.argtypes = [i32, i64, i64, i32, i32, i32, i32, i32,
+                                                         i32, i32]
     lib.fsa_selected_attn_bwd.restype = ctypes.c_int
     lib.fsa_selected_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, i32, i64, i64, i32, i32, i32,
                                           i32, i32, i32, i32, f32, i32, P, sz, P, P, P, P]
@@ -121,10 +121,11 @@ def fsa_selected_attn_fwd_workspace_size(batch: int, total_q: int, max_seqlen_q:
                                                             block_size, topk, num_splits))
 
 
-def fsa_selected_attn_bwd_workspace_size(batch: int, total_q: int, max_seqlen_q: int,
-                                         max_seqlen_k: int, num_heads_q: int, num_heads_kv: int,
-                                         head_dim: int, block_size: int, topk: int) -> int:
-    return int(load().fsa_selected_attn_bwd_workspace_size(batch, total_q, max_seqlen_q,
+def fsa_selected_attn_bwd_workspace_size(batch: int, total_q: int, total_k: int,
+                                         max_seqlen_q: int, max_seqlen_k: int, num_heads_q: int,
+                                         num_heads_kv: int, head_dim: int, block_size: int,
+                                         topk: int) -> int:
+    return int(load().fsa_selected_attn_bwd_workspace_size(batch, total_q, total_k, max_seqlen_q,
                                                             max_seqlen_k, num_heads_q,
                                                             num_heads_kv, head_dim, block_size,
                                                             topk))
@@ -222,8 +223,8 @@ def fsa_selected_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    need = lib.fsa_selected_attn_bwd_workspace_size(batch, total_q, max_seqlen_q, max_seqlen_k,
-                                                    hq, hkv, d, block_size, topk)
+    need = lib.fsa_selected_attn_bwd_workspace_size(batch, total_q, total_k, max_seqlen_q,
+                                                    max_seqlen_k, hq, hkv, d, block_size, topk)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()

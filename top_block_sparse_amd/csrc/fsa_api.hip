@@ -395,12 +395,12 @@ fsa_status_t fsa_topk_decode_fp8(const void* q, const void* k_cache, const void*
 }
 
 struct BwdLayout {
-    size_t dvec, counts, cursor, toks, total;
+    size_t dvec, counts, cursor, toks, kv_acc, total;
     int nb_max;
 };
 
-static BwdLayout bwd_layout(int32_t batch, int64_t total_q, int32_t max_seqlen_k, int32_t Hq,
-                            int32_t Hkv, int32_t topk) {
+static BwdLayout bwd_layout(int32_t batch, int64_t total_q, int64_t total_k, int32_t max_seqlen_k,
+                            int32_t Hq, int32_t Hkv, int32_t D, int32_t topk) {
     BwdLayout l{};
     l.nb_max = (max_seqlen_k + fsa::kBlockKeys - 1) / fsa::kBlockKeys;
     if (l.nb_max < 1) l.nb_max = 1;
@@ -413,6 +413,8 @@ static BwdLayout bwd_layout(int32_t batch, int64_t total_q, int32_t max_seqlen_k
     off = align_up(off + (size_t)batch * Hkv * l.nb_max * 4);
     l.toks = off;
     off = align_up(off + (size_t)total_q * Hkv * topk * 4);
+    l.kv_acc = off;
+    off = align_up(off + (size_t)total_k * Hkv * 2 * D * 4);
     l.total = off;
     return l;
 }
@@ -427,14 +429,16 @@ static fsa_status_t check_bwd_shape(int32_t batch, int64_t total_q, int32_t max_
     return FSA_SUCCESS;
 }
 
-size_t fsa_selected_attn_bwd_workspace_size(int32_t batch, int64_t total_q, int32_t max_seqlen_q,
-                                            int32_t max_seqlen_k, int32_t num_heads_q,
-                                            int32_t num_heads_kv, int32_t head_dim,
-                                            int32_t block_size, int32_t topk) {
-    if (check_bwd_shape(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv,
+size_t fsa_selected_attn_bwd_workspace_size(int32_t batch, int64_t total_q, int64_t total_k,
+                                            int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                            int32_t num_heads_q, int32_t num_heads_kv,
+                                            int32_t head_dim, int32_t block_size, int32_t topk) {
+    if (total_k < 0 ||
+        check_bwd_shape(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv,
                         head_dim, block_size, topk) != FSA_SUCCESS)
         return 0;
-    return bwd_layout(batch, total_q, max_seqlen_k, num_heads_q, num_heads_kv, topk).total;
+    return bwd_layout(batch, total_q, total_k, max_seqlen_k, num_heads_q, num_heads_kv, head_dim,
+                      topk).total;
 }
 
 fsa_status_t fsa_selected_attn_bwd(const void* q, const void* k, const void* v, const void* out,
@@ -458,7 +462,8 @@ fsa_status_t fsa_selected_attn_bwd(const void* q, const void* k, const void* v, 
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
         !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
         return FSA_ERROR_INVALID_VALUE;
-    const BwdLayout lay = bwd_layout(batch, total_q, max_seqlen_k, num_heads_q, num_heads_kv, topk);
+    const BwdLayout lay = bwd_layout(batch, total_q, total_k, max_seqlen_k, num_heads_q,
+                                     num_heads_kv, head_dim, topk);
     if (workspace == nullptr || workspace_bytes < lay.total ||
         (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
         return FSA_ERROR_WORKSPACE;
@@ -466,7 +471,8 @@ fsa_status_t fsa_selected_attn_bwd(const void* q, const void* k, const void* v, 
     int T = fsa::sel_attn_bwd_rows_per_tile() / G;
     if (T > 64) T = 64;
     if (T < 1) T = 1;
-    if (fsa::sel_attn_bwd_dq_lds_bytes(head_dim, T, topk) > 160 * 1024) return FSA_ERROR_NOT_SUPPORTED;
+    const int dq_ring = fsa::sel_attn_bwd_dq_ring(head_dim, T, topk);
+    if (dq_ring < 2) return FSA_ERROR_NOT_SUPPORTED;
 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     fsa::SelBwdParams p{};
@@ -486,6 +492,7 @@ fsa_status_t fsa_selected_attn_bwd(const void* q, const void* k, const void* v, 
     p.counts = reinterpret_cast<int32_t*>(ws + lay.counts);
     p.cursor = reinterpret_cast<int32_t*>(ws + lay.cursor);
     p.toks = reinterpret_cast<int32_t*>(ws + lay.toks);
+    p.kv_acc = reinterpret_cast<float*>(ws + lay.kv_acc);
     p.total_q = total_q;
     p.total_k = total_k;
     p.batch = batch;
@@ -495,7 +502,21 @@ fsa_status_t fsa_selected_attn_bwd(const void* q, const void* k, const void* v, 
     p.topk = topk;
     p.causal = causal ? 1 : 0;
     p.nb_max = lay.nb_max;
+    {
+        // a block is split only when it has more steps of 32 rows than one
+        // part takes (>= 64 steps, at most 32 parts); the parts meet in fp32
+        // atomics
+        const long long tpc = 32 / G;          // whole tokens per step of 32 rows
+        const long long max_steps = ((long long)max_seqlen_q + tpc - 1) / tpc;
+        long long np = (max_steps + 63) / 64;
+        if (np > 32) np = 32;
+        if (np < 1) np = 1;
+        p.nparts = (int)np;
+        p.part_steps = (int)((max_steps + np - 1) / np);
+        if (p.part_steps < 1) p.part_steps = 1;
+    }
     p.T = T;
+    p.ring = dq_ring;
     p.mtiles = (T * G + 15) / 16;
     p.tiles_per_seq = (max_seqlen_q + T - 1) / T;
     if (p.tiles_per_seq < 1) p.tiles_per_seq = 1;

@@ -70,9 +70,12 @@ struct SelBwdParams {
     int32_t* counts;         // workspace [batch*Hkv][nb_max + 1]: counts, then offsets
     int32_t* cursor;         // workspace [batch*Hkv][nb_max]
     int32_t* toks;           // workspace [total_q * Hkv * topk]: token lists per block
+    float* kv_acc;           // workspace [total_k][Hkv][2][D] fp32: dK, dV of split blocks
     int64_t total_q, total_k;
     int batch, Hq, Hkv, G, topk, causal, nb_max;
+    int nparts, part_steps;  // a block's 32-row steps go to <= nparts workgroups of part_steps
     int T, mtiles, tiles_per_seq;   // dq tiling
+    int ring;                       // dq LDS ring slots of K/V blocks (2..4)
     float scale, scale_log2;
 };
 
@@ -102,6 +105,7 @@ int decode_table_slots(int D, int G, int topk);
 hipError_t launch_lse_merge(const MergeParams& p, int D, hipStream_t stream);
 hipError_t launch_sel_attn_bwd(const SelBwdParams& p, int D, hipStream_t stream);
 int sel_attn_bwd_rows_per_tile();   // query rows (T*G) one dq workgroup covers
-size_t sel_attn_bwd_dq_lds_bytes(int D, int T, int topk);
+size_t sel_attn_bwd_dq_lds_bytes(int D, int T, int topk, int ring);
+int sel_attn_bwd_dq_ring(int D, int T, int topk);   // ring slots that fit in LDS (0: none)
 
 }  // namespace fsa

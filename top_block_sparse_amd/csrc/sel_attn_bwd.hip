@@ -13,9 +13,12 @@
 //   2. bwd_count / bwd_scan / bwd_fill: for every (sequence, kv head, key
 //      block), the list of query tokens that selected it (each token's list
 //      read as a set) -- an inverted index, so that
-//   3. bwd_dkv: one workgroup per (sequence, kv head, block) accumulates dK and
+//   3. bwd_dkv: a workgroup per (sequence, kv head, block) accumulates dK and
 //      dV of its 64 keys in registers over the block's tokens, 32 query rows at
-//      a time (no atomics on dK / dV; blocks nobody selected get zeros).  Four
+//      a time, and writes them (blocks nobody selected get zeros).  A block
+//      many tokens selected (block 0, the local blocks) is split over several
+//      workgroups whose fp32 partials are added in a workspace and converted
+//      by bwd_dkv_finish.  Four
 //      waves own 16 keys each.  S = Q K^T and dP = dO V^T put the query rows
 //      on the MFMA M dimension, so their accumulators are directly the B
 //      operands of dV^T = dO^T P and dK^T = Q^T dS (after a fixed reordering of
@@ -35,8 +38,9 @@ namespace {
 
 constexpr int kBwdRows = 32;            // query rows per dK/dV step
 constexpr int kBwdKvThreads = 256;      // 4 waves x 16 keys
-constexpr int kBwdDqWaves = 8;          // m-tiles per dq workgroup
-constexpr int kBwdDqThreads = kBwdDqWaves * 64;
+constexpr int kBwdDqWaves = 8;          // m-tiles (compute waves) per dq workgroup
+constexpr int kBwdDqProducers = 2;      // waves that only move K/V blocks into LDS
+constexpr int kBwdDqThreads = (kBwdDqWaves + kBwdDqProducers) * 64;
 constexpr int kBwdWin = 256;            // blocks per union-building window (dq)
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
@@ -54,6 +58,21 @@ __device__ __forceinline__ float row16_sum(float x) {
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
     return x;
+}
+
+// workgroup barrier that orders LDS accesses only: global loads in flight
+// (prefetches) are not waited for
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at "no wait")
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // a wave-uniform 64-bit value (readfirstlane works on 32 bits and returns a
@@ -128,7 +147,10 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const SelBwdParams p) {
         const int h = (int)(row - t * p.Hq);
         p.dvec[(int64_t)h * p.total_q + t] = acc;
     }
-    // counters
+    // split-block accumulators and counters
+    const int64_t na = p.total_k * p.Hkv * 2 * D / 4;
+    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < na; x += (int64_t)gridDim.x * 256)
+        reinterpret_cast<f32x4_t*>(p.kv_acc)[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int64_t nc = (int64_t)p.batch * p.Hkv * (p.nb_max + 1);
     const int64_t nu = (int64_t)p.batch * p.Hkv * p.nb_max;
     for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < nc; x += (int64_t)gridDim.x * 256) {
@@ -221,13 +243,23 @@ struct KvLds {
 template <int D>
 __global__ void __launch_bounds__(kBwdKvThreads) bwd_dkv_kernel(const SelBwdParams p) {
     constexpr int KS = D / 32, DT = D / 16;
+    constexpr int CPR = D / 8;                                   // 16-byte chunks per row
+    constexpr int NI = kBwdRows * CPR / kBwdKvThreads;           // chunks per thread per step
+    static_assert(NI * kBwdKvThreads == kBwdRows * CPR && kBwdKvThreads % CPR == 0, "row staging");
     using L = KvLds<D>;
     __shared__ __align__(16) uint8_t smem[L::bytes];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
 
-    const int blk = blockIdx.x % p.nb_max;
-    const int unit = blockIdx.x / p.nb_max;          // b * Hkv + g
+    // workgroup order: block-major (the early blocks, which causal lists pick
+    // most, start first), then part, then (sequence, kv head) innermost, so
+    // that the busy workgroups of a block spread over the XCDs while each
+    // (sequence, kv head) keeps to one XCD's L2 when their count is a
+    // multiple of 8
+    const int nunits = p.batch * p.Hkv;
+    const int unit = blockIdx.x % nunits;                // b * Hkv + g
+    const int part = (blockIdx.x / nunits) % p.nparts;
+    const int blk = blockIdx.x / nunits / p.nparts;
     const int g = unit % p.Hkv, b = unit / p.Hkv;
     const SeqBounds sb = bounds(p, b);
     const int nblk = (sb.Sk + kBlockKeys - 1) / kBlockKeys;
@@ -235,9 +267,19 @@ __global__ void __launch_bounds__(kBwdKvThreads) bwd_dkv_kernel(const SelBwdPara
     const int off = sb.Sk - sb.Sq;
     const int G = p.G;
     const int tpc = kBwdRows / G;                     // tokens per step (G <= 32)
+    const int rows_used = tpc * G;
     const int32_t* cnt = p.counts + (int64_t)unit * (p.nb_max + 1);
-    const int tb = cnt[blk], ntk = cnt[blk + 1] - tb;
+    const int tb = cnt[blk], ntk_all = cnt[blk + 1] - tb;
+    // a block selected by many tokens is split over workgroups (parts) whose
+    // fp32 partial sums meet in kv_acc; a one-part block writes bf16 directly
+    const int nsteps = (ntk_all + tpc - 1) / tpc;
+    const bool split = nsteps > p.part_steps;
+    const int s_lo = part * p.part_steps;
+    if (part > 0 && s_lo >= nsteps) return;
+    const int s_hi = nsteps < s_lo + p.part_steps ? nsteps : s_lo + p.part_steps;
     const int32_t* tl = p.toks + toks_base(p, sb, g) + tb;
+    const int c_lo = s_lo * tpc;
+    const int ntk = s_hi * tpc < ntk_all ? s_hi * tpc : ntk_all;   // tokens [c_lo, ntk)
 
     // this wave's 16 keys: K and V as B operands (lane: key key0 + lr, 8 dims)
     const int key0 = wave * 16;
@@ -260,41 +302,81 @@ __global__ void __launch_bounds__(kBwdKvThreads) bwd_dkv_kernel(const SelBwdPara
     }
     const float c2 = p.scale_log2;
 
-    for (int c0 = 0; c0 < ntk; c0 += tpc) {
-        // stage 32 rows (tokens c0.., G heads each) of Q and dO, both layouts
-        for (int x = tid; x < kBwdRows * (D / 8); x += kBwdKvThreads) {
-            const int r = x / (D / 8), c = x - r * (D / 8);
-            const int ti = c0 + r / G;
-            const bool ok = r < tpc * G && ti < ntk;
-            u32x4_t qv = {0u, 0u, 0u, 0u}, ov = {0u, 0u, 0u, 0u};
-            if (ok) {
-                const int64_t t = sb.q0 + tl[ti];
-                const int64_t rowo = (t * p.Hq + g * G + (r % G)) * (int64_t)D + c * 8;
-                qv = *reinterpret_cast<const u32x4_t*>(p.q + rowo);
-                ov = *reinterpret_cast<const u32x4_t*>(p.dout + rowo);
-            }
-            *reinterpret_cast<u32x4_t*>(smem + L::qrow + r * L::kRowStride + c * 16) = qv;
-            *reinterpret_cast<u32x4_t*>(smem + L::orow + r * L::kRowStride + c * 16) = ov;
-            const int fl = 16 * ((r % 16) / 4) + 4 * (r % 4) + 2 * (c % 2);
-            const int fo = ((r / 16) * DT + c / 2) * 512 + fl * 8;
-            *reinterpret_cast<u32x4_t*>(smem + L::qtr + fo) = qv;
-            *reinterpret_cast<u32x4_t*>(smem + L::otr + fo) = ov;
+    // Rows of a step are gathered one step ahead into registers (and their
+    // token ids two steps ahead), so the gathers overlap the MFMA work.  The
+    // loads are unconditional (rows past the end read a real row and are
+    // zeroed when staged), so waiting for one step never waits for the next.
+    // This thread stages chunk column cc of rows (tid + 256 k) / CPR; threads
+    // below kBwdRows also stage the row data of row tid.
+    const int cc = tid % CPR;
+    const int ri_row = tid % kBwdRows;
+    int tk[NI], tki = 0;            // token ids of the step fetched next
+    int tok_ok = 0, row_ok = 0;     // bit k: chunk k is a real row, bit NI: row data
+    u32x4_t qv[NI], ov[NI];
+    float lse_r = 0.f, dv_r = 0.f;
+    int cpos = 0;
+    auto fetch_tok = [&](int c0) {
+        int m = 0;
+#pragma unroll
+        for (int k = 0; k < NI; ++k) {
+            const int r = (tid + k * kBwdKvThreads) / CPR, ti = c0 + r / G;
+            const bool ok = r < rows_used && ti < ntk;
+            tk[k] = tl[ok ? ti : ntk - 1];
+            m |= (int)ok << k;
+        }
+        const int ti = c0 + ri_row / G;
+        const bool ok = ri_row < rows_used && ti < ntk;
+        tki = tl[ok ? ti : ntk - 1];
+        tok_ok = m | ((int)ok << NI);
+    };
+    auto fetch_rows = [&]() {
+#pragma unroll
+        for (int k = 0; k < NI; ++k) {
+            const int r = (tid + k * kBwdKvThreads) / CPR;
+            const int64_t rowo = ((sb.q0 + tk[k]) * p.Hq + g * G + (r % G)) * (int64_t)D + cc * 8;
+            qv[k] = *reinterpret_cast<const u32x4_t*>(p.q + rowo);
+            ov[k] = *reinterpret_cast<const u32x4_t*>(p.dout + rowo);
+        }
+        const int64_t t = sb.q0 + tki;
+        const int64_t h = g * G + (ri_row % G);
+        lse_r = p.lse[h * p.total_q + t];
+        dv_r = p.dvec[h * p.total_q + t];
+        cpos = p.causal ? tki + off : 0x7fffffff;
+        row_ok = tok_ok;
+    };
+    auto stage = [&]() {                                   // registers -> row and tr layouts
+#pragma unroll
+        for (int k = 0; k < NI; ++k) {
+            const int r = (tid + k * kBwdKvThreads) / CPR;
+            const bool ok = (row_ok >> k) & 1;
+            const u32x4_t z = {0u, 0u, 0u, 0u};
+            const u32x4_t a = ok ? qv[k] : z, c = ok ? ov[k] : z;
+            *reinterpret_cast<u32x4_t*>(smem + L::qrow + r * L::kRowStride + cc * 16) = a;
+            *reinterpret_cast<u32x4_t*>(smem + L::orow + r * L::kRowStride + cc * 16) = c;
+            const int fl = 16 * ((r % 16) / 4) + 4 * (r % 4) + 2 * (cc % 2);
+            const int fo = ((r / 16) * DT + cc / 2) * 512 + fl * 8;
+            *reinterpret_cast<u32x4_t*>(smem + L::qtr + fo) = a;
+            *reinterpret_cast<u32x4_t*>(smem + L::otr + fo) = c;
         }
         if (tid < kBwdRows) {
-            const int r = tid, ti = c0 + r / G;
-            f32x4_t info = {INFINITY, 0.f, 0.f, 0.f};        // lse2, D, cpos, valid
-            if (r < tpc * G && ti < ntk) {
-                const int i = tl[ti];
-                const int64_t t = sb.q0 + i;
-                const int h = g * G + (r % G);
-                info[0] = p.lse[(int64_t)h * p.total_q + t] * kLog2e;
-                info[1] = p.dvec[(int64_t)h * p.total_q + t];
-                info[2] = __int_as_float(p.causal ? i + off : 0x7fffffff);
-                info[3] = 1.f;
-            }
-            *reinterpret_cast<f32x4_t*>(smem + L::rowinfo + r * 16) = info;
+            const bool ok = (row_ok >> NI) & 1;
+            const f32x4_t info = ok ? f32x4_t{lse_r * kLog2e, dv_r, __int_as_float(cpos), 1.f}
+                                    : f32x4_t{INFINITY, 0.f, 0.f, 0.f};   // lse2, D, cpos, valid
+            *reinterpret_cast<f32x4_t*>(smem + L::rowinfo + tid * 16) = info;
         }
-        __syncthreads();
+    };
+
+    if (c_lo < ntk) {                 // (ntk >= 1 below: clamped ids stay in the list)
+        fetch_tok(c_lo);
+        fetch_rows();
+        fetch_tok(c_lo + tpc);
+    }
+    for (int c0 = c_lo; c0 < ntk; c0 += tpc) {
+        stage();
+        lds_barrier();
+        fetch_rows();                 // the next step (staged as zeros past the end)
+        fetch_tok(c0 + 2 * tpc);
+        __builtin_amdgcn_sched_barrier(0);   // keep the gathers ahead of the MFMA work
 
         // S = Q K^T and dP = dO V^T for rows 0-15 / 16-31 and this wave's keys
         f32x4_t st[2], dp[2];
@@ -317,11 +399,11 @@ __global__ void __launch_bounds__(kBwdKvThreads) bwd_dkv_kernel(const SelBwdPara
         for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const f32x4_t info = *reinterpret_cast<const f32x4_t*>(smem + L::rowinfo + (16 * rt + 4 * lg + i) * 16);
-                const bool vis = key_ok && info[3] != 0.f && kabs <= __float_as_int(info[2]);
-                const float pr = vis ? fast_exp2(fmaf(st[rt][i], c2, -info[0])) : 0.f;
+                const f32x4_t ri = *reinterpret_cast<const f32x4_t*>(smem + L::rowinfo + (16 * rt + 4 * lg + i) * 16);
+                const bool vis = key_ok && ri[3] != 0.f && kabs <= __float_as_int(ri[2]);
+                const float pr = vis ? fast_exp2(fmaf(st[rt][i], c2, -ri[0])) : 0.f;
                 pv[rt][i] = pr;
-                dsv[rt][i] = pr * (dp[rt][i] - info[1]);
+                dsv[rt][i] = pr * (dp[rt][i] - ri[1]);
             }
         }
         const u32x4_t pB = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
@@ -338,52 +420,107 @@ __global__ void __launch_bounds__(kBwdKvThreads) bwd_dkv_kernel(const SelBwdPara
             adv[dt] = mfma_16x16x32(u32x4_t{olo[0], olo[1], ohi[0], ohi[1]}, pB, adv[dt]);
             adk[dt] = mfma_16x16x32(u32x4_t{qlo[0], qlo[1], qhi[0], qhi[1]}, dB, adk[dt]);
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // lane: key kabs, dims 16dt + 4lg .. +4
-    if (key_ok) {
-        const int64_t row = ((sb.k0 + kabs) * p.Hkv + g) * (int64_t)D + lg * 4;
+    if (!split) {
+        if (key_ok) {
+            const int64_t row = ((sb.k0 + kabs) * p.Hkv + g) * (int64_t)D + lg * 4;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const f32x4_t a = adk[dt] * p.scale;
-            const f32x4_t c = adv[dt];
-            *reinterpret_cast<u32x2_t*>(p.dk + row + dt * 16) =
-                u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-            *reinterpret_cast<u32x2_t*>(p.dv + row + dt * 16) =
-                u32x2_t{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])};
+            for (int dt = 0; dt < DT; ++dt) {
+                const f32x4_t a = adk[dt] * p.scale;
+                const f32x4_t c = adv[dt];
+                *reinterpret_cast<u32x2_t*>(p.dk + row + dt * 16) =
+                    u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+                *reinterpret_cast<u32x2_t*>(p.dv + row + dt * 16) =
+                    u32x2_t{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])};
+            }
+        }
+        return;
+    }
+    // split block: the partial dK (scaled), then dV, goes through LDS as
+    // [key][dim] fp32 so that each atomic wave instruction covers 64
+    // consecutive floats of one key row
+    float* sacc = reinterpret_cast<float*>(smem);
+    constexpr int AS = D + 4;                      // padded fp32 row
+    static_assert(kBlockKeys * AS * 4 <= L::bytes, "partials fit the staging area");
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        if (half) lds_barrier();
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            *reinterpret_cast<f32x4_t*>(sacc + (key0 + lr) * AS + dt * 16 + lg * 4) = half ? adv[dt] : adk[dt] * p.scale;
+        lds_barrier();
+        for (int x = tid; x < kBlockKeys * D; x += kBwdKvThreads) {
+            const int key = x / D, d = x - key * D;
+            const int ka = blk * kBlockKeys + key;
+            if (ka < sb.Sk)
+                atomicAdd(p.kv_acc + ((sb.k0 + ka) * p.Hkv + g) * 2 * D + half * D + d, sacc[key * AS + d]);
         }
     }
 }
 
+// dK, dV of the split blocks: fp32 sums -> bf16 (one workgroup per block)
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dkv_finish_kernel(const SelBwdParams p) {
+    const int blk = blockIdx.x % p.nb_max;
+    const int unit = blockIdx.x / p.nb_max;
+    const int g = unit % p.Hkv, b = unit / p.Hkv;
+    const SeqBounds sb = bounds(p, b);
+    const int nblk = (sb.Sk + kBlockKeys - 1) / kBlockKeys;
+    if (blk >= nblk) return;
+    const int tpc = kBwdRows / p.G;
+    const int32_t* cnt = p.counts + (int64_t)unit * (p.nb_max + 1);
+    const int nsteps = (cnt[blk + 1] - cnt[blk] + tpc - 1) / tpc;
+    if (nsteps <= p.part_steps) return;               // written directly
+    for (int x = threadIdx.x; x < kBlockKeys * D / 4; x += 256) {
+        const int key = x / (D / 4), c = (x - key * (D / 4)) * 4;
+        const int kabs = blk * kBlockKeys + key;
+        if (kabs >= sb.Sk) continue;
+        const int64_t krow = (sb.k0 + kabs) * p.Hkv + g;
+        const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p.kv_acc + krow * 2 * D + c);
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p.kv_acc + krow * 2 * D + D + c);
+        *reinterpret_cast<u32x2_t*>(p.dk + krow * D + c) = u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+        *reinterpret_cast<u32x2_t*>(p.dv + krow * D + c) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+}
+
 // ---- 4. dQ: tiles of T tokens of one kv head, one m-tile of 16 rows per wave
+// A block's K and V sit in a ring slot in the fragment-permuted row layout:
+// 16-byte chunk c of key row r at ((r/16)*DT + c/2)*512 + (4(r%16) + 2(c%2))*8,
+// so that a plain 16-byte read gives the A operand of S^T = K Q^T (and of
+// dP^T = V dO^T), and a transposing 8-byte read gives the A operand of
+// dQ^T = K^T dS^T; each 1 KiB of the slot is one direct-to-LDS load.
 template <int D>
 struct DqLds {
     static constexpr int KS = D / 32, DT = D / 16;
-    static constexpr int kKA = 0;                         // K, fragment (kt, s): 1 KiB
-    static constexpr int kVA = 4 * KS * 1024;             // V, same layout
-    static constexpr int kKT = 2 * kVA;                   // K, transposing-read fragments
-    static constexpr int kSlot = kKT + 4 * DT * 512;
-    static constexpr int masks = kSlot;                            // u64 [kBwdWin]
-    static constexpr int umask = masks + kBwdWin * 8;              // u64 [kBwdWin]
-    static constexpr int ulist = umask + kBwdWin * 8;              // i32 [kBwdWin]
-    static constexpr int count = ulist + kBwdWin * 4;              // i32
-    static constexpr int ent = count + 16;                         // i32 [T * topk]
-    __host__ __device__ static size_t bytes(int T, int topk) { return (size_t)ent + (size_t)T * topk * 4; }
+    static constexpr int kPart = kBlockKeys * D * 2;          // K or V of one block
+    static constexpr int kSlot = 2 * kPart;                   // K then V
+    __host__ __device__ static int masks(int ring) { return ring * kSlot; }           // u64 [kBwdWin]
+    __host__ __device__ static int umask(int ring) { return masks(ring) + kBwdWin * 8; }  // u64 [kBwdWin]
+    __host__ __device__ static int ulist(int ring) { return umask(ring) + kBwdWin * 8; }  // i32 [kBwdWin]
+    __host__ __device__ static int count(int ring) { return ulist(ring) + kBwdWin * 4; }  // i32
+    __host__ __device__ static int ent(int ring) { return count(ring) + 16; }             // i32 [T * topk]
+    __host__ __device__ static size_t bytes(int T, int topk, int ring) {
+        return (size_t)ent(ring) + (size_t)T * topk * 4;
+    }
 };
 
 template <int D>
 __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParams p) {
     constexpr int KS = D / 32, DT = D / 16;
     using L = DqLds<D>;
-    constexpr int NIK = 4 * KS;                 // 1 KiB DMA pieces per part
-    constexpr int NI = 3 * NIK;                 // per block
+    constexpr int NIK = L::kPart / 1024;            // 1 KiB DMA pieces per part
+    constexpr int PPW = 2 * NIK / kBwdDqProducers;  // pieces per producer wave per block
+    static_assert(PPW * kBwdDqProducers == 2 * NIK && 2 * PPW < 64, "DMA split");
     extern __shared__ __align__(16) uint8_t smem[];
-    unsigned long long* s_masks = reinterpret_cast<unsigned long long*>(smem + L::masks);
-    unsigned long long* s_umask = reinterpret_cast<unsigned long long*>(smem + L::umask);
-    int* s_ulist = reinterpret_cast<int*>(smem + L::ulist);
-    int* s_count = reinterpret_cast<int*>(smem + L::count);
-    int* s_ent = reinterpret_cast<int*>(smem + L::ent);
+    const int ring = p.ring;
+    unsigned long long* s_masks = reinterpret_cast<unsigned long long*>(smem + L::masks(ring));
+    unsigned long long* s_umask = reinterpret_cast<unsigned long long*>(smem + L::umask(ring));
+    int* s_ulist = reinterpret_cast<int*>(smem + L::ulist(ring));
+    int* s_count = reinterpret_cast<int*>(smem + L::count(ring));
+    int* s_ent = reinterpret_cast<int*>(smem + L::ent(ring));
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -455,6 +592,35 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
     const uint8_t* kseq = reinterpret_cast<const uint8_t*>(p.k + (sb.k0 * p.Hkv + g) * (int64_t)D);
     const uint8_t* vseq = reinterpret_cast<const uint8_t*>(p.v + (sb.k0 * p.Hkv + g) * (int64_t)D);
     const float c2 = p.scale_log2;
+    // Producer wave pw moves pieces pw, pw + kBwdDqProducers, ... of each block.
+    // This lane's 16 bytes of a 1 KiB DMA piece: piece f covers the two
+    // 512-byte fragments 2f, 2f+1 -> (row group, chunk pair); lane -> (row, chunk)
+    const int pw = __builtin_amdgcn_readfirstlane(wave) - kBwdDqWaves;   // >= 0 on producer waves
+    int dma_off[PPW];
+#pragma unroll
+    for (int x = 0; x < PPW; ++x) {
+        const int f = (pw + x * kBwdDqProducers) % NIK;         // piece within its part
+        const int fr = 2 * f + (lane >> 5);                     // fragment
+        const int fl = 2 * (lane & 31);                         // 8-byte unit within it
+        const int r = 16 * (fr / DT) + fl / 4;                  // key row (fl = 4 (r%16) + 2 (c%2))
+        const int c = 2 * (fr % DT) + (fl & 2) / 2;             // 16-byte chunk
+        dma_off[x] = r * (int)row_bytes + c * 16;
+    }
+    auto issue = [&](int blk, int slot) {                       // DMA block blk -> ring slot
+        const int rows = sb.Sk - blk * kBlockKeys < kBlockKeys ? sb.Sk - blk * kBlockKeys : kBlockKeys;
+        const uint32_t nrec = (uint32_t)((rows - 1) * row_bytes + D * 2);
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(kseq + blk * kBlockKeys * row_bytes), 0, nrec, 0x00020000);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(vseq + blk * kBlockKeys * row_bytes), 0, nrec, 0x00020000);
+#pragma unroll
+        for (int x = 0; x < PPW; ++x) {
+            const int inst = pw + x * kBwdDqProducers;          // piece: K pieces, then V pieces
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(inst < NIK ? kr : vr,
+                                                     (lds_void_t*)(smem + slot * L::kSlot + inst * 1024),
+                                                     16, (uint32_t)dma_off[x], 0, 0, 0);
+        }
+    };
     __syncthreads();
 
     for (int win_lo = 0; win_lo < nb_range; win_lo += kBwdWin) {
@@ -484,39 +650,29 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
         __syncthreads();
         const int n_u = __builtin_amdgcn_readfirstlane(s_count[0]);
 
-        for (int u = 0; u < n_u; ++u) {
+        // Ring: blocks u+1 .. u+ring-2 stay in flight while block u is used.
+        // Producer and compute waves run separate loops with one barrier per
+        // block each, so no compute wave ever has a direct-to-LDS load of its
+        // own outstanding (nothing makes it wait for one) and the producers
+        // wait only for the block due next.
+        if (wave >= kBwdDqWaves) {
+            for (int u = 0; u < n_u && u < ring - 1; ++u)
+                issue(__builtin_amdgcn_readfirstlane(s_ulist[u]), u);
+            for (int u = 0; u < n_u; ++u) {
+                const int younger = (n_u - 1 - u) < (ring - 2) ? (n_u - 1 - u) : (ring - 2);
+                if (younger <= 0) wait_vmcnt<0>();
+                else if (younger == 1) wait_vmcnt<PPW>();
+                else wait_vmcnt<2 * PPW>();
+                asm volatile("s_barrier" ::: "memory");     // block u landed; block u-1 done
+                if (u + ring - 1 < n_u)                     // into the slot of block u-1
+                    issue(__builtin_amdgcn_readfirstlane(s_ulist[u + ring - 1]), (u + ring - 1) % ring);
+            }
+        } else for (int u = 0; u < n_u; ++u) {
+            lds_barrier();
             const int blk = __builtin_amdgcn_readfirstlane(s_ulist[u]);
             const unsigned long long bm = uniform_u64(s_umask[u]);
-            // block -> slot: K and V in the A-operand layout, K again for transposing reads
-            {
-                const int rows = sb.Sk - blk * kBlockKeys < kBlockKeys ? sb.Sk - blk * kBlockKeys : kBlockKeys;
-                const uint32_t nrec = (uint32_t)((rows - 1) * row_bytes + D * 2);
-                const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-                    (void*)(kseq + blk * kBlockKeys * row_bytes), 0, nrec, 0x00020000);
-                const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-                    (void*)(vseq + blk * kBlockKeys * row_bytes), 0, nrec, 0x00020000);
-                for (int inst = wave; inst < NI; inst += kBwdDqWaves) {
-                    int r, col;
-                    if (inst < 2 * NIK) {                 // A layout: fragment (kt, s)
-                        const int f = inst % NIK;
-                        const int kt = f / KS, s = f % KS;
-                        r = kt * 16 + (lane & 15);
-                        col = (4 * s + (lane >> 4)) * 16;
-                    } else {                              // transposing-read fragments
-                        const int f = 2 * (inst - 2 * NIK) + (lane >> 5);
-                        const int dt = f % DT, kh = f / DT;
-                        const int fl = 2 * (lane & 31);
-                        const int flr = fl & 15, flg = fl >> 4;
-                        r = 16 * kh + 4 * flg + (flr >> 2);
-                        col = (dt * 16 + 4 * (flr & 3)) * 2;
-                    }
-                    const uint32_t goff = (uint32_t)(r * row_bytes + col);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds((inst >= NIK && inst < 2 * NIK) ? vr : kr,
-                                                             (lds_void_t*)(smem + inst * 1024), 16, goff, 0, 0, 0);
-                }
-                __builtin_amdgcn_s_waitcnt(0x0070 | 0x0f00);   // vmcnt(0)
-            }
-            __syncthreads();
+            const uint8_t* kslot = smem + (u % ring) * L::kSlot;
+            const uint8_t* vslot = kslot + L::kPart;
             if ((bm & mt_tok) != 0ull) {
                 const bool sel = row_tok < 64 && ((bm >> row_tok) & 1ull) != 0ull;
                 f32x4_t st[4], dpt[4];
@@ -529,8 +685,10 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
                 for (int s = 0; s < KS; ++s) {
 #pragma unroll
                     for (int kt = 0; kt < 4; ++kt) {
-                        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(smem + L::kKA + (kt * KS + s) * 1024 + lane * 16);
-                        const u32x4_t va = *reinterpret_cast<const u32x4_t*>(smem + L::kVA + (kt * KS + s) * 1024 + lane * 16);
+                        // key row kt*16 + lr, chunk 4s + lg
+                        const int a = (kt * DT + 2 * s + (lg >> 1)) * 512 + lr * 32 + (lg & 1) * 16;
+                        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(kslot + a);
+                        const u32x4_t va = *reinterpret_cast<const u32x4_t*>(vslot + a);
                         st[kt] = mfma_16x16x32(ka, qf[s], st[kt]);
                         dpt[kt] = mfma_16x16x32(va, of[s], dpt[kt]);
                     }
@@ -555,15 +713,15 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
                                         pack_bf16x2(ds[2 * ks + 1][2], ds[2 * ks + 1][3])};
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
-                        const uint8_t* p0 = smem + L::kKT + ((2 * ks) * DT + dt) * 512 + lane * 8;
+                        const uint8_t* p0 = kslot + ((2 * ks) * DT + dt) * 512 + lane * 8;
                         const u32x2_t lo = tr_read(p0);
                         const u32x2_t hi = tr_read(p0 + DT * 512);
                         acc[dt] = mfma_16x16x32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, dB, acc[dt]);
                     }
                 }
             }
-            __syncthreads();   // slot reused by the next block
         }
+        lds_barrier();   // ring and union buffers free for the next window
     }
 
     if (valid) {
@@ -578,8 +736,14 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
 
 int sel_attn_bwd_rows_per_tile() { return kBwdDqWaves * 16; }
 
-size_t sel_attn_bwd_dq_lds_bytes(int D, int T, int topk) {
-    return D == 64 ? DqLds<64>::bytes(T, topk) : DqLds<128>::bytes(T, topk);
+size_t sel_attn_bwd_dq_lds_bytes(int D, int T, int topk, int ring) {
+    return D == 64 ? DqLds<64>::bytes(T, topk, ring) : DqLds<128>::bytes(T, topk, ring);
+}
+
+int sel_attn_bwd_dq_ring(int D, int T, int topk) {
+    for (int ring = 4; ring >= 2; --ring)
+        if (sel_attn_bwd_dq_lds_bytes(D, T, topk, ring) <= 160 * 1024) return ring;
+    return 0;
 }
 
 template <int D>
@@ -592,8 +756,10 @@ static hipError_t launch_bwd_d(const SelBwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_index_kernel<false>, dim3(gl), dim3(256), 0, stream, p);
     hipLaunchKernelGGL(bwd_scan_kernel, dim3(p.batch * p.Hkv), dim3(256), 0, stream, p);
     hipLaunchKernelGGL(bwd_index_kernel<true>, dim3(gl), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)(p.batch * p.Hkv * p.nb_max)),
+    hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)(p.batch * p.Hkv * p.nb_max * p.nparts)),
                        dim3(kBwdKvThreads), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dkv_finish_kernel<D>, dim3((unsigned)(p.batch * p.Hkv * p.nb_max)),
+                       dim3(256), 0, stream, p);
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_kernel<D>),
@@ -601,7 +767,7 @@ static hipError_t launch_bwd_d(const SelBwdParams& p, hipStream_t stream) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const size_t lds = DqLds<D>::bytes(p.T, p.topk);
+    const size_t lds = DqLds<D>::bytes(p.T, p.topk, p.ring);
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)(p.batch * p.Hkv * p.tiles_per_seq)),
                        dim3(kBwdDqThreads), lds, stream, p);
     return hipGetLastError();
