@@ -517,6 +517,8 @@ fsa_status_t fsa_selected_attn_bwd(const void* q, const void* k, const void* v, 
     }
     p.T = T;
     p.ring = dq_ring;
+    p.nchunk_q = (max_seqlen_q + fsa::sel_attn_bwd_index_chunk() - 1) / fsa::sel_attn_bwd_index_chunk();
+    if (p.nchunk_q < 1) p.nchunk_q = 1;
     p.mtiles = (T * G + 15) / 16;
     p.tiles_per_seq = (max_seqlen_q + T - 1) / T;
     if (p.tiles_per_seq < 1) p.tiles_per_seq = 1;

@@ -37,6 +37,42 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
+// A wave-uniform 64-bit value.  readfirstlane works on 32 bits and returns a
+// signed int, so each half goes through uint32_t (the low half must not be
+// sign-extended into the high one).
+__device__ __forceinline__ unsigned long long uniform_u64(unsigned long long x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// LDS word read that completes before it returns.  Waves that have
+// direct-to-LDS loads in flight read LDS through it: the compiler would make a
+// plain LDS read wait for all of those loads.
+__device__ __forceinline__ uint32_t lds_load_sync(const void* p) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(v)
+                 : "v"((uint32_t)(uintptr_t)p)
+                 : "memory");
+    return v;
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads in flight
+// (prefetches) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Workgroups are handed to the 8 XCDs round-robin (id % 8).  Give each XCD a
 // contiguous range of logical work ids so that work sharing K/V lands on the
 // same L2.

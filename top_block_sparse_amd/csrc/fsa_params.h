@@ -76,6 +76,7 @@ struct SelBwdParams {
     int nparts, part_steps;  // a block's 32-row steps go to <= nparts workgroups of part_steps
     int T, mtiles, tiles_per_seq;   // dq tiling
     int ring;                       // dq LDS ring slots of K/V blocks (2..4)
+    int nchunk_q;                   // index workgroups per (sequence, kv head)
     float scale, scale_log2;
 };
 
@@ -105,6 +106,7 @@ int decode_table_slots(int D, int G, int topk);
 hipError_t launch_lse_merge(const MergeParams& p, int D, hipStream_t stream);
 hipError_t launch_sel_attn_bwd(const SelBwdParams& p, int D, hipStream_t stream);
 int sel_attn_bwd_rows_per_tile();   // query rows (T*G) one dq workgroup covers
+int sel_attn_bwd_index_chunk();     // tokens one index workgroup covers
 size_t sel_attn_bwd_dq_lds_bytes(int D, int T, int topk, int ring);
 int sel_attn_bwd_dq_ring(int D, int T, int topk);   // ring slots that fit in LDS (0: none)
 

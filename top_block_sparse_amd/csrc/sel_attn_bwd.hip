@@ -10,9 +10,9 @@
 //
 // Kernels, in launch order:
 //   1. bwd_prep:  D of every row (16 lanes per row); clears the counters.
-//   2. bwd_count / bwd_scan / bwd_fill: for every (sequence, kv head, key
-//      block), the list of query tokens that selected it (each token's list
-//      read as a set) -- an inverted index, so that
+//   2. bwd_index (count) / bwd_scan / bwd_index (fill): for every (sequence,
+//      kv head, key block), the list of query tokens that selected it (each
+//      token's list read as a set) -- an inverted index, so that
 //   3. bwd_dkv: a workgroup per (sequence, kv head, block) accumulates dK and
 //      dV of its 64 keys in registers over the block's tokens, 32 query rows at
 //      a time, and writes them (blocks nobody selected get zeros).  A block
@@ -42,6 +42,7 @@ constexpr int kBwdDqWaves = 8;          // m-tiles (compute waves) per dq workgr
 constexpr int kBwdDqProducers = 2;      // waves that only move K/V blocks into LDS
 constexpr int kBwdDqThreads = (kBwdDqWaves + kBwdDqProducers) * 64;
 constexpr int kBwdWin = 256;            // blocks per union-building window (dq)
+constexpr int kSpinLimit = 1 << 22;     // bounded ring waits (normal waits are ~1e3)
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
@@ -58,30 +59,6 @@ __device__ __forceinline__ float row16_sum(float x) {
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
     return x;
-}
-
-// workgroup barrier that orders LDS accesses only: global loads in flight
-// (prefetches) are not waited for
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at "no wait")
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// a wave-uniform 64-bit value (readfirstlane works on 32 bits and returns a
-// signed int: each half goes through uint32_t so the low half is not
-// sign-extended into the high one)
-__device__ __forceinline__ unsigned long long uniform_u64(unsigned long long x) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
-    return ((unsigned long long)hi << 32) | lo;
 }
 
 // sequence holding global query token t (cu_q non-decreasing)
@@ -160,37 +137,72 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const SelBwdParams p) {
 }
 
 // ---- 2. inverted index: token lists per (sequence, kv head, block)
-// One thread per (token, kv head) list; an id counts if it is in range,
-// causally visible and the first occurrence in its list.
+// A workgroup takes kIdxChunk consecutive tokens of one (sequence, kv head),
+// one list per thread.  An id counts if it is in range, causally visible and
+// the first occurrence in its list.  Per window of kIdxWin blocks the
+// workgroup first histograms its ids in LDS; the count pass then adds each
+// bin to the global count once, and the fill pass reserves a range per bin
+// with one global atomic and places the tokens through LDS cursors.  (The
+// busiest blocks -- block 0 and the local blocks -- would otherwise serialize
+// thousands of same-address global atomics.)
+constexpr int kIdxChunk = 256;
+constexpr int kIdxWin = 8192;
+
 template <bool FILL>
-__global__ void __launch_bounds__(256) bwd_index_kernel(const SelBwdParams p) {
-    const int64_t lid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (lid >= p.total_q * p.Hkv) return;
-    const int64_t t = lid / p.Hkv;
-    const int g = (int)(lid - t * p.Hkv);
-    if (t >= p.cu_q[p.batch]) return;
-    const int b = seq_of(p.cu_q, p.batch, t);
+__global__ void __launch_bounds__(kIdxChunk) bwd_index_kernel(const SelBwdParams p) {
+    __shared__ int hist[kIdxWin];
+    const int nchunk = p.nchunk_q;
+    const int chunk = blockIdx.x % nchunk;
+    const int unit = blockIdx.x / nchunk;               // b * Hkv + g
+    const int g = unit % p.Hkv, b = unit / p.Hkv;
     const SeqBounds sb = bounds(p, b);
-    if (t < sb.q0 || t >= sb.q0 + sb.Sq) return;
-    const int i = (int)(t - sb.q0);
+    const int i0 = chunk * kIdxChunk;
+    if (i0 >= sb.Sq) return;
+    const int i = i0 + (int)threadIdx.x;                // this thread's token (in the sequence)
+    const bool tok_ok = i < sb.Sq;
     const int off = sb.Sk - sb.Sq;
     int nblk = (sb.Sk + kBlockKeys - 1) / kBlockKeys;
-    nblk = nblk < p.nb_max ? nblk : p.nb_max;        // (max_seqlen_k bounds every S_k)
-    const int32_t* lst = p.blk_idx + lid * p.topk;
-    const int64_t unit = (int64_t)b * p.Hkv + g;
-    for (int e = 0; e < p.topk; ++e) {
+    nblk = nblk < p.nb_max ? nblk : p.nb_max;          // (max_seqlen_k bounds every S_k)
+    const int32_t* lst = p.blk_idx + ((sb.q0 + (tok_ok ? i : 0)) * p.Hkv + g) * (int64_t)p.topk;
+    int32_t* cnt = p.counts + (int64_t)unit * (p.nb_max + 1);
+    int32_t* cur = p.cursor + (int64_t)unit * p.nb_max;
+    const int64_t tbase = toks_base(p, sb, g);
+    // an entry's id if it counts, else -1
+    auto entry = [&](int e) -> int {
         const int id = lst[e];
-        if (id < 0 || id >= nblk) continue;
-        if (p.causal && (long long)id * kBlockKeys > (long long)i + off) continue;
-        bool first = true;
-        for (int e2 = 0; e2 < e; ++e2) first = first && lst[e2] != id;
-        if (!first) continue;
-        if constexpr (!FILL) {
-            atomicAdd(&p.counts[unit * (p.nb_max + 1) + id], 1);
-        } else {
-            const int pos = atomicAdd(&p.cursor[unit * p.nb_max + id], 1);
-            p.toks[toks_base(p, sb, g) + p.counts[unit * (p.nb_max + 1) + id] + pos] = i;
+        if (id < 0 || id >= nblk) return -1;
+        if (p.causal && (long long)id * kBlockKeys > (long long)i + off) return -1;
+        for (int e2 = 0; e2 < e; ++e2)
+            if (lst[e2] == id) return -1;
+        return id;
+    };
+    for (int w0 = 0; w0 < nblk; w0 += kIdxWin) {
+        const int wn = (nblk - w0) < kIdxWin ? (nblk - w0) : kIdxWin;
+        for (int x = threadIdx.x; x < wn; x += kIdxChunk) hist[x] = 0;
+        __syncthreads();
+        if (tok_ok)
+            for (int e = 0; e < p.topk; ++e) {
+                const int id = entry(e);
+                if (id >= w0 && id < w0 + wn) atomicAdd(&hist[id - w0], 1);
+            }
+        __syncthreads();
+        for (int x = threadIdx.x; x < wn; x += kIdxChunk) {
+            const int h = hist[x];
+            if constexpr (!FILL) {
+                if (h > 0) atomicAdd(&cnt[w0 + x], h);
+            } else {
+                hist[x] = h > 0 ? cnt[w0 + x] + atomicAdd(&cur[w0 + x], h) : 0;   // this chunk's range
+            }
         }
+        if constexpr (FILL) {
+            __syncthreads();
+            if (tok_ok)
+                for (int e = 0; e < p.topk; ++e) {
+                    const int id = entry(e);
+                    if (id >= w0 && id < w0 + wn) p.toks[tbase + atomicAdd(&hist[id - w0], 1)] = i;
+                }
+        }
+        __syncthreads();
     }
 }
 
@@ -501,7 +513,9 @@ struct DqLds {
     __host__ __device__ static int umask(int ring) { return masks(ring) + kBwdWin * 8; }  // u64 [kBwdWin]
     __host__ __device__ static int ulist(int ring) { return umask(ring) + kBwdWin * 8; }  // i32 [kBwdWin]
     __host__ __device__ static int count(int ring) { return ulist(ring) + kBwdWin * 4; }  // i32
-    __host__ __device__ static int ent(int ring) { return count(ring) + 16; }             // i32 [T * topk]
+    __host__ __device__ static int ready(int ring) { return count(ring) + 16; }           // u32 [4][producers]
+    __host__ __device__ static int done(int ring) { return ready(ring) + 4 * kBwdDqProducers * 4; }  // u32 [4]
+    __host__ __device__ static int ent(int ring) { return done(ring) + 16; }              // i32 [T * topk]
     __host__ __device__ static size_t bytes(int T, int topk, int ring) {
         return (size_t)ent(ring) + (size_t)T * topk * 4;
     }
@@ -520,10 +534,13 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
     unsigned long long* s_umask = reinterpret_cast<unsigned long long*>(smem + L::umask(ring));
     int* s_ulist = reinterpret_cast<int*>(smem + L::ulist(ring));
     int* s_count = reinterpret_cast<int*>(smem + L::count(ring));
+    uint32_t* s_ready = reinterpret_cast<uint32_t*>(smem + L::ready(ring));
+    uint32_t* s_done = reinterpret_cast<uint32_t*>(smem + L::done(ring));
     int* s_ent = reinterpret_cast<int*>(smem + L::ent(ring));
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
+    if (tid < 4 * (kBwdDqProducers + 1)) s_ready[tid] = 0u;   // s_ready and s_done
 
     int w = xcd_remap(blockIdx.x, (int)gridDim.x);
     const int j = p.tiles_per_seq - 1 - (w % p.tiles_per_seq);
@@ -574,7 +591,19 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
             dval = p.dvec[(int64_t)head * p.total_q + tq];
         }
     }
-    const int cpos = p.causal ? tok0 + t_l + off : 0x7fffffff;
+    // last visible key of the row, and its minimum over the m-tile's rows:
+    // blocks that end at or before it need no per-key mask
+    const int row_lim = p.causal ? (tok0 + t_l + off < sb.Sk - 1 ? tok0 + t_l + off : sb.Sk - 1) : sb.Sk - 1;
+    int lo_lim;
+    {
+        int lo = valid ? row_lim : 0x7fffffff;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_xor(lo, o);
+            lo = y < lo ? y : lo;
+        }
+        lo_lim = __builtin_amdgcn_readfirstlane(lo);
+    }
     const int row_tok = valid ? t_l : 64;
     unsigned long long mk = 0ull;
     if (mt < p.mtiles) {
@@ -621,6 +650,16 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
                                                      16, (uint32_t)dma_off[x], 0, 0, 0);
         }
     };
+    auto publish = [&](int slot, uint32_t seq_plus1) {
+        if (lane == 0) {
+            asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                         :
+                         : "v"((uint32_t)(uintptr_t)(s_ready + slot * kBwdDqProducers + pw)), "v"(seq_plus1)
+                         : "memory");
+        }
+    };
+    const int depth = ring - 1 < 3 ? ring - 1 : 3;    // blocks in flight per producer
+    uint32_t seq0 = 0;                                // ring sequence number of the window's first block
     __syncthreads();
 
     for (int win_lo = 0; win_lo < nb_range; win_lo += kBwdWin) {
@@ -650,36 +689,59 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
         __syncthreads();
         const int n_u = __builtin_amdgcn_readfirstlane(s_count[0]);
 
-        // Ring: blocks u+1 .. u+ring-2 stay in flight while block u is used.
-        // Producer and compute waves run separate loops with one barrier per
-        // block each, so no compute wave ever has a direct-to-LDS load of its
-        // own outstanding (nothing makes it wait for one) and the producers
-        // wait only for the block due next.
+        // Ring protocol.  The producers copy the union's blocks in order into
+        // ring slots (up to `depth` blocks in flight) and publish a slot by
+        // writing its sequence number once their loads have landed; each
+        // compute wave waits for the slot, uses it if one of its tokens
+        // selected the block, and counts itself done with it; a producer
+        // refills a slot only after every compute wave is done with it.
+        // Compute waves never wait for one another, so the uneven work of
+        // random selections evens out over the tile.  Every wait is bounded.
         if (wave >= kBwdDqWaves) {
-            for (int u = 0; u < n_u && u < ring - 1; ++u)
-                issue(__builtin_amdgcn_readfirstlane(s_ulist[u]), u);
-            for (int u = 0; u < n_u; ++u) {
-                const int younger = (n_u - 1 - u) < (ring - 2) ? (n_u - 1 - u) : (ring - 2);
-                if (younger <= 0) wait_vmcnt<0>();
-                else if (younger == 1) wait_vmcnt<PPW>();
-                else wait_vmcnt<2 * PPW>();
-                asm volatile("s_barrier" ::: "memory");     // block u landed; block u-1 done
-                if (u + ring - 1 < n_u)                     // into the slot of block u-1
-                    issue(__builtin_amdgcn_readfirstlane(s_ulist[u + ring - 1]), (u + ring - 1) % ring);
+            for (int i = 0; i < n_u; ++i) {
+                const uint32_t seq = seq0 + (uint32_t)i;
+                const int slot = (int)(seq % (uint32_t)ring);
+                const uint32_t need_done = kBwdDqWaves * (seq / (uint32_t)ring);
+                for (int sp = 0; sp < kSpinLimit && lds_load_sync(s_done + slot) < need_done; ++sp)
+                    __builtin_amdgcn_s_sleep(1);
+                issue(__builtin_amdgcn_readfirstlane((int)lds_load_sync(s_ulist + i)), slot);
+                if (i >= depth - 1) {
+                    if (depth == 3) wait_vmcnt<2 * PPW>();
+                    else if (depth == 2) wait_vmcnt<PPW>();
+                    else wait_vmcnt<0>();
+                    const uint32_t ps = seq - (uint32_t)(depth - 1);
+                    publish((int)(ps % (uint32_t)ring), ps + 1);
+                }
+            }
+            wait_vmcnt<0>();
+            for (int i = n_u > depth - 1 ? n_u - (depth - 1) : 0; i < n_u; ++i) {
+                const uint32_t ps = seq0 + (uint32_t)i;
+                publish((int)(ps % (uint32_t)ring), ps + 1);
             }
         } else for (int u = 0; u < n_u; ++u) {
-            lds_barrier();
+            const uint32_t seq = seq0 + (uint32_t)u;
+            const int slot = (int)(seq % (uint32_t)ring);
+            for (int sp = 0; sp < kSpinLimit; ++sp) {
+                bool ok = true;
+#pragma unroll
+                for (int q = 0; q < kBwdDqProducers; ++q)
+                    ok = ok && lds_load_sync(s_ready + slot * kBwdDqProducers + q) >= seq + 1;
+                if (ok) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
             const int blk = __builtin_amdgcn_readfirstlane(s_ulist[u]);
             const unsigned long long bm = uniform_u64(s_umask[u]);
-            const uint8_t* kslot = smem + (u % ring) * L::kSlot;
+            const uint8_t* kslot = smem + slot * L::kSlot;
             const uint8_t* vslot = kslot + L::kPart;
             if ((bm & mt_tok) != 0ull) {
                 const bool sel = row_tok < 64 && ((bm >> row_tok) & 1ull) != 0ull;
+                const float msub = sel ? lse2 : INFINITY;      // unselected rows get P = 0
+                // dP^T starts at -D, so the MFMA leaves dP - D
                 f32x4_t st[4], dpt[4];
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
                     st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    dpt[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    dpt[kt] = f32x4_t{-dval, -dval, -dval, -dval};
                 }
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
@@ -696,14 +758,16 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
                 // dS^T (lane: keys blk*64 + 16kt + 4lg + i, row lr)
                 float ds[4][4];
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
+                for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = blk * kBlockKeys + kt * 16 + lg * 4 + i;
-                        const bool vis = sel && key < sb.Sk && key <= cpos;
-                        const float pr = vis ? fast_exp2(fmaf(st[kt][i], c2, -lse2)) : 0.f;
-                        ds[kt][i] = pr * (dpt[kt][i] - dval);
-                    }
+                    for (int i = 0; i < 4; ++i) ds[kt][i] = fast_exp2(fmaf(st[kt][i], c2, -msub)) * dpt[kt][i];
+                if (blk * kBlockKeys + kBlockKeys - 1 > lo_lim) {      // diagonal or partial block
+                    const int lim = row_lim - blk * kBlockKeys;
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (kt * 16 + lg * 4 + i > lim) ds[kt][i] = 0.f;
                 }
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
@@ -720,7 +784,11 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
                     }
                 }
             }
+            // done with the slot: its reads have completed before the count
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            if (lane == 0) __hip_atomic_fetch_add(s_done + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
+        seq0 += (uint32_t)n_u;
         lds_barrier();   // ring and union buffers free for the next window
     }
 
@@ -735,6 +803,8 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
 }
 
 int sel_attn_bwd_rows_per_tile() { return kBwdDqWaves * 16; }
+
+int sel_attn_bwd_index_chunk() { return kIdxChunk; }
 
 size_t sel_attn_bwd_dq_lds_bytes(int D, int T, int topk, int ring) {
     return D == 64 ? DqLds<64>::bytes(T, topk, ring) : DqLds<128>::bytes(T, topk, ring);
@@ -751,11 +821,10 @@ static hipError_t launch_bwd_d(const SelBwdParams& p, hipStream_t stream) {
     const int64_t nrows = p.total_q * p.Hq;
     const unsigned gp = (unsigned)((nrows + 15) / 16 > 0 ? (nrows + 15) / 16 : 1);
     hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(gp), dim3(256), 0, stream, p);
-    const int64_t nl = p.total_q * p.Hkv;
-    const unsigned gl = (unsigned)((nl + 255) / 256 > 0 ? (nl + 255) / 256 : 1);
-    hipLaunchKernelGGL(bwd_index_kernel<false>, dim3(gl), dim3(256), 0, stream, p);
+    const unsigned gl = (unsigned)(p.batch * p.Hkv * p.nchunk_q);
+    hipLaunchKernelGGL(bwd_index_kernel<false>, dim3(gl), dim3(kIdxChunk), 0, stream, p);
     hipLaunchKernelGGL(bwd_scan_kernel, dim3(p.batch * p.Hkv), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(bwd_index_kernel<true>, dim3(gl), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(bwd_index_kernel<true>, dim3(gl), dim3(kIdxChunk), 0, stream, p);
     hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)(p.batch * p.Hkv * p.nb_max * p.nparts)),
                        dim3(kBwdKvThreads), 0, stream, p);
     hipLaunchKernelGGL(bwd_dkv_finish_kernel<D>, dim3((unsigned)(p.batch * p.Hkv * p.nb_max)),

@@ -85,12 +85,6 @@ struct SelLds {
     }
 };
 
-__device__ __forceinline__ unsigned long long uniform_u64(unsigned long long x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
-    return ((unsigned long long)hi << 32) | lo;
-}
-
 __device__ __forceinline__ float lane_max4(float x) {
     // max over lanes l, l^16, l^32, l^48 (the four lanes holding one query row)
     auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -115,32 +109,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ u32x2_t lds_read_tr16(const uint8_t* p) {
     const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
     return __builtin_bit_cast(u32x2_t, v);
-}
-
-// LDS word read that completes before it returns.  Used by the ring protocol
-// (flags written by other waves) and by the producers, whose buffer->LDS
-// loads the compiler would otherwise make every LDS read wait for.
-__device__ __forceinline__ uint32_t lds_load_sync(const void* p) {
-    uint32_t v;
-    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(v)
-                 : "v"((uint32_t)(uintptr_t)p)
-                 : "memory");
-    return v;
-}
-
-// Workgroup barrier that orders LDS only (no drain of global loads).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at "no wait").
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 template <int D>
