@@ -238,18 +238,23 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(const SelBwdParams p) {
 }
 
 // ---- 3. dK, dV of one key block
+// Staging buffer of one step (two alternate): the 32 rows of Q and of dO in
+// the fragment-permuted layout -- 16-byte chunk c of row r in fragment
+// (r/16)*DT + c/2 at byte (4(r%16) + 2(c%2))*8 -- so that a plain 16-byte read
+// gives the A operand of S = Q K^T (dP = dO V^T) and a transposing 8-byte read
+// the A operand of dK^T = Q^T dS (dV^T = dO^T P).  Fragments sit kFrag = 544
+// bytes apart (512 + 32 of padding) so that the 16 chunks of one row, written
+// by 16 adjacent lanes, land in 16 different bank groups.
 template <int D>
 struct KvLds {
     static constexpr int DT = D / 16;
-    static constexpr int kRowStride = D * 2 + 16;                 // padded bf16 row
-    static constexpr int kRowBytes = kBwdRows * kRowStride;
-    static constexpr int kTrBytes = kBwdRows * D * 2;              // 2 h x DT fragments of 512 B
-    static constexpr int qrow = 0;
-    static constexpr int orow = qrow + kRowBytes;
-    static constexpr int qtr = orow + kRowBytes;
-    static constexpr int otr = qtr + kTrBytes;
-    static constexpr int rowinfo = otr + kTrBytes;                 // f32x4 per row: lse2, D, cpos, valid
-    static constexpr int bytes = rowinfo + kBwdRows * 16;
+    static constexpr int kFrag = 544;
+    static constexpr int kPart = 2 * DT * kFrag;                  // 32 rows x D
+    static constexpr int q = 0;
+    static constexpr int o = q + kPart;
+    static constexpr int rowinfo = o + kPart;                     // f32x4 per row: lse2, D, last key
+    static constexpr int kBuf = rowinfo + kBwdRows * 16;
+    static constexpr int bytes = 2 * kBuf;
 };
 
 template <int D>
@@ -356,67 +361,93 @@ __global__ void __launch_bounds__(kBwdKvThreads) bwd_dkv_kernel(const SelBwdPara
         cpos = p.causal ? tki + off : 0x7fffffff;
         row_ok = tok_ok;
     };
-    auto stage = [&]() {                                   // registers -> row and tr layouts
+    auto stage = [&](int buf) {                            // registers -> staging buffer buf
+        uint8_t* sb_ = smem + buf * L::kBuf;
 #pragma unroll
         for (int k = 0; k < NI; ++k) {
             const int r = (tid + k * kBwdKvThreads) / CPR;
             const bool ok = (row_ok >> k) & 1;
             const u32x4_t z = {0u, 0u, 0u, 0u};
-            const u32x4_t a = ok ? qv[k] : z, c = ok ? ov[k] : z;
-            *reinterpret_cast<u32x4_t*>(smem + L::qrow + r * L::kRowStride + cc * 16) = a;
-            *reinterpret_cast<u32x4_t*>(smem + L::orow + r * L::kRowStride + cc * 16) = c;
-            const int fl = 16 * ((r % 16) / 4) + 4 * (r % 4) + 2 * (cc % 2);
-            const int fo = ((r / 16) * DT + cc / 2) * 512 + fl * 8;
-            *reinterpret_cast<u32x4_t*>(smem + L::qtr + fo) = a;
-            *reinterpret_cast<u32x4_t*>(smem + L::otr + fo) = c;
+            const int fo = ((r / 16) * DT + cc / 2) * L::kFrag + (4 * (r % 16) + 2 * (cc % 2)) * 8;
+            *reinterpret_cast<u32x4_t*>(sb_ + L::q + fo) = ok ? qv[k] : z;
+            *reinterpret_cast<u32x4_t*>(sb_ + L::o + fo) = ok ? ov[k] : z;
         }
         if (tid < kBwdRows) {
+            // rows that are padding get lse2 = +inf (so P = 0) and no key limit
             const bool ok = (row_ok >> NI) & 1;
-            const f32x4_t info = ok ? f32x4_t{lse_r * kLog2e, dv_r, __int_as_float(cpos), 1.f}
-                                    : f32x4_t{INFINITY, 0.f, 0.f, 0.f};   // lse2, D, cpos, valid
-            *reinterpret_cast<f32x4_t*>(smem + L::rowinfo + tid * 16) = info;
+            const f32x4_t info = ok ? f32x4_t{lse_r * kLog2e, dv_r, __int_as_float(cpos), 0.f}
+                                    : f32x4_t{INFINITY, 0.f, __int_as_float(0x7fffffff), 0.f};
+            *reinterpret_cast<f32x4_t*>(sb_ + L::rowinfo + tid * 16) = info;
         }
     };
 
+    // Two staging buffers: while step i is computed from buffer i&1, the rows
+    // of step i+1 (gathered during step i-1) are staged into the other one,
+    // so one barrier per step suffices.
+    const int blk_last = blk * kBlockKeys + kBlockKeys - 1;   // last key of the block
+    const bool partial = blk_last >= sb.Sk;
     if (c_lo < ntk) {                 // (ntk >= 1 below: clamped ids stay in the list)
         fetch_tok(c_lo);
         fetch_rows();
         fetch_tok(c_lo + tpc);
-    }
-    for (int c0 = c_lo; c0 < ntk; c0 += tpc) {
-        stage();
+        stage(0);
+        fetch_rows();
+        fetch_tok(c_lo + 2 * tpc);
         lds_barrier();
-        fetch_rows();                 // the next step (staged as zeros past the end)
-        fetch_tok(c0 + 2 * tpc);
-        __builtin_amdgcn_sched_barrier(0);   // keep the gathers ahead of the MFMA work
-
-        // S = Q K^T and dP = dO V^T for rows 0-15 / 16-31 and this wave's keys
+    }
+    for (int c0 = c_lo, it = 0; c0 < ntk; c0 += tpc, ++it) {
+        const uint8_t* cb = smem + (it & 1) * L::kBuf;
+        // row data of rows 16rt + 4lg + i
+        f32x4_t ri[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ri[rt][i] = *reinterpret_cast<const f32x4_t*>(cb + L::rowinfo + (16 * rt + 4 * lg + i) * 16);
+        // S = Q K^T and dP - D = dO V^T - D for rows 0-15 / 16-31 and this
+        // wave's keys (the accumulator of dP starts at -D)
         f32x4_t st[2], dp[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             st[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            dp[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            const int roff = (16 * rt + lr) * L::kRowStride + lg * 16;
+            dp[rt] = f32x4_t{-ri[rt][0][1], -ri[rt][1][1], -ri[rt][2][1], -ri[rt][3][1]};
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const u32x4_t qa = *reinterpret_cast<const u32x4_t*>(smem + L::qrow + roff + s * 64);
-                const u32x4_t oa = *reinterpret_cast<const u32x4_t*>(smem + L::orow + roff + s * 64);
+                // row 16rt + lr, chunk 4s + lg
+                const int a = (rt * DT + 2 * s + (lg >> 1)) * L::kFrag + lr * 32 + (lg & 1) * 16;
+                const u32x4_t qa = *reinterpret_cast<const u32x4_t*>(cb + L::q + a);
+                const u32x4_t oa = *reinterpret_cast<const u32x4_t*>(cb + L::o + a);
                 st[rt] = mfma_16x16x32(qa, kf[s], st[rt]);
                 dp[rt] = mfma_16x16x32(oa, vf[s], dp[rt]);
             }
         }
-        // P and dS (lane: rows 16rt + 4lg + i, key kabs)
+        // P and dS (lane: rows 16rt + 4lg + i, key kabs); per-key masks only
+        // where a row's last visible key falls inside the block
+        bool cut = false;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cut = cut || __float_as_int(ri[rt][i][2]) < blk_last;
+        const bool need_mask = partial || __builtin_amdgcn_ballot_w64(cut) != 0ull;
         float pv[2][4], dsv[2][4];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const f32x4_t ri = *reinterpret_cast<const f32x4_t*>(smem + L::rowinfo + (16 * rt + 4 * lg + i) * 16);
-                const bool vis = key_ok && ri[3] != 0.f && kabs <= __float_as_int(ri[2]);
-                const float pr = vis ? fast_exp2(fmaf(st[rt][i], c2, -ri[0])) : 0.f;
+                const float pr = fast_exp2(fmaf(st[rt][i], c2, -ri[rt][i][0]));
                 pv[rt][i] = pr;
-                dsv[rt][i] = pr * (dp[rt][i] - ri[1]);
+                dsv[rt][i] = pr * dp[rt][i];
             }
+        }
+        if (need_mask) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (!key_ok || kabs > __float_as_int(ri[rt][i][2])) {
+                        pv[rt][i] = 0.f;
+                        dsv[rt][i] = 0.f;
+                    }
         }
         const u32x4_t pB = {pack_bf16x2(pv[0][0], pv[0][1]), pack_bf16x2(pv[0][2], pv[0][3]),
                             pack_bf16x2(pv[1][0], pv[1][1]), pack_bf16x2(pv[1][2], pv[1][3])};
@@ -425,13 +456,16 @@ __global__ void __launch_bounds__(kBwdKvThreads) bwd_dkv_kernel(const SelBwdPara
         // dV^T += dO^T P, dK^T += Q^T dS  (A operands by transposing reads)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const u32x2_t olo = tr_read(smem + L::otr + dt * 512 + lane * 8);
-            const u32x2_t ohi = tr_read(smem + L::otr + (DT + dt) * 512 + lane * 8);
-            const u32x2_t qlo = tr_read(smem + L::qtr + dt * 512 + lane * 8);
-            const u32x2_t qhi = tr_read(smem + L::qtr + (DT + dt) * 512 + lane * 8);
+            const u32x2_t olo = tr_read(cb + L::o + dt * L::kFrag + lane * 8);
+            const u32x2_t ohi = tr_read(cb + L::o + (DT + dt) * L::kFrag + lane * 8);
+            const u32x2_t qlo = tr_read(cb + L::q + dt * L::kFrag + lane * 8);
+            const u32x2_t qhi = tr_read(cb + L::q + (DT + dt) * L::kFrag + lane * 8);
             adv[dt] = mfma_16x16x32(u32x4_t{olo[0], olo[1], ohi[0], ohi[1]}, pB, adv[dt]);
             adk[dt] = mfma_16x16x32(u32x4_t{qlo[0], qlo[1], qhi[0], qhi[1]}, dB, adk[dt]);
         }
+        stage((it + 1) & 1);          // the next step (zeros past the end)
+        fetch_rows();                 // gathers for the step after it
+        fetch_tok(c0 + 3 * tpc);
         lds_barrier();
     }
 
