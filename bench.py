@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 METRIC = "selected-attn fwd effective TFLOP/s + decode HBM GB/s, % roofline (1 GPU)"
 PREFILL = "prefill_b2_s8192_h32_kv8_d128_top16"
 DECODE = "decode_b32_h32_kv8_d128_L32768_p256_top2048"
+WINDOW_WL = "sliding_window_512_b2_s8192_h32_kv8_d128"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -161,7 +162,7 @@ def main():
         if args.mode == "decode_fp8":
             del sets
 
-    WINDOW = 512
+    WINDOW = 512                       # the window of WINDOW_WL
     # keys visible to each row under the causal window (WINDOW - 1, 0)
     w_keys = sum(min(WINDOW, i + 1) for s_len in pspec.seqlens for i in range(s_len))
     w_flops = 4.0 * pspec.head_dim * pspec.num_heads_q * w_keys
@@ -299,7 +300,7 @@ def main():
     traffic = measured_traffic(kern_src, PREFILL)
     roofline = {"bound": "mfma", "achieved": round(p_tflops_evt, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(p_tflops_evt / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": "sel_attn_fwd_kernel<128>",
+                "traffic": traffic, "kernel": "sel_attn_fwd_kernel<128, false>",
                 "flops_per_launch": flops, "avg_launch_ms": round(float(p_ms.mean()), 4)}
     dec_src = os.path.join(ROOT, "top_block_sparse_amd", "csrc", "topk_decode.hip")
     d_traffic = measured_traffic(dec_src, DECODE)
@@ -309,25 +310,27 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(d_gbs_evt, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(d_gbs_evt / PEAK_HBM_GBS, 4),
                      "traffic": d_traffic, "bytes_per_call": d_bytes,
-                     "scope": "whole call: prepass + split + merge kernels"},
+                     "scope": "whole call: the fused decode kernel (plus the LSE merge when split)"},
     }
 
     log(f"window : mean {w_ms.mean():.3f} ms  {w_tflops:.1f} TFLOP/s (events)")
     window_obj = {
         "value": round(w_tflops, 2), "unit": "TFLOP/s",
-        "workload": f"sliding_window_{WINDOW}_b2_s8192_h32_kv8_d128",
+        "workload": WINDOW_WL,
         "ms_per_call": round(float(w_ms.mean()), 4),
         "roofline": {"bound": "mfma", "achieved": round(w_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(w_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "flops_per_call": w_flops},
+                     "traffic": measured_traffic(kern_src, WINDOW_WL), "flops_per_call": w_flops},
     }
     log(f"backward: mean {b_ms.mean():.3f} ms  {b_tflops:.1f} TFLOP/s (events)")
+    bwd_src = os.path.join(ROOT, "top_block_sparse_amd", "csrc", "sel_attn_bwd.hip")
     backward_obj = {
         "value": round(b_tflops, 2), "unit": "TFLOP/s", "workload": PREFILL + "_backward",
         "ms_per_call": round(float(b_ms.mean()), 4),
         "roofline": {"bound": "mfma", "achieved": round(b_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(b_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "flops_per_call": b_flops,
+                     "traffic": measured_traffic(bwd_src, PREFILL + "_backward"),
+                     "flops_per_call": b_flops,
                      "scope": "whole call: D prep, block index, dK/dV and dQ kernels"},
     }
     decode_fp8_obj = {

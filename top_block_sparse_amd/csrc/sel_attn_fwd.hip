@@ -111,7 +111,10 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const uint8_t* p) {
     return __builtin_bit_cast(u32x2_t, v);
 }
 
-template <int D>
+// WIN: a lower key bound (sliding window) or window-derived (dense) block
+// sets are possible; without it the kernel keeps none of that state, which
+// the selected-attention path would otherwise pay for in registers.
+template <int D, bool WIN>
 __global__ void __launch_bounds__(kSelThreads)
 sel_attn_fwd_kernel(const SelFwdParams p) {
     constexpr int KS = D / 32;                  // MFMA k-steps over the head dim
@@ -168,8 +171,9 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         const long long last_key = (long long)tok0 + ntok - 1 + off + p.wr;
         nb_range = last_key < 0 ? 0 : (int)(last_key / kBlockKeys + 1 < nblk ? last_key / kBlockKeys + 1 : nblk);
     }
-    if (p.wl >= 0) {
-        const long long first_key = (long long)tok0 + off - p.wl;
+    const int wl = WIN ? p.wl : -1;             // lower window bound (-1: none)
+    if (wl >= 0) {
+        const long long first_key = (long long)tok0 + off - wl;
         nb_lo = first_key <= 0 ? 0 : (int)(first_key / kBlockKeys);
     }
     const int topk = p.topk;
@@ -185,7 +189,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         bool ok = id >= nb_lo && id < nb_range;
         const long long c = (long long)tok0 + tl + off;
         if (ok && p.wr >= 0) ok = (long long)id * kBlockKeys <= c + p.wr;
-        if (ok && p.wl >= 0) ok = (long long)id * kBlockKeys + kBlockKeys - 1 >= c - p.wl;
+        if (ok && wl >= 0) ok = (long long)id * kBlockKeys + kBlockKeys - 1 >= c - wl;
         s_ent[e] = ok ? id : -1;
     }
     if (tid < kSelRingMax * (kSelProducers + 1)) s_ready[tid] = 0u;   // s_ready and s_done
@@ -214,7 +218,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         if (p.wr >= 0 && c + p.wr + 1 < lim) lim = c + p.wr + 1;
         row_lim = (int)(lim < -1 ? -1 : lim);
         long long lo_k = 0;
-        if (p.wl >= 0 && c - p.wl > 0) lo_k = c - p.wl;
+        if (wl >= 0 && c - wl > 0) lo_k = c - wl;
         row_lo = (int)lo_k;
         int lo = valid ? row_lim : 0x7fffffff;
         int hl = valid ? row_lo : 0;
@@ -226,7 +230,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
             hl = z > hl ? z : hl;
         }
         lo_lim = __builtin_amdgcn_readfirstlane(lo);
-        hi_lo = __builtin_amdgcn_readfirstlane(hl);
+        hi_lo = WIN ? __builtin_amdgcn_readfirstlane(hl) : 0;
         const uint16_t* qrow = p.q + ((q0 + tok0 + tl) * p.Hq + g * G + hh) * (int64_t)D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -276,7 +280,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
                 for (int i = 0; i < 4; ++i)
                     if (kt * 16 + lg * 4 + i >= lim) x[kt * 4 + i] = -INFINITY;
         }
-        if (blk * kBlockKeys < hi_lo) {                          // window start
+        if (WIN && blk * kBlockKeys < hi_lo) {                   // window start
             const int lo = row_lo - blk * kBlockKeys;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
@@ -379,7 +383,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     uint32_t seq0 = 0;    // ring sequence number of the window's first block
     for (int win_lo = nb_lo; win_lo < nb_range; win_lo += kSelWin) {
         const int win_n = (nb_range - win_lo) < kSelWin ? (nb_range - win_lo) : kSelWin;
-        if (p.dense) {
+        if (WIN && p.dense) {
             // every block of the window: the tokens whose key range meets it
             for (int x = tid; x < kSelWin; x += kSelThreads) {
                 unsigned long long mk = 0ull;
@@ -387,8 +391,8 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
                     const long long bk = (long long)(win_lo + x) * kBlockKeys;
                     long long t_lo = 0, t_hi = ntok - 1;
                     if (p.wr >= 0 && bk - p.wr - tok0 - off > t_lo) t_lo = bk - p.wr - tok0 - off;
-                    if (p.wl >= 0 && bk + kBlockKeys - 1 + p.wl - tok0 - off < t_hi)
-                        t_hi = bk + kBlockKeys - 1 + p.wl - tok0 - off;
+                    if (wl >= 0 && bk + kBlockKeys - 1 + wl - tok0 - off < t_hi)
+                        t_hi = bk + kBlockKeys - 1 + wl - tok0 - off;
                     if (t_lo <= t_hi) {
                         const int nbits = (int)(t_hi - t_lo + 1);
                         mk = (nbits >= 64 ? ~0ull : ((1ull << nbits) - 1ull)) << t_lo;
@@ -516,18 +520,24 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
 }
 
 // Launch helpers (host side).
-template <int D>
-hipError_t launch_sel_attn_fwd(const SelFwdParams& p, hipStream_t stream) {
+template <int D, bool WIN>
+static hipError_t launch_sel_attn_fwd_t(const SelFwdParams& p, hipStream_t stream) {
     const size_t lds = SelLds<D>::bytes(p.T, p.topk, p.ring);
     static bool attr_set = false;   // idempotent; racing threads set the same value
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sel_attn_fwd_kernel<D>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sel_attn_fwd_kernel<D, WIN>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(sel_attn_fwd_kernel<D>, dim3(p.n_wg), dim3(kSelThreads), lds, stream, p);
+    hipLaunchKernelGGL((sel_attn_fwd_kernel<D, WIN>), dim3(p.n_wg), dim3(kSelThreads), lds, stream, p);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_sel_attn_fwd(const SelFwdParams& p, hipStream_t stream) {
+    return (p.wl >= 0 || p.dense) ? launch_sel_attn_fwd_t<D, true>(p, stream)
+                                  : launch_sel_attn_fwd_t<D, false>(p, stream);
 }
 
 template hipError_t launch_sel_attn_fwd<64>(const SelFwdParams&, hipStream_t);
