@@ -64,6 +64,9 @@ def _load():
         lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
         lib.oracle_lse_merge.restype = None
         lib.oracle_lse_merge.argtypes = [i64, i32, P, P, P, P]
+        lib.oracle_block_select.restype = ctypes.c_int
+        lib.oracle_block_select.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32,
+                                            i32, i32, f64, P, i64, P, P]
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         _lib = lib
@@ -202,6 +205,43 @@ def window_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
     if rc != 0:
         raise ValueError("oracle_window_attn_fwd rejected its arguments")
     return out, lse
+
+
+def block_select(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q, cu_seqlens_k,
+                 kernel_size: int = 32, kernel_stride: int = 16, block_size: int = 64,
+                 topk: int = 16, init_blocks: int = 1, local_blocks: int = 2,
+                 softmax_scale: Optional[float] = None, tokens=None, with_scores: bool = False):
+    """Block lists from compressed attention (mean-pooled key windows, block
+    importance, top-k with forced init / local blocks) for every query token
+    (or the listed ``tokens``).  Returns ``blk_idx [n, Hkv, topk] int32`` and,
+    with ``with_scores``, the block importances ``[n, Hkv, nb_max] float64``."""
+    lib = _load()
+    total_q, Hq, d = q.shape
+    Hkv = k.shape[1]
+    cu_q = _i32(cu_seqlens_q)
+    cu_k = _i32(cu_seqlens_k)
+    batch = cu_q.size - 1
+    scale = (1.0 / np.sqrt(d)) if softmax_scale is None else float(softmax_scale)
+    qb, kb = _bits(q), _bits(k)
+    if tokens is None:
+        tp, n = None, total_q
+    else:
+        tarr = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+        tp, n = tarr.ctypes.data, tarr.size
+    if block_size <= 0 or topk <= 0:
+        raise ValueError("oracle.block_select: block_size and topk must be positive")
+    max_sk = int(max([cu_k[b + 1] - cu_k[b] for b in range(batch)], default=0))
+    nb_max = (max_sk + block_size - 1) // block_size
+    out = np.full((n, Hkv, topk), -1, dtype=np.int32)
+    sc = np.zeros((n, Hkv, max(nb_max, 1)), dtype=np.float64) if with_scores else None
+    rc = lib.oracle_block_select(qb.data_ptr(), kb.data_ptr(), cu_q.ctypes.data, cu_k.ctypes.data,
+                                 batch, Hq, Hkv, d, int(kernel_size), int(kernel_stride),
+                                 int(block_size), int(topk), int(init_blocks), int(local_blocks),
+                                 scale, tp, n, out.ctypes.data,
+                                 sc.ctypes.data if with_scores else None)
+    if rc != 0:
+        raise ValueError("oracle_block_select rejected its arguments")
+    return (out, sc[:, :, :nb_max]) if with_scores else out
 
 
 def e4m3_value(byte: int) -> float:

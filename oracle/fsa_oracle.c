@@ -523,6 +523,175 @@ int oracle_topk_decode_fp8(const uint16_t* q, const uint8_t* k_cache, const uint
 }
 
 /*
+ * Block-index producer: NSA-style selection of the blocks a query token
+ * attends to, from a compressed view of the keys (FSA page, quick start:
+ * kernel_size 32 / kernel_stride 16 summaries of the keys, block_size 64,
+ * topk, init_blocks, local_blocks).  The pages name these parameters only;
+ * each step below is the plain reading stated beside it.
+ *
+ *  1. Compressed keys.  Window j of a sequence covers keys
+ *     [j*stride, j*stride + ksize); windows exist while they fit inside the
+ *     sequence.  Its summary is the mean of its ksize keys (per kv head) --
+ *     the weight-free form of a learned summary -- rounded to bf16, the
+ *     precision in which the kernel takes the selection decision.
+ *  2. Compressed attention.  Row (token i, q head h) sees window j when the
+ *     whole window lies in its causal past: j*stride + ksize - 1 <= i + S_k -
+ *     S_q.  p_j = softmax over the visible windows of scale * <q, c_j>; a row
+ *     with no visible window has p = 0.
+ *  3. Block importance.  Each window's probability is spread evenly over its
+ *     keys; block b (keys [b*bs, b*bs + bs)) collects the mass of its keys,
+ *     summed over the q heads of the kv head's group (the list is shared by
+ *     the group):  I[b] = sum_h sum_j p_hj * |window j n block b| / ksize.
+ *  4. Selection (the init / local vocabulary of the quick start).  With
+ *     qb = floor((i + S_k - S_q) / bs) (no list when negative): blocks
+ *     0 .. init-1 (those <= qb), then the local blocks qb, qb-1, ... (local
+ *     of them, >= 0, not yet listed), truncated to topk; the remaining slots
+ *     take the candidates b in [init, qb - local + 1) of largest I[b], ties
+ *     to the smaller b, listed by decreasing importance; -1 pads the rest.
+ *
+ * q [total_q, Hq, d], k [total_k, Hkv, d] bf16; tokens / ntok as above.
+ * blk_idx [ntok, Hkv, topk] int32.  scores: NULL, or [ntok, Hkv, nb_max]
+ * fp64 receiving I (0 beyond the sequence's blocks), nb_max =
+ * ceil(max S_k / bs).
+ */
+static uint16_t round_bf16(double x) {
+    float f = (float)x;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+int oracle_block_select(const uint16_t* q, const uint16_t* k, const int32_t* cu_q,
+                        const int32_t* cu_k, int32_t batch, int32_t Hq, int32_t Hkv, int32_t d,
+                        int32_t ksize, int32_t stride, int32_t bs, int32_t topk, int32_t init,
+                        int32_t local, double scale, const int64_t* tokens, int64_t ntok,
+                        int32_t* blk_idx, double* scores) {
+    if (batch < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || ksize <= 0 ||
+        stride <= 0 || bs <= 0 || topk <= 0 || init < 0 || local < 0)
+        return -1;
+    const int G = Hq / Hkv;
+    const int64_t total_q = cu_q[batch];
+    if (tokens == NULL && ntok != total_q) return -1;
+    int64_t max_sk = 0;
+    for (int b = 0; b < batch; ++b)
+        if (cu_k[b + 1] - cu_k[b] > max_sk) max_sk = cu_k[b + 1] - cu_k[b];
+    const int64_t nb_max = (max_sk + bs - 1) / bs;
+    const int64_t ncmp_max = max_sk >= ksize ? (max_sk - ksize) / stride + 1 : 0;
+
+    /* step 1: compressed keys of every sequence, [batch][ncmp_max][Hkv][d] */
+    uint16_t* cmp = (uint16_t*)calloc((size_t)(batch * ncmp_max * Hkv * d) + 1, sizeof(uint16_t));
+    if (cmp == NULL) return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < batch; ++b)
+        for (int64_t j = 0; j < ncmp_max; ++j) {
+            const int64_t Sk = cu_k[b + 1] - cu_k[b];
+            const int64_t ncmp = Sk >= ksize ? (Sk - ksize) / stride + 1 : 0;
+            if (j >= ncmp) continue;
+            for (int g = 0; g < Hkv; ++g)
+                for (int c = 0; c < d; ++c) {
+                    double sum = 0.0;
+                    for (int r = 0; r < ksize; ++r)
+                        sum += widen_bf16(k[((cu_k[b] + j * stride + r) * Hkv + g) * (int64_t)d + c]);
+                    cmp[(((int64_t)b * ncmp_max + j) * Hkv + g) * d + c] = round_bf16(sum / ksize);
+                }
+        }
+
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)(ncmp_max + 1));
+        double* imp = (double*)malloc(sizeof(double) * (size_t)(nb_max + 1));
+        char* used = (char*)malloc((size_t)(nb_max + 1));
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < ntok; ++r) {
+            const int64_t t = tokens ? tokens[r] : r;
+            if (t < 0 || t >= total_q) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            int b = 0;
+            while (b + 1 < batch && cu_q[b + 1] <= t) ++b;
+            const int64_t i = t - cu_q[b];
+            const int64_t Sq = cu_q[b + 1] - cu_q[b];
+            const int64_t Sk = cu_k[b + 1] - cu_k[b];
+            const int64_t c = i + Sk - Sq;                    /* aligned key position */
+            const int64_t nblk = (Sk + bs - 1) / bs;
+            const int64_t ncmp = Sk >= ksize ? (Sk - ksize) / stride + 1 : 0;
+            int64_t nvis = 0;                                 /* visible windows: 0 .. nvis-1 */
+            if (c - ksize + 1 >= 0) nvis = (c - ksize + 1) / stride + 1;
+            if (nvis > ncmp) nvis = ncmp;
+            for (int g = 0; g < Hkv; ++g) {
+                for (int64_t x = 0; x < nblk; ++x) imp[x] = 0.0;
+                for (int hh = 0; hh < G && nvis > 0; ++hh) {
+                    const int h = g * G + hh;
+                    const uint16_t* qr = q + (t * Hq + h) * (int64_t)d;
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < nvis; ++j) {              /* step 2 */
+                        const uint16_t* cj = cmp + (((int64_t)b * ncmp_max + j) * Hkv + g) * d;
+                        double dot = 0.0;
+                        for (int e = 0; e < d; ++e) dot += widen_bf16(qr[e]) * widen_bf16(cj[e]);
+                        p[j] = scale * dot;
+                        if (p[j] > m) m = p[j];
+                    }
+                    double l = 0.0;
+                    for (int64_t j = 0; j < nvis; ++j) {
+                        p[j] = exp(p[j] - m);
+                        l += p[j];
+                    }
+                    for (int64_t j = 0; j < nvis; ++j) {              /* step 3 */
+                        const int64_t k0 = j * stride, k1 = j * stride + ksize;
+                        for (int64_t x = k0 / bs; x * bs < k1 && x < nblk; ++x) {
+                            const int64_t lo = k0 > x * bs ? k0 : x * bs;
+                            const int64_t hi = k1 < x * bs + bs ? k1 : x * bs + bs;
+                            imp[x] += (p[j] / l) * (double)(hi - lo) / ksize;
+                        }
+                    }
+                }
+                if (scores != NULL)
+                    for (int64_t x = 0; x < nb_max; ++x)
+                        scores[(r * Hkv + g) * nb_max + x] = x < nblk ? imp[x] : 0.0;
+                /* step 4 */
+                int32_t* out = blk_idx + (r * Hkv + g) * (int64_t)topk;
+                for (int e = 0; e < topk; ++e) out[e] = -1;
+                if (c < 0) continue;
+                const int64_t qb = c / bs < nblk - 1 ? c / bs : nblk - 1;
+                for (int64_t x = 0; x < nblk; ++x) used[x] = 0;
+                int n = 0;
+                for (int64_t x = 0; x < init && x <= qb && n < topk; ++x) {
+                    out[n++] = (int32_t)x;
+                    used[x] = 1;
+                }
+                for (int64_t y = 0; y < local && n < topk; ++y) {
+                    const int64_t x = qb - y;
+                    if (x < 0) break;
+                    if (used[x]) continue;
+                    out[n++] = (int32_t)x;
+                    used[x] = 1;
+                }
+                const int64_t lo = init, hi = qb - local + 1;
+                while (n < topk) {
+                    int64_t best = -1;
+                    for (int64_t x = lo; x < hi; ++x) {
+                        if (used[x]) continue;
+                        if (best < 0 || imp[x] > imp[best]) best = x;   /* ties: smaller x */
+                    }
+                    if (best < 0) break;
+                    out[n++] = (int32_t)best;
+                    used[best] = 1;
+                }
+            }
+        }
+        free(p);
+        free(imp);
+        free(used);
+    }
+    free(cmp);
+    return bad ? -1 : 0;
+}
+
+/*
  * Merge n partial results (lse_parts[n], o_parts[n, d]) of one row computed on
  * disjoint key subsets.  An empty part carries LSE = -inf and adds nothing.
  */

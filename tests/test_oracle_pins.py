@@ -685,3 +685,172 @@ def test_bwd_gqa_equals_summed_mha():
     assert np.allclose(dq, dq2, atol=1e-12)
     assert np.allclose(dk, dk2.reshape(S, hkv, G, d).sum(2), atol=1e-12)
     assert np.allclose(dv, dv2.reshape(S, hkv, G, d).sum(2), atol=1e-12)
+
+
+# ------------------------------------------------------------------ block-index producer
+# Pins for oracle.block_select (compressed keys -> compressed attention -> block
+# importance -> top-k with forced init / local blocks; the readings are stated
+# in oracle/fsa_oracle.c).
+
+def _rows_positions(cu_q, cu_k):
+    """(token, aligned key position, S_k) for every query token."""
+    out = []
+    for b in range(len(cu_q) - 1):
+        sq, sk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        for i in range(sq):
+            out.append((cu_q[b] + i, i + sk - sq, sk))
+    return out
+
+
+def test_block_select_uniform_scores_follow_key_coverage():
+    """q = 0: every visible window is equally likely, so a block's importance is
+    G / (ksize * nvis) times the number of (visible window, key) incidences on
+    its keys -- counted here key by key -- and the picks follow from sorting
+    those counts (ties to the smaller block)."""
+    G, Hkv, d, ks, st, bs, topk = 3, 2, 16, 32, 16, 64, 6
+    S = 700
+    q = torch.zeros((S, G * Hkv, d), dtype=torch.bfloat16)
+    k = rand_bf16((S, Hkv, d), 11)
+    cu = np.array([0, S], dtype=np.int32)
+    lists, sc = oracle.block_select(q, k, cu, cu, ks, st, bs, topk, 1, 2, with_scores=True)
+    nblk = (S + bs - 1) // bs
+    for t, c, sk in _rows_positions(cu, cu):
+        nvis = (c - ks + 1) // st + 1 if c - ks + 1 >= 0 else 0
+        cover = np.zeros(sk)
+        for j in range(nvis):
+            cover[j * st:j * st + ks] += 1
+        want = np.zeros(nblk)
+        if nvis:
+            for x in range(sk):
+                want[x // bs] += cover[x]
+            want *= G / (ks * nvis)
+        np.testing.assert_allclose(sc[t, 0, :nblk], want, rtol=1e-12, atol=1e-15)
+        # expected list: forced, then candidates by (-importance, block)
+        qb = c // bs
+        forced = [0] + [x for x in (qb, qb - 1) if x > 0]
+        forced = list(dict.fromkeys(forced))[:topk]
+        cand = [x for x in range(1, qb - 1) if x not in forced]
+        cand.sort(key=lambda x: (-want[x], x))
+        exp = (forced + cand)[:topk]
+        exp += [-1] * (topk - len(exp))
+        assert lists[t, 0].tolist() == exp and lists[t, 1].tolist() == exp, (t, lists[t, 0], exp)
+
+
+def test_block_select_unit_windows_equal_dense_causal_attention():
+    """ksize = stride = 1: every key is its own window (its summary is the key
+    itself, already bf16), so a block's importance is the causal softmax mass
+    of its keys summed over the group -- checked against torch softmax in
+    float64 with a bottom-right causal mask."""
+    G, Hkv, d, bs = 2, 2, 32, 8
+    Sq, Sk = 40, 56
+    q = rand_bf16((Sq, G * Hkv, d), 21)
+    k = rand_bf16((Sk, Hkv, d), 22)
+    cu_q = np.array([0, Sq], dtype=np.int32)
+    cu_k = np.array([0, Sk], dtype=np.int32)
+    _, sc = oracle.block_select(q, k, cu_q, cu_k, 1, 1, bs, 4, 1, 2, with_scores=True)
+    qq, kk = q.to(torch.float64), k.to(torch.float64).repeat_interleave(G, dim=1)
+    s = torch.einsum("qhd,khd->hqk", qq, kk) / math.sqrt(d)
+    mask = torch.arange(Sk)[None, :] <= (torch.arange(Sq)[:, None] + Sk - Sq)
+    p = torch.softmax(s.masked_fill(~mask, float("-inf")), dim=-1)          # [Hq, Sq, Sk]
+    nblk = Sk // bs
+    mass = p.reshape(Hkv, G, Sq, nblk, bs).sum(dim=(1, 4)).permute(1, 0, 2)  # [Sq, Hkv, nblk]
+    np.testing.assert_allclose(sc, mass.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_block_select_window_means_closed_form():
+    """ksize = stride = block = 2 with key coordinate 0 set to r / 8 and q = e0:
+    window j's summary is (4j + 1) / 16 exactly, so p_j is the softmax of
+    scale * (4j + 1) / 16 over the visible windows and block j gets p_j."""
+    d, S = 8, 24
+    kf = np.zeros((S, 1, d), dtype=np.float32)
+    kf[:, 0, 0] = np.arange(S) / 8.0
+    k = bf16(kf)
+    qf = np.zeros((S, 1, d), dtype=np.float32)
+    qf[:, 0, 0] = 1.0
+    q = bf16(qf)
+    cu = np.array([0, S], dtype=np.int32)
+    scale = 0.75
+    _, sc = oracle.block_select(q, k, cu, cu, 2, 2, 2, 3, 1, 1, softmax_scale=scale, with_scores=True)
+    for i in range(S):
+        nvis = (i - 1) // 2 + 1 if i >= 1 else 0
+        want = np.zeros(S // 2)
+        if nvis:
+            z = scale * (4 * np.arange(nvis) + 1) / 16.0
+            e = np.exp(z - z.max())
+            want[:nvis] = e / e.sum()
+        np.testing.assert_allclose(sc[i, 0], want, rtol=1e-12, atol=1e-15)
+
+
+def test_block_select_mass_is_one_per_head_and_picks_are_top_scores():
+    """Random inputs: importances sum to G per (token, kv head) once a window is
+    visible (each window's mass is spread over keys that all lie in blocks);
+    the forced prefix is the input generator's rule; the other picks are the
+    largest importances among the candidates, in decreasing order."""
+    G, Hkv, d, topk = 4, 2, 32, 7
+    seqs = (513, 300)
+    cu = np.array([0, seqs[0], sum(seqs)], dtype=np.int32)
+    q = rand_bf16((sum(seqs), G * Hkv, d), 31)
+    k = rand_bf16((sum(seqs), Hkv, d), 32)
+    lists, sc = oracle.block_select(q, k, cu, cu, 32, 16, 64, topk, 1, 2, with_scores=True)
+    ref_forced = inputs_forced(seqs, Hkv, topk)
+    for t, c, sk in _rows_positions(cu, cu):
+        nvis = (c - 31) // 16 + 1 if c >= 31 else 0
+        for g in range(Hkv):
+            tot = sc[t, g].sum()
+            assert abs(tot - (G if nvis else 0.0)) < 1e-9, (t, g, tot)
+            row = [x for x in lists[t, g].tolist() if x >= 0]
+            nf = len(ref_forced[t])
+            assert row[:nf] == ref_forced[t], (t, row, ref_forced[t])
+            qb = c // 64
+            cand = set(range(1, qb - 1)) - set(row[:nf])
+            picked = row[nf:]
+            assert len(picked) == min(topk - nf, len(cand))
+            assert set(picked) <= cand
+            rest = cand - set(picked)
+            if picked and rest:
+                assert min(sc[t, g, x] for x in picked) >= max(sc[t, g, x] for x in rest)
+            assert all(sc[t, g, a] >= sc[t, g, b] for a, b in zip(picked, picked[1:]))
+
+
+def inputs_forced(seqs, hkv, topk):
+    """Forced prefix (init 1, local 2) per token from the input generator."""
+    from top_block_sparse_amd import inputs
+    lists = inputs.select_block_lists(seqs, seqs, hkv, 64, topk, 1, 2, "uniform",
+                                      np.random.default_rng(0))
+    out = []
+    base = 0
+    for s in seqs:
+        for i in range(s):
+            qb = i // 64
+            nf = len(dict.fromkeys([x for x in [0, qb, qb - 1] if x >= 0]))
+            out.append(lists[base + i, 0, :min(nf, topk)].tolist())
+        base += s
+    return out
+
+
+def test_block_select_planted_block_is_picked_first():
+    """Keys of one block aligned with every query make its windows dominate:
+    it is the first pick after the forced blocks wherever it is a candidate."""
+    G, Hkv, d, S, star = 2, 1, 32, 640, 4
+    qf = np.zeros((S, G, d), dtype=np.float32)
+    qf[:, :, 0] = 1.0
+    qf += 0.01 * np.random.default_rng(5).standard_normal(qf.shape)
+    kf = 0.1 * np.random.default_rng(6).standard_normal((S, Hkv, d)).astype(np.float32)
+    kf[star * 64:(star + 1) * 64, :, 0] = 8.0
+    q, k = bf16(qf), bf16(kf)
+    cu = np.array([0, S], dtype=np.int32)
+    lists = oracle.block_select(q, k, cu, cu, 32, 16, 64, 5, 1, 2)
+    for i in range(S):
+        qb = i // 64
+        if 1 <= star < qb - 1:
+            assert lists[i, 0, 3] == star, (i, lists[i, 0])
+
+
+def test_block_select_rejects_bad_arguments():
+    q = torch.zeros((4, 2, 8), dtype=torch.bfloat16)
+    k = torch.zeros((4, 1, 8), dtype=torch.bfloat16)
+    cu = np.array([0, 4], dtype=np.int32)
+    for kw in ({"kernel_size": 0}, {"kernel_stride": 0}, {"block_size": 0}, {"topk": 0},
+               {"init_blocks": -1}, {"local_blocks": -1}):
+        with pytest.raises(ValueError):
+            oracle.block_select(q, k, cu, cu, **kw)
