@@ -251,6 +251,53 @@ fsa_status_t fsa_topk_decode_fp8(const void* q, const void* k_cache, const void*
                                  float softmax_scale, int32_t num_splits, void* workspace,
                                  size_t workspace_bytes, void* out, float* lse, void* stream);
 
+/*
+ * Block-index producer: the lists fsa_selected_attn_fwd reads, from a
+ * compressed view of the keys (FSA page, quick start: kernel_size 32,
+ * kernel_stride 16, block_size 64, topk, init_blocks 1, local_blocks 2; the
+ * page gives the parameters, the steps below are the reading this library
+ * takes):
+ *   1. window j of a sequence covers keys [16j, 16j + 32) (windows that fit
+ *      in the sequence); its summary c_j is the mean of those keys per kv
+ *      head, rounded to bf16;
+ *   2. row (token i, q head h) sees window j when 16j + 31 <= i + S_k - S_q
+ *      (the whole window in its causal past); p_j = softmax of
+ *      softmax_scale * <q, c_j> over the visible windows;
+ *   3. block b (keys [64b, 64b + 64)) scores the probability mass of its keys,
+ *      each window's p_j spread evenly over its 32 keys, summed over the q
+ *      heads of the kv head's group;
+ *   4. with qb = floor((i + S_k - S_q) / 64): blocks 0 .. init_blocks-1 (those
+ *      <= qb), then the local blocks qb, qb-1, ... (local_blocks of them,
+ *      >= 0, not yet listed), then the blocks in [init_blocks, qb -
+ *      local_blocks + 1) of highest score (ties to the smaller id), in
+ *      decreasing score order; -1 pads.  A row with qb < 0 gets all -1.
+ *
+ *   q        bf16 [total_q, num_heads_q, head_dim], 16-byte aligned
+ *   k        bf16 [total_k, num_heads_kv, head_dim], 16-byte aligned
+ *   cu_seqlens_q/k, batch, total_q/k, max_seqlen_q/k, head counts, head_dim
+ *            (64 or 128), softmax_scale (<= 0: 1/sqrt(head_dim)): as in
+ *            fsa_selected_attn_fwd; max_seqlen_k must bound every S_k
+ *   kernel_size, kernel_stride, block_size  32, 16, 64 (others:
+ *            FSA_ERROR_NOT_SUPPORTED)
+ *   topk     1..64; init_blocks, local_blocks >= 0
+ *            (num_heads_q / num_heads_kv <= 64)
+ *   workspace at least fsa_block_select_workspace_size(...) bytes (the
+ *            compressed keys), 16-byte aligned; may be NULL when that is 0
+ *   blk_idx  int32 [total_q, num_heads_kv, topk], written
+ * Scores are accumulated in fp32 in an order that can vary between calls, so
+ * blocks whose scores tie to rounding may swap places.
+ */
+size_t fsa_block_select_workspace_size(int32_t batch, int32_t max_seqlen_k, int32_t num_heads_kv,
+                                       int32_t head_dim, int32_t kernel_size, int32_t kernel_stride);
+fsa_status_t fsa_block_select(const void* q, const void* k, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int32_t batch, int64_t total_q,
+                              int64_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                              int32_t kernel_size, int32_t kernel_stride, int32_t block_size,
+                              int32_t topk, int32_t init_blocks, int32_t local_blocks,
+                              float softmax_scale, void* workspace, size_t workspace_bytes,
+                              int32_t* blk_idx, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

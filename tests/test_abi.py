@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     assert sorted(names) == sorted(_lib.EXPORTS)
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
@@ -252,3 +252,42 @@ def test_bwd_workspace(lib):
                  + 16384 * 8 * 2 * 128 * 4)
     assert f(2, 16384, 16384, 8192, 8192, 32, 8, 96, 64, 16) == 0
     assert bwd(lib, batch=0, q=None) == 0
+
+
+def select(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, cuq=FAKE, cuk=FAKE, batch=2, total_q=100, total_k=100, maxq=64,
+             maxk=64, hq=8, hkv=2, d=128, ks=32, st=16, bs=64, topk=16, init=1, local=2,
+             scale=0.0, ws=None, ws_bytes=0, out=FAKE, stream=None)
+    a.update(kw)
+    return lib.fsa_block_select(a["q"], a["k"], a["cuq"], a["cuk"], a["batch"], a["total_q"],
+                                a["total_k"], a["maxq"], a["maxk"], a["hq"], a["hkv"], a["d"],
+                                a["ks"], a["st"], a["bs"], a["topk"], a["init"], a["local"],
+                                a["scale"], a["ws"], a["ws_bytes"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=6, hkv=4), INVALID),
+    (dict(d=96), NOT_SUPPORTED),
+    (dict(ks=64), NOT_SUPPORTED),
+    (dict(st=32), NOT_SUPPORTED),
+    (dict(bs=32), NOT_SUPPORTED),
+    (dict(topk=0), INVALID),
+    (dict(topk=65), NOT_SUPPORTED),
+    (dict(init=-1), INVALID),
+    (dict(local=-1), INVALID),
+    (dict(hq=256, hkv=2), NOT_SUPPORTED),      # group above 64
+    (dict(out=None), INVALID),
+    (dict(q=FAKE + 4), INVALID),                # 16-byte alignment
+    (dict(ws=None), WORKSPACE),                 # compressed keys need room
+    (dict(ws=FAKE, ws_bytes=16), WORKSPACE),
+])
+def test_block_select_argument_errors(lib, kw, code):
+    assert select(lib, **kw) == code
+
+
+def test_block_select_workspace(lib):
+    f = lib.fsa_block_select_workspace_size
+    assert f(2, 8192, 8, 128, 32, 16) >= 2 * 511 * 8 * 128 * 2
+    assert f(2, 31, 8, 128, 32, 16) == 0           # no window fits
+    assert f(2, 8192, 8, 96, 32, 16) == 0
+    assert select(lib, batch=0, q=None) == 0

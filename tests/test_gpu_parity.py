@@ -544,3 +544,126 @@ def test_bwd_medium_gqa_workload():
     ref = oracle.selected_attn_bwd(dd["q"], dd["k"], dd["v"], do, dd["blk_idx"],
                                    dd["cu_seqlens_q"], dd["cu_seqlens_k"], 64)
     compare_grads(got, ref, what="medium")
+
+
+# ------------------------------------------------------------------ block-index producer
+# The lists are integers decided by floating point: the GPU scores blocks in
+# fp32 (MFMA over the same bf16 compressed keys the oracle rounds to), the
+# oracle in fp64.  So the forced blocks and the number of entries must match
+# exactly, and the other picks must be a valid top set under the oracle's
+# scores: each picked block scores at least every candidate left out, and the
+# picks come in non-increasing score order, both up to SEL_TOL (block scores
+# lie in [0, G]; fp32 scores differ from fp64 by ~1e-6 of G).
+SEL_TOL = 2e-5
+
+
+def run_select(dd, topk, init=1, local=2, hq=None):
+    g = to_dev(dd, ("q", "k", "cu_seqlens_q", "cu_seqlens_k"))
+    out = fsa.fsa_block_select(g["q"], g["k"], g["cu_seqlens_q"], g["cu_seqlens_k"],
+                               dd["max_seqlen_q"], dd["max_seqlen_k"], topk=topk,
+                               init_blocks=init, local_blocks=local)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_select(got, ref, sc, cu_q, cu_k, tokens, init, local, G, what=""):
+    """got/ref/sc rows are indexed like ``tokens`` (got: full [total_q, ...])."""
+    exact = 0
+    for r, t in enumerate(tokens):
+        b = int(np.searchsorted(cu_q, t, side="right") - 1)
+        i = t - cu_q[b]
+        c = i + (cu_k[b + 1] - cu_k[b]) - (cu_q[b + 1] - cu_q[b])
+        for g in range(ref.shape[1]):
+            gr, rr = got[t, g].tolist(), ref[r, g].tolist()
+            nv = sum(x >= 0 for x in rr)
+            assert sum(x >= 0 for x in gr) == nv and all(x < 0 for x in gr[nv:]), (what, t, g, gr, rr)
+            if gr == rr:
+                exact += 1
+                continue
+            qb = c // 64
+            nf = len(dict.fromkeys([x for x in list(range(min(init, qb + 1)))
+                                    + [qb - y for y in range(local)] if x >= 0]))
+            nf = min(nf, len(rr))
+            assert gr[:nf] == rr[:nf], (what, t, g, gr, rr)
+            cand = set(range(init, qb - local + 1)) - set(rr[:nf])
+            picked = gr[nf:nv]
+            assert len(set(picked)) == len(picked) and set(picked) <= cand, (what, t, g, gr)
+            s = sc[r, g]
+            rest = cand - set(picked)
+            if picked and rest:
+                assert min(s[x] for x in picked) >= max(s[x] for x in rest) - SEL_TOL * G, (what, t, g)
+            for a_, b_ in zip(picked, picked[1:]):
+                assert s[a_] >= s[b_] - SEL_TOL * G, (what, t, g)
+    return exact
+
+
+SELECT_SHAPES = [
+    # seqlens_q, seqlens_k (None = same), hq, hkv, d, topk, init, local
+    ((1024,), None, 4, 1, 64, 4, 1, 2),
+    ((1024,), None, 4, 1, 64, 16, 1, 2),
+    ((700, 333), None, 3, 1, 128, 8, 1, 2),
+    ((600,), (1500,), 8, 2, 128, 16, 1, 2),            # S_q < S_k (bottom-right)
+    ((517, 20, 0, 300), None, 16, 1, 64, 16, 2, 3),    # a sequence with no window, an empty one
+    ((1100,), None, 2, 2, 128, 12, 0, 0),              # no forced blocks
+    ((2048,), None, 64, 1, 64, 32, 1, 2),              # group of 64 (one token per tile)
+]
+
+
+@pytest.mark.parametrize("case", range(len(SELECT_SHAPES)))
+def test_block_select_shapes(case):
+    sq, sk, hq, hkv, d, topk, init, local = SELECT_SHAPES[case]
+    spec = inputs.PrefillSpec(f"sel{case}", tuple(sq), hq, hkv, d, topk, seed=70 + case,
+                              seqlens_k=None if sk is None else tuple(sk))
+    dd = inputs.make_prefill(spec)
+    got = run_select(dd, topk, init, local)
+    ref, sc = oracle.block_select(dd["q"], dd["k"], dd["cu_seqlens_q"], dd["cu_seqlens_k"],
+                                  topk=topk, init_blocks=init, local_blocks=local, with_scores=True)
+    cu_q, cu_k = dd["cu_seqlens_q"].numpy(), dd["cu_seqlens_k"].numpy()
+    toks = np.arange(int(cu_q[-1]))
+    exact = check_select(got, ref, sc, cu_q, cu_k, toks, init, local, hq // hkv, f"case {case}")
+    assert exact >= 0.97 * toks.size * hkv, exact
+
+
+def test_block_select_uniform_scores():
+    """q = 0: every block of equal coverage ties; only validity is unique."""
+    spec = inputs.PrefillSpec("selq0", (900,), 4, 2, 64, 8, seed=90)
+    dd = inputs.make_prefill(spec)
+    dd["q"] = torch.zeros_like(dd["q"])
+    got = run_select(dd, 8)
+    ref, sc = oracle.block_select(dd["q"], dd["k"], dd["cu_seqlens_q"], dd["cu_seqlens_k"],
+                                  topk=8, with_scores=True)
+    check_select(got, ref, sc, dd["cu_seqlens_q"].numpy(), dd["cu_seqlens_k"].numpy(),
+                 np.arange(900), 1, 2, 2, "q=0")
+
+
+def test_block_select_planted_block():
+    """One block's keys aligned with every query: it is the first free pick."""
+    S, star = 1280, 6
+    spec = inputs.PrefillSpec("selstar", (S,), 4, 1, 128, 6, seed=91)
+    dd = inputs.make_prefill(spec)
+    q = dd["q"].float() * 0.05
+    q[:, :, 0] = 1.0
+    k = dd["k"].float() * 0.1
+    k[star * 64:(star + 1) * 64, :, 0] = 6.0
+    dd["q"], dd["k"] = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    got = run_select(dd, 6)
+    for i in range(S):
+        qb = i // 64
+        if 1 <= star < qb - 1:
+            assert got[i, 0, 3] == star, (i, got[i, 0])
+
+
+@pytest.mark.parametrize("name", ["prefill_b2_s8192_h32_kv8_d128_top16",
+                                  "long_s131072_h64_kv4_d128_top32_zipf"])
+def test_block_select_full_size(name):
+    """Full-size workloads, sampled tokens against the oracle."""
+    spec = inputs.PREFILL_WORKLOADS[name]
+    dd = inputs.make_prefill(spec)
+    got = run_select(dd, spec.topk)
+    cu_q = dd["cu_seqlens_q"].numpy()
+    toks = sample_tokens(cu_q, 300 if spec.seqlens[0] <= 8192 else 60, 17)
+    ref, sc = oracle.block_select(dd["q"], dd["k"], dd["cu_seqlens_q"], dd["cu_seqlens_k"],
+                                  topk=spec.topk, tokens=toks, with_scores=True)
+    exact = check_select(got, ref, sc, cu_q, dd["cu_seqlens_k"].numpy(), toks, 1, 2,
+                         spec.num_heads_q // spec.num_heads_kv, name)
+    assert exact >= 0.95 * toks.size * spec.num_heads_kv, exact

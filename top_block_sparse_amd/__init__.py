@@ -10,6 +10,8 @@ call through the binding loads the library and raises if it is not built.
 from ._lib import (  # noqa: F401
     FsaError,
     fsa_abi_version,
+    fsa_block_select,
+    fsa_block_select_workspace_size,
     fsa_selected_attn_bwd,
     fsa_selected_attn_bwd_workspace_size,
     fsa_selected_attn_fwd,
@@ -24,7 +26,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "FsaError", "fsa_abi_version", "fsa_selected_attn_bwd", "fsa_selected_attn_bwd_workspace_size",
+    "FsaError", "fsa_abi_version", "fsa_block_select", "fsa_block_select_workspace_size",
+    "fsa_selected_attn_bwd", "fsa_selected_attn_bwd_workspace_size",
     "fsa_selected_attn_fwd",
     "fsa_selected_attn_fwd_workspace_size", "fsa_sliding_window_fwd",
     "fsa_sliding_window_fwd_workspace_size", "fsa_status_string", "fsa_topk_decode",

@@ -28,7 +28,8 @@ EXPORTS = ("fsa_status_string", "fsa_abi_version", "fsa_selected_attn_fwd_worksp
            "fsa_selected_attn_fwd", "fsa_topk_decode_workspace_size",
            "fsa_topk_decode_auto_splits", "fsa_topk_decode", "fsa_topk_decode_fp8",
            "fsa_sliding_window_fwd_workspace_size", "fsa_sliding_window_fwd",
-           "fsa_selected_attn_bwd_workspace_size", "fsa_selected_attn_bwd")
+           "fsa_selected_attn_bwd_workspace_size", "fsa_selected_attn_bwd",
+           "fsa_block_select_workspace_size", "fsa_block_select")
 
 _lib = None
 
@@ -80,6 +81,11 @@ def load() -> ctypes.CDLL:
     lib.fsa_topk_decode.restype = ctypes.c_int
     lib.fsa_topk_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f32,
                                     i32, P, sz, P, P, P]
+    lib.fsa_block_select_workspace_size.restype = sz
+    lib.fsa_block_select_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.fsa_block_select.restype = ctypes.c_int
+    lib.fsa_block_select.argtypes = [P, P, P, P, i32, i64, i64, i32, i32, i32, i32, i32, i32, i32,
+                                     i32, i32, i32, i32, f32, P, sz, P, P]
     _lib = lib
     return lib
 
@@ -355,3 +361,50 @@ def fsa_topk_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.T
 
 def default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
+
+
+def fsa_block_select_workspace_size(batch: int, max_seqlen_k: int, num_heads_kv: int,
+                                    head_dim: int, kernel_size: int = 32,
+                                    kernel_stride: int = 16) -> int:
+    return int(load().fsa_block_select_workspace_size(batch, max_seqlen_k, num_heads_kv, head_dim,
+                                                      kernel_size, kernel_stride))
+
+
+def fsa_block_select(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                     cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                     topk: int = 16, kernel_size: int = 32, kernel_stride: int = 16,
+                     block_size: int = 64, init_blocks: int = 1, local_blocks: int = 2,
+                     softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block lists ``int32 [total_q, Hkv, topk]`` for ``fsa_selected_attn_fwd``
+    from compressed attention over mean-pooled key windows (include/fsa.h)."""
+    lib = load()
+    _check_dev("q", q, torch.bfloat16, 3)
+    _check_dev("k", k, torch.bfloat16, 3)
+    _check_dev("cu_seqlens_q", cu_seqlens_q, torch.int32, 1)
+    _check_dev("cu_seqlens_k", cu_seqlens_k, torch.int32, 1)
+    total_q, hq, d = q.shape
+    total_k, hkv, dk = k.shape
+    if dk != d:
+        raise ValueError("q and k must share head_dim")
+    batch = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty((total_q, hkv, topk), dtype=torch.int32, device=q.device)
+    else:
+        _check_dev("out", out, torch.int32, 3)
+        if tuple(out.shape) != (total_q, hkv, topk):
+            raise ValueError("out must be [total_q, Hkv, topk]")
+    need = lib.fsa_block_select_workspace_size(batch, max_seqlen_k, hkv, d, kernel_size,
+                                               kernel_stride)
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = lib.fsa_block_select(_ptr(q), _ptr(k), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch,
+                              total_q, total_k, max_seqlen_q, max_seqlen_k, hq, hkv, d,
+                              kernel_size, kernel_stride, block_size, topk, init_blocks,
+                              local_blocks, scale, _ptr(workspace), ws_bytes, _ptr(out),
+                              _stream(q.device))
+    if st != FSA_SUCCESS:
+        raise FsaError(st, "fsa_block_select")
+    return out

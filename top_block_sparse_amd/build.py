@@ -14,7 +14,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libfsa.so")
-SOURCES = ["fsa_api.hip", "sel_attn_fwd.hip", "sel_attn_bwd.hip", "topk_decode.hip", "lse_merge.hip"]
+SOURCES = ["fsa_api.hip", "sel_attn_fwd.hip", "sel_attn_bwd.hip", "topk_decode.hip", "lse_merge.hip",
+           "block_select.hip"]
 # The prefill kernel never produces or tests NaNs (masked scores are -inf,
 # which stays honoured), so fmax there compiles to a single instruction.
 EXTRA_FLAGS = {"sel_attn_fwd.hip": ["-fno-honor-nans"]}

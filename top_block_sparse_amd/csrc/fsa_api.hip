@@ -120,6 +120,46 @@ DecodeLayout decode_layout(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, in
 
 float resolve_scale(float s, int D) { return s > 0.f ? s : 1.0f / std::sqrt((float)D); }
 
+// Block-index producer: the importance table [T][blocks] (fp32) of one tile
+// lives in LDS; T tokens times G heads fill at most 4 m-tiles of 16 rows.
+constexpr int kSelectCmpSize = 32, kSelectCmpStride = 16;
+constexpr int kMaxTopkSelect = 64;
+constexpr int kMaxGroupSelect = 64;
+constexpr size_t kSelectLdsBudget = 64 * 1024;
+
+struct SelectPlan {
+    int T, mtiles, tiles_per_seq, ncmp_max, nb_max;
+};
+
+fsa_status_t check_select(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
+                          int32_t Hkv, int32_t D, int32_t ks, int32_t stride, int32_t bs,
+                          int32_t topk, int32_t init, int32_t local) {
+    if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || Hq <= 0 || Hkv <= 0 || topk <= 0 ||
+        init < 0 || local < 0 || ks <= 0 || stride <= 0 || bs <= 0)
+        return FSA_ERROR_INVALID_VALUE;
+    if (Hq % Hkv != 0) return FSA_ERROR_INVALID_VALUE;
+    if (D != 64 && D != 128) return FSA_ERROR_NOT_SUPPORTED;
+    if (ks != kSelectCmpSize || stride != kSelectCmpStride || bs != fsa::kBlockKeys)
+        return FSA_ERROR_NOT_SUPPORTED;
+    if (topk > kMaxTopkSelect || Hq / Hkv > kMaxGroupSelect) return FSA_ERROR_NOT_SUPPORTED;
+    return FSA_SUCCESS;
+}
+
+SelectPlan plan_select(int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv) {
+    SelectPlan pl{};
+    const int G = Hq / Hkv;
+    pl.nb_max = (max_seqlen_k + fsa::kBlockKeys - 1) / fsa::kBlockKeys;
+    if (pl.nb_max < 1) pl.nb_max = 1;
+    pl.ncmp_max = max_seqlen_k >= kSelectCmpSize ? (max_seqlen_k - kSelectCmpSize) / kSelectCmpStride + 1 : 0;
+    int T = 64 / G;
+    const int t_lds = (int)(kSelectLdsBudget / ((size_t)pl.nb_max * 4));
+    T = T < t_lds ? T : t_lds;
+    pl.T = T;                                   // 0: the table does not fit
+    pl.mtiles = (T * G + 15) / 16;
+    pl.tiles_per_seq = T > 0 ? (max_seqlen_q + T - 1) / T : 0;
+    return pl;
+}
+
 }  // namespace
 
 static fsa_status_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
@@ -527,6 +567,67 @@ fsa_status_t fsa_selected_attn_bwd(const void* q, const void* k, const void* v, 
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     if (fsa::launch_sel_attn_bwd(p, head_dim, s) != hipSuccess) return FSA_ERROR_LAUNCH;
+    return FSA_SUCCESS;
+}
+
+size_t fsa_block_select_workspace_size(int32_t batch, int32_t max_seqlen_k, int32_t num_heads_kv,
+                                       int32_t head_dim, int32_t kernel_size, int32_t kernel_stride) {
+    if (check_select(batch, 0, max_seqlen_k, num_heads_kv, num_heads_kv, head_dim, kernel_size,
+                     kernel_stride, fsa::kBlockKeys, 1, 0, 0) != FSA_SUCCESS)
+        return 0;
+    const SelectPlan pl = plan_select(0, max_seqlen_k, num_heads_kv, num_heads_kv);
+    return align_up((size_t)batch * pl.ncmp_max * num_heads_kv * head_dim * 2);
+}
+
+fsa_status_t fsa_block_select(const void* q, const void* k, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int32_t batch, int64_t total_q,
+                              int64_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                              int32_t kernel_size, int32_t kernel_stride, int32_t block_size,
+                              int32_t topk, int32_t init_blocks, int32_t local_blocks,
+                              float softmax_scale, void* workspace, size_t workspace_bytes,
+                              int32_t* blk_idx, void* stream) {
+    fsa_status_t st = check_select(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv,
+                                   head_dim, kernel_size, kernel_stride, block_size, topk,
+                                   init_blocks, local_blocks);
+    if (st != FSA_SUCCESS) return st;
+    if (total_q < 0 || total_k < 0) return FSA_ERROR_INVALID_VALUE;
+    if (total_q > INT32_MAX || total_k > INT32_MAX) return FSA_ERROR_NOT_SUPPORTED;
+    if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FSA_SUCCESS;   // nothing to do
+    if (!q || !k || !cu_seqlens_q || !cu_seqlens_k || !blk_idx) return FSA_ERROR_INVALID_VALUE;
+    if (!aligned16(q) || !aligned16(k)) return FSA_ERROR_INVALID_VALUE;
+    const SelectPlan pl = plan_select(max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv);
+    if (pl.T < 1) return FSA_ERROR_NOT_SUPPORTED;
+    const size_t need = fsa_block_select_workspace_size(batch, max_seqlen_k, num_heads_kv, head_dim,
+                                                        kernel_size, kernel_stride);
+    if (pl.ncmp_max > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+        return FSA_ERROR_WORKSPACE;
+
+    fsa::BlockSelectParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.cmp = static_cast<uint16_t*>(workspace);
+    p.blk_idx = blk_idx;
+    p.total_q = total_q;
+    p.total_k = total_k;
+    p.batch = batch;
+    p.Hq = num_heads_q;
+    p.Hkv = num_heads_kv;
+    p.G = num_heads_q / num_heads_kv;
+    p.topk = topk;
+    p.init = init_blocks;
+    p.local = local_blocks;
+    p.ncmp_max = pl.ncmp_max;
+    p.nb_max = pl.nb_max;
+    p.T = pl.T;
+    p.mtiles = pl.mtiles;
+    p.tiles_per_seq = pl.tiles_per_seq;
+    p.scale_log2 = resolve_scale(softmax_scale, head_dim) * fsa::kLog2e;
+    (void)hipGetLastError();
+    if (fsa::launch_block_select(p, head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return FSA_ERROR_LAUNCH;
     return FSA_SUCCESS;
 }
 

@@ -52,6 +52,22 @@ struct DecodeParams {
     float scale_log2;
 };
 
+// Block-index producer (block_select.hip).
+struct BlockSelectParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    uint16_t* cmp;          // workspace: compressed keys [batch][ncmp_max][Hkv][D] bf16
+    int32_t* blk_idx;       // [total_q][Hkv][topk]
+    int64_t total_q, total_k;
+    int batch, Hq, Hkv, G, topk, init, local;
+    int ncmp_max;           // windows of the longest sequence
+    int nb_max;             // blocks of the longest sequence
+    int T, mtiles, tiles_per_seq;
+    float scale_log2;
+};
+
 // Selected-attention backward (sel_attn_bwd.hip).
 struct SelBwdParams {
     const uint16_t* q;
@@ -105,6 +121,8 @@ size_t decode_lds_bytes(int D, int G, int ts, int topk);
 int decode_table_slots(int D, int G, int topk);
 hipError_t launch_lse_merge(const MergeParams& p, int D, hipStream_t stream);
 hipError_t launch_sel_attn_bwd(const SelBwdParams& p, int D, hipStream_t stream);
+hipError_t launch_block_select(const BlockSelectParams& p, int D, hipStream_t stream);
+size_t block_select_lds_bytes(int T, int nb_max);
 int sel_attn_bwd_rows_per_tile();   // query rows (T*G) one dq workgroup covers
 int sel_attn_bwd_index_chunk();     // tokens one index workgroup covers
 size_t sel_attn_bwd_dq_lds_bytes(int D, int T, int topk, int ring);
