@@ -32,6 +32,7 @@ METRIC = "selected-attn fwd effective TFLOP/s + decode HBM GB/s, % roofline (1 G
 PREFILL = "prefill_b2_s8192_h32_kv8_d128_top16"
 DECODE = "decode_b32_h32_kv8_d128_L32768_p256_top2048"
 WINDOW_WL = "sliding_window_512_b2_s8192_h32_kv8_d128"
+SELECT_WL = "block_select_b2_s8192_h32_kv8_d128_top16"   # lists for the prefill workload
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -71,7 +72,7 @@ def main():
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=("full", "prefill", "decode", "decode_fp8", "window",
-                                       "backward", "copy"),
+                                       "backward", "select", "copy"),
                     default="full",
                     help="profiling runs: launch only one kernel family (or a plain 1 GiB "
                          "device copy used to calibrate HBM byte counters) --steps times, "
@@ -107,7 +108,7 @@ def main():
         return
 
     # ---------------- inputs (generated on the host, then resident in HBM)
-    want_p = args.mode in ("full", "prefill", "window", "backward")
+    want_p = args.mode in ("full", "prefill", "window", "backward", "select")
     want_d = args.mode in ("full", "decode", "decode_fp8")
     want_f8 = args.mode in ("full", "decode_fp8")
     pspec = inputs.PREFILL_WORKLOADS[PREFILL]
@@ -173,6 +174,20 @@ def main():
                                    pg["cu_seqlens_k"], pd["max_seqlen_q"], pd["max_seqlen_k"],
                                    WINDOW - 1, 0, out=w_out, lse=p_lse)
 
+    # block-index producer: one q.c product per (query row, visible key window)
+    s_pairs = sum(max(0, (i - 31) // 16 + 1) for s_len in pspec.seqlens for i in range(s_len))
+    s_flops = 2.0 * pspec.head_dim * pspec.num_heads_q * s_pairs
+    s_out = (torch.empty((pg["q"].shape[0], pspec.num_heads_kv, pspec.topk), dtype=torch.int32,
+                         device=dev) if want_p else None)
+    s_ws = (torch.empty(max(fsa.fsa_block_select_workspace_size(
+        len(pspec.seqlens), pd["max_seqlen_k"], pspec.num_heads_kv, pspec.head_dim), 1),
+        dtype=torch.uint8, device=dev) if want_p else None)
+
+    def select():
+        fsa.fsa_block_select(pg["q"], pg["k"], pg["cu_seqlens_q"], pg["cu_seqlens_k"],
+                             pd["max_seqlen_q"], pd["max_seqlen_k"], topk=pspec.topk,
+                             out=s_out, workspace=s_ws)
+
     bwd_state = {}
 
     def backward():
@@ -208,7 +223,8 @@ def main():
 
     if args.mode != "full":
         step = {"prefill": lambda i: prefill(), "decode": decode, "decode_fp8": decode_fp8,
-                "window": lambda i: window(), "backward": lambda i: backward()}[args.mode]
+                "window": lambda i: window(), "backward": lambda i: backward(),
+                "select": lambda i: select()}[args.mode]
         for i in range(args.warmup + args.steps):
             step(i)
         torch.cuda.synchronize()
@@ -222,6 +238,7 @@ def main():
         decode_fp8(i)
         window()
         backward()
+        select()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -274,6 +291,14 @@ def main():
         b_ev[i][0].record(stream)
         backward()
         b_ev[i][1].record(stream)
+    torch.cuda.synchronize()
+
+    log(f"timing {K} block-selection calls")
+    s_ev = [(ev(), ev()) for _ in range(K)]
+    for i in range(K):
+        s_ev[i][0].record(stream)
+        select()
+        s_ev[i][1].record(stream)
     torch.cuda.synchronize()
 
     p_ms = np.array([a.elapsed_time(b) for a, b in p_ev])
@@ -333,6 +358,20 @@ def main():
                      "flops_per_call": b_flops,
                      "scope": "whole call: D prep, block index, dK/dV and dQ kernels"},
     }
+    s_ms = np.array([a.elapsed_time(b) for a, b in s_ev])
+    s_tflops = s_flops / (s_ms.mean() * 1e-3) / 1e12
+    log(f"select : mean {s_ms.mean():.3f} ms  {s_tflops:.1f} TFLOP/s (events)")
+    sel_src = os.path.join(ROOT, "top_block_sparse_amd", "csrc", "block_select.hip")
+    select_obj = {
+        "value": round(s_tflops, 2), "unit": "TFLOP/s", "workload": SELECT_WL,
+        "ms_per_call": round(float(s_ms.mean()), 4),
+        "roofline": {"bound": "mfma", "achieved": round(s_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(s_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(sel_src, SELECT_WL), "flops_per_call": s_flops,
+                     "scope": "whole call: key-window means + compressed attention, block "
+                              "importance and top-k (flops: one q.c product per row and "
+                              "visible window; the kernel runs two passes)"},
+    }
     decode_fp8_obj = {
         "value": round(f_gbs_evt, 1), "unit": "GB/s", "workload": DECODE + "_fp8_e4m3",
         "us_per_call": round(float(f_ms.mean()) * 1e3, 2),
@@ -368,6 +407,7 @@ def main():
         "decode_fp8": decode_fp8_obj,
         "sliding_window": window_obj,
         "backward": backward_obj,
+        "block_select": select_obj,
     }
 
     if not args.no_cpu_baseline:

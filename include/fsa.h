@@ -280,7 +280,7 @@ fsa_status_t fsa_topk_decode_fp8(const void* q, const void* k_cache, const void*
  *   kernel_size, kernel_stride, block_size  32, 16, 64 (others:
  *            FSA_ERROR_NOT_SUPPORTED)
  *   topk     1..64; init_blocks, local_blocks >= 0
- *            (num_heads_q / num_heads_kv <= 64)
+ *            (num_heads_q / num_heads_kv <= 128)
  *   workspace at least fsa_block_select_workspace_size(...) bytes (the
  *            compressed keys), 16-byte aligned; may be NULL when that is 0
  *   blk_idx  int32 [total_q, num_heads_kv, topk], written

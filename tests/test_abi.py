@@ -275,7 +275,7 @@ def select(lib, **kw):
     (dict(topk=65), NOT_SUPPORTED),
     (dict(init=-1), INVALID),
     (dict(local=-1), INVALID),
-    (dict(hq=256, hkv=2), NOT_SUPPORTED),      # group above 64
+    (dict(hq=512, hkv=2), NOT_SUPPORTED),      # group above 128
     (dict(out=None), INVALID),
     (dict(q=FAKE + 4), INVALID),                # 16-byte alignment
     (dict(ws=None), WORKSPACE),                 # compressed keys need room

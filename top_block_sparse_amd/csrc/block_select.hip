@@ -21,11 +21,12 @@
 // Kernels:
 //   cmp_keys_kernel   one thread per (sequence, window, kv head, 8 dims):
 //                     fp32 sum of 32 bf16 keys, times 1/32, RNE to bf16;
-//   block_select_kernel  a workgroup per (T tokens, kv head): each wave owns
-//                     one 16-row m-tile of the T*G query rows (GQA-packed
-//                     like the prefill) and runs S^T = C Q^T with
+//   block_select_kernel  a workgroup per (T tokens, kv head): each of 8 waves
+//                     owns one 16-row m-tile of the T*G query rows
+//                     (GQA-packed like the prefill) and runs S^T = C Q^T with
 //                     v_mfma_f32_16x16x32_bf16 over the visible windows in
 //                     two passes -- row max and sum, then probabilities --
+//                     from chunks of 64 window summaries staged once in LDS,
 //                     adding block masses into an LDS table [T][blocks];
 //                     then one wave per token takes the forced blocks and
 //                     picks the rest by repeated wave-wide argmax.
@@ -39,7 +40,7 @@ namespace {
 constexpr int kSelBlock = 64;          // keys per selection block
 constexpr int kCmpSize = 32;           // keys per compressed window
 constexpr int kCmpStride = 16;         // window stride
-constexpr int kSelectWaves = 4;
+constexpr int kSelectWaves = 8;
 constexpr int kSelectThreads = kSelectWaves * 64;
 constexpr int kWinChunk = 64;          // windows per MFMA chunk (4 key tiles of 16)
 
@@ -67,6 +68,42 @@ __device__ __forceinline__ uint32_t rne_bf16_bits(float x) {
     uint32_t u = __float_as_uint(x);
     u += 0x7FFFu + ((u >> 16) & 1u);
     return u >> 16;
+}
+
+// sum over aligned groups of n lanes (n = 1, 2, 4, 8 or 16) of a 16-lane row;
+// every lane of a group ends with the group's sum
+__device__ __forceinline__ float group_sum(float x, int n) {
+    if (n >= 2) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+    if (n >= 4) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+    if (n >= 8) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+    if (n >= 16) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+    return x;
+}
+
+// wave-wide maximum of a 64-bit key: DPP within each 16-lane row, then the
+// gfx950 permlane swaps across rows (all VALU; no LDS round trips)
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
+    auto pick = [](unsigned long long a, unsigned long long b) { return a > b ? a : b; };
+#define FSA_DPP_U64(v, ctrl)                                                                       \
+    ((((unsigned long long)(uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)((v) >> 32), ctrl, \
+                                                                 0xF, 0xF, false)) << 32) |       \
+     (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v), ctrl, 0xF, 0xF, false))
+    x = pick(x, FSA_DPP_U64(x, 0xB1));
+    x = pick(x, FSA_DPP_U64(x, 0x4E));
+    x = pick(x, FSA_DPP_U64(x, 0x141));
+    x = pick(x, FSA_DPP_U64(x, 0x140));
+#undef FSA_DPP_U64
+    {
+        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+        x = pick(((unsigned long long)hi[0] << 32) | lo[0], ((unsigned long long)hi[1] << 32) | lo[1]);
+    }
+    {
+        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+        x = pick(((unsigned long long)hi[0] << 32) | lo[0], ((unsigned long long)hi[1] << 32) | lo[1]);
+    }
+    return uniform_u64(x);
 }
 
 }  // namespace
@@ -108,11 +145,19 @@ __global__ void __launch_bounds__(256) cmp_keys_kernel(const BlockSelectParams p
 }
 
 // ---- 2. compressed attention, block importance and selection
+// LDS: the importance table [T][nb_max] fp32, then two buffers of one chunk
+// of 64 window summaries in MFMA A-operand order -- fragment (kt, s), 1 KiB,
+// lane l's 16 bytes = C[16kt + l%16][32s + 8(l/16) .. +8] -- so every operand
+// read is one contiguous wave read.  The chunk is loaded once per workgroup
+// (all waves share it), the next one while the current one is used.
 template <int D>
 __global__ void __launch_bounds__(kSelectThreads) block_select_kernel(const BlockSelectParams p) {
     constexpr int KS = D / 32;
+    constexpr int CPR = D / 8;                                   // 16-byte pieces per window
+    constexpr int kChunkBytes = kWinChunk * D * 2;
+    constexpr int NL = kWinChunk * CPR / kSelectThreads;         // pieces per thread per chunk
+    static_assert(NL * kSelectThreads == kWinChunk * CPR, "chunk staging");
     extern __shared__ __align__(16) uint8_t smem[];
-    float* s_imp = reinterpret_cast<float*>(smem);     // [T][nb_max]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
 
@@ -132,9 +177,10 @@ __global__ void __launch_bounds__(kSelectThreads) block_select_kernel(const Bloc
     int ncmp = n_windows(sb.Sk);
     ncmp = ncmp < p.ncmp_max ? ncmp : p.ncmp_max;
     const int G = p.G;
+    float* s_imp = reinterpret_cast<float*>(smem);                 // [T][nb]
+    uint8_t* cbuf = smem + (((size_t)p.T * nb * 4 + 15) & ~(size_t)15);
 
     for (int x = tid; x < p.T * nb; x += kSelectThreads) s_imp[x] = 0.f;
-    __syncthreads();
 
     // this wave's m-tile: row = wave*16 + lr -> (token t_l, head hh)
     const int row = wave * 16 + lr;
@@ -144,14 +190,11 @@ __global__ void __launch_bounds__(kSelectThreads) block_select_kernel(const Bloc
     int nvis = c >= kCmpSize - 1 ? (c - (kCmpSize - 1)) / kCmpStride + 1 : 0;
     nvis = nvis < ncmp ? nvis : ncmp;
     if (!valid) nvis = 0;
-    int nvis_w = nvis;                                 // the wave's largest
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_xor(nvis_w, o);
-        nvis_w = y > nvis_w ? y : nvis_w;
-    }
-    nvis_w = __builtin_amdgcn_readfirstlane(nvis_w);
-    const int nch = (nvis_w + kWinChunk - 1) / kWinChunk;
+    // windows the tile's last token sees: the chunk count of every wave
+    const int c_last = tok0 + ntok - 1 + off;
+    int nv_tile = c_last >= kCmpSize - 1 ? (c_last - (kCmpSize - 1)) / kCmpStride + 1 : 0;
+    nv_tile = nv_tile < ncmp ? nv_tile : ncmp;
+    const int nch = (nv_tile + kWinChunk - 1) / kWinChunk;
 
     u32x4_t qf[KS];
     {
@@ -164,20 +207,38 @@ __global__ void __launch_bounds__(kSelectThreads) block_select_kernel(const Bloc
     const int64_t cstride = (int64_t)p.Hkv * D;        // elements between windows
     const float c2 = p.scale_log2;
 
-    // S^T for chunk ch: st[kt][i] = score of window ch*64 + 16kt + 4lg + i (log2 units)
-    auto scores = [&](int ch, f32x4_t (&st)[4]) {
+    // chunk staging: piece x = tid + 256 n -> window x / CPR, 8-dim piece x % CPR
+    u32x4_t stg[NL];
+    auto fetch = [&](int ch) {
+#pragma unroll
+        for (int n = 0; n < NL; ++n) {
+            const int x = tid + n * kSelectThreads;
+            int wi = ch * kWinChunk + x / CPR;
+            wi = wi < p.ncmp_max ? wi : p.ncmp_max - 1;          // (masked below)
+            stg[n] = *reinterpret_cast<const u32x4_t*>(cbase + wi * cstride + (x % CPR) * 8);
+        }
+    };
+    auto stage = [&](int buf) {
+        uint8_t* dst = cbuf + buf * kChunkBytes;
+#pragma unroll
+        for (int n = 0; n < NL; ++n) {
+            const int x = tid + n * kSelectThreads;
+            const int wr = x / CPR, pc = x % CPR;                 // window in chunk, piece
+            const int kt = wr / 16, s = pc / 4;
+            const int l = (pc % 4) * 16 + wr % 16;                // fragment lane
+            *reinterpret_cast<u32x4_t*>(dst + (kt * KS + s) * 1024 + l * 16) = stg[n];
+        }
+    };
+    // S^T of chunk ch from buffer buf: st[kt][i] = window ch*64 + 16kt + 4lg + i (log2 units)
+    auto scores = [&](int ch, int buf, f32x4_t (&st)[4]) {
+        const uint8_t* src = cbuf + buf * kChunkBytes + lane * 16;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                int wi = ch * kWinChunk + kt * 16 + lr;
-                wi = wi < p.ncmp_max ? wi : p.ncmp_max - 1;   // (masked below)
-                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(cbase + wi * cstride + s * 32 + lg * 8);
-                st[kt] = mfma_16x16x32(a, qf[s], st[kt]);
-            }
-        }
+            for (int kt = 0; kt < 4; ++kt)
+                st[kt] = mfma_16x16x32(*reinterpret_cast<const u32x4_t*>(src + (kt * KS + s) * 1024), qf[s], st[kt]);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -187,56 +248,76 @@ __global__ void __launch_bounds__(kSelectThreads) block_select_kernel(const Bloc
             }
     };
 
-    // pass 1: row max and sum (per lane, then over the row's four lanes)
-    float m = -INFINITY, l = 0.f;
-    for (int ch = 0; ch < nch; ++ch) {
-        f32x4_t st[4];
-        scores(ch, st);
-        float mx = m;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[kt][i]);
-        if (mx != -INFINITY) {
-            float sum = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sum += fast_exp2(st[kt][i] - mx);
-            l = l * fast_exp2(m - mx) + sum;
-            m = mx;
-        }
-    }
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1) {
-        const float mo = __shfl_xor(m, o), lo = __shfl_xor(l, o);
-        const float mn = fmaxf(m, mo);
-        if (mn != -INFINITY) {
-            l = (m == -INFINITY ? 0.f : l * fast_exp2(m - mn)) + (mo == -INFINITY ? 0.f : lo * fast_exp2(mo - mn));
-            m = mn;
-        }
-    }
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-
-    // pass 2: probabilities -> block masses of token t_l
+    // Two passes over the chunks: row max and sum, then probabilities ->
+    // block masses of token t_l.  Step st_i runs chunk st_i % nch from buffer
+    // st_i & 1 while the next step's chunk is fetched.
+    float m = -INFINITY, l = 0.f, inv = 0.f;
     float* imp_row = s_imp + (valid ? t_l : 0) * nb;
-    for (int ch = 0; ch < nch; ++ch) {
+    // lanes summed before an atomic: a token's rows within the m-tile (G
+    // dividing 16), all 16 rows (G a multiple of 16), else none
+    const int gsum = (16 % G == 0) ? G : (G % 16 == 0 ? 16 : 1);
+    const int nsteps = 2 * nch;
+    if (nsteps > 0) {
+        fetch(0);
+        stage(0);
+    }
+    __syncthreads();                                   // table cleared, chunk 0 staged
+    for (int si = 0; si < nsteps; ++si) {
+        const int ch = si % nch, buf = si & 1;
+        if (si + 1 < nsteps) fetch((si + 1) % nch);
         f32x4_t st[4];
-        scores(ch, st);
-        if (valid) {
+        if (wave < p.mtiles) {
+            scores(ch, buf, st);
+            if (si < nch) {                                         // pass 1
+                float mx = m;
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) {
-                float pr[4];
+                for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) pr[i] = st[kt][i] == -INFINITY ? 0.f : fast_exp2(st[kt][i] - m) * inv;
-                const int blk = ch * (kWinChunk / 4) + kt * 4 + lg;   // block of windows 4blk .. 4blk+3
-                const float own = pr[0] + pr[1] + pr[2] + 0.5f * pr[3];
-                if (own != 0.f) atomicAdd(imp_row + blk, own);
-                if (pr[3] != 0.f) atomicAdd(imp_row + blk + 1, 0.5f * pr[3]);
+                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[kt][i]);
+                if (mx != -INFINITY) {
+                    float sum = 0.f;
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sum += fast_exp2(st[kt][i] - mx);
+                    l = l * fast_exp2(m - mx) + sum;
+                    m = mx;
+                }
+                if (si == nch - 1) {                                // the row's four lanes
+#pragma unroll
+                    for (int o = 16; o < 64; o <<= 1) {
+                        const float mo = __shfl_xor(m, o), lo = __shfl_xor(l, o);
+                        const float mn = fmaxf(m, mo);
+                        if (mn != -INFINITY) {
+                            l = (m == -INFINITY ? 0.f : l * fast_exp2(m - mn)) +
+                                (mo == -INFINITY ? 0.f : lo * fast_exp2(mo - mn));
+                            m = mn;
+                        }
+                    }
+                    inv = l > 0.f ? 1.f / l : 0.f;
+                }
+            } else {                                                // pass 2
+                // the rows of one token (its G heads) are adjacent lanes: their
+                // masses are summed in registers first, and one lane per token
+                // and block adds them to the table
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    float pr[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pr[i] = st[kt][i] == -INFINITY ? 0.f : fast_exp2(st[kt][i] - m) * inv;
+                    const int blk = ch * (kWinChunk / 4) + kt * 4 + lg;   // block of windows 4blk .. 4blk+3
+                    const float own = group_sum(pr[0] + pr[1] + pr[2] + 0.5f * pr[3], gsum);
+                    const float nxt = group_sum(0.5f * pr[3], gsum);
+                    if (valid && (lr % gsum) == 0) {
+                        if (own != 0.f) atomicAdd(imp_row + blk, own);
+                        if (nxt != 0.f) atomicAdd(imp_row + blk + 1, nxt);
+                    }
+                }
             }
         }
+        if (si + 1 < nsteps) stage((si + 1) & 1);
+        __syncthreads();
     }
-    __syncthreads();
 
     // selection: one wave per token
     for (int t = wave; t < ntok; t += kSelectWaves) {
@@ -269,14 +350,7 @@ __global__ void __launch_bounds__(kSelectThreads) block_select_kernel(const Bloc
                         best = key > best ? key : best;
                     }
                 }
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const uint32_t bl = __shfl_xor((uint32_t)best, o);
-                    const uint32_t bh = __shfl_xor((uint32_t)(best >> 32), o);
-                    const unsigned long long ob = ((unsigned long long)bh << 32) | bl;
-                    best = ob > best ? ob : best;
-                }
-                best = uniform_u64(best);
+                best = wave_max_u64(best);
                 if (best == 0ull) break;                    // no candidate left
                 const int x = (int)(0xFFFFFFFFu - (uint32_t)best);
                 if (lane == n) first = x;
@@ -290,7 +364,9 @@ __global__ void __launch_bounds__(kSelectThreads) block_select_kernel(const Bloc
     }
 }
 
-size_t block_select_lds_bytes(int T, int nb_max) { return (size_t)T * nb_max * 4; }
+size_t block_select_lds_bytes(int T, int nb_max, int D) {
+    return (((size_t)T * nb_max * 4 + 15) & ~(size_t)15) + 2 * (size_t)kWinChunk * D * 2;
+}
 
 hipError_t launch_block_select(const BlockSelectParams& p, int D, hipStream_t stream) {
     const int64_t ncmp_items = (int64_t)p.batch * p.ncmp_max * p.Hkv * (D / 8);
@@ -299,7 +375,7 @@ hipError_t launch_block_select(const BlockSelectParams& p, int D, hipStream_t st
         if (D == 64) hipLaunchKernelGGL(cmp_keys_kernel<64>, dim3(gc), dim3(256), 0, stream, p);
         else hipLaunchKernelGGL(cmp_keys_kernel<128>, dim3(gc), dim3(256), 0, stream, p);
     }
-    const size_t lds = block_select_lds_bytes(p.T, p.nb_max);
+    const size_t lds = block_select_lds_bytes(p.T, p.nb_max, D);
     static bool attr_set[2] = {false, false};
     const int di = D == 64 ? 0 : 1;
     if (!attr_set[di]) {

@@ -121,10 +121,10 @@ DecodeLayout decode_layout(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, in
 float resolve_scale(float s, int D) { return s > 0.f ? s : 1.0f / std::sqrt((float)D); }
 
 // Block-index producer: the importance table [T][blocks] (fp32) of one tile
-// lives in LDS; T tokens times G heads fill at most 4 m-tiles of 16 rows.
+// lives in LDS; T tokens times G heads fill at most 8 m-tiles of 16 rows.
 constexpr int kSelectCmpSize = 32, kSelectCmpStride = 16;
 constexpr int kMaxTopkSelect = 64;
-constexpr int kMaxGroupSelect = 64;
+constexpr int kMaxGroupSelect = 128;
 constexpr size_t kSelectLdsBudget = 64 * 1024;
 
 struct SelectPlan {
@@ -151,7 +151,7 @@ SelectPlan plan_select(int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, i
     pl.nb_max = (max_seqlen_k + fsa::kBlockKeys - 1) / fsa::kBlockKeys;
     if (pl.nb_max < 1) pl.nb_max = 1;
     pl.ncmp_max = max_seqlen_k >= kSelectCmpSize ? (max_seqlen_k - kSelectCmpSize) / kSelectCmpStride + 1 : 0;
-    int T = 64 / G;
+    int T = 128 / G;                            // 8 m-tiles of 16 rows
     const int t_lds = (int)(kSelectLdsBudget / ((size_t)pl.nb_max * 4));
     T = T < t_lds ? T : t_lds;
     pl.T = T;                                   // 0: the table does not fit

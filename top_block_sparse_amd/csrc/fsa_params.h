@@ -122,7 +122,7 @@ int decode_table_slots(int D, int G, int topk);
 hipError_t launch_lse_merge(const MergeParams& p, int D, hipStream_t stream);
 hipError_t launch_sel_attn_bwd(const SelBwdParams& p, int D, hipStream_t stream);
 hipError_t launch_block_select(const BlockSelectParams& p, int D, hipStream_t stream);
-size_t block_select_lds_bytes(int T, int nb_max);
+size_t block_select_lds_bytes(int T, int nb_max, int D);
 int sel_attn_bwd_rows_per_tile();   // query rows (T*G) one dq workgroup covers
 int sel_attn_bwd_index_chunk();     // tokens one index workgroup covers
 size_t sel_attn_bwd_dq_lds_bytes(int D, int T, int topk, int ring);
