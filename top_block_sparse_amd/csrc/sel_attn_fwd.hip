@@ -15,17 +15,20 @@
 // union through a ring of LDS slots:
 //   - two producer waves copy each K/V block straight from HBM/L2 into a ring
 //     slot with buffer->LDS loads (16 bytes per lane, no registers involved;
-//     rows past the sequence end read as zero), keep up to three blocks in
-//     flight, and publish a slot by writing its sequence number once their
-//     loads have landed;
-//   - each of the fourteen consumer waves owns one m-tile, waits for the next
-//     slot, computes it if any of its tokens selected the block, and counts
-//     itself done with the slot; a producer reuses a slot only after all
-//     consumers are done with it.
+//     rows past the sequence end read as zero), keep two blocks in flight,
+//     and publish a slot by writing its sequence number once its loads have
+//     landed; before waiting for a slot to free up they publish everything
+//     already loaded;
+//   - each of the fourteen consumer waves owns one m-tile and visits only the
+//     union blocks that one of its tokens selected: it waits for the block's
+//     slot, computes it and counts itself done with the slot;
+//   - the union build also counts, per block, the m-tiles that need it, and a
+//     producer reuses a slot once that many consumers are done with it.
 // Consumers never wait for one another, so the uneven per-block work of
 // random selections evens out over the tile instead of costing a barrier per
-// block.  Every wait is a bounded spin, so a logic error can only produce
-// wrong values, never a hung GPU.
+// block, and a block no token of an m-tile chose costs that m-tile nothing.
+// Every wait is a bounded spin, so a logic error can only produce wrong
+// values, never a hung GPU.
 //
 // Per m-tile and block the contraction runs transposed, S^T = K * Q^T with
 // v_mfma_f32_16x16x32_bf16: the key index is the MFMA row, the query row the
@@ -49,7 +52,7 @@ constexpr int kSelWaves = kSelConsumers + kSelProducers;
 constexpr int kSelThreads = kSelWaves * 64;
 constexpr int kSelWin = 256;                       // blocks per union-building window
 constexpr int kSelRingMax = 4;                     // LDS slots of K/V blocks (3 if LDS is short)
-constexpr int kSelDepth = 3;                       // blocks in flight per producer (<= slots)
+constexpr int kSelDepth = 2;                       // blocks in flight per producer (<= slots)
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kSpinLimit = 1 << 22;                // bounded waits (normal waits are ~1e3)
 constexpr float kLazy = 8.f;                       // lazy-rescale threshold (log2 units)
@@ -76,7 +79,8 @@ struct SelLds {
     __host__ __device__ static int masks(int ring) { return ring * kSlot; }                // u64 [kSelWin]
     __host__ __device__ static int umask(int ring) { return masks(ring) + kSelWin * 8; }   // u64 [kSelWin]
     __host__ __device__ static int ulist(int ring) { return umask(ring) + kSelWin * 8; }   // i32 [kSelWin]
-    __host__ __device__ static int count(int ring) { return ulist(ring) + kSelWin * 4; }   // i32
+    __host__ __device__ static int ncnt(int ring) { return ulist(ring) + kSelWin * 4; }    // i32 [kSelWin]
+    __host__ __device__ static int count(int ring) { return ncnt(ring) + kSelWin * 4; }    // i32
     __host__ __device__ static int ready(int ring) { return count(ring) + 16; }            // u32 [ring][producers]
     __host__ __device__ static int done(int ring) { return ready(ring) + kSelRingMax * kSelProducers * 4; }
     __host__ __device__ static int ent(int ring) { return done(ring) + kSelRingMax * 4; }  // i32 [T*topk]
@@ -84,6 +88,15 @@ struct SelLds {
         return (size_t)ent(ring) + (size_t)T * topk * 4;
     }
 };
+
+__device__ __forceinline__ u32x2_t lds_load2_sync(const void* p) {
+    u32x2_t v;
+    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(v)
+                 : "v"((uint32_t)(uintptr_t)p)
+                 : "memory");
+    return v;
+}
 
 __device__ __forceinline__ float lane_max4(float x) {
     // max over lanes l, l^16, l^32, l^48 (the four lanes holding one query row)
@@ -130,6 +143,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     unsigned long long* s_masks = reinterpret_cast<unsigned long long*>(smem + L::masks(ring));
     unsigned long long* s_umask = reinterpret_cast<unsigned long long*>(smem + L::umask(ring));
     int* s_ulist = reinterpret_cast<int*>(smem + L::ulist(ring));
+    int* s_ncnt = reinterpret_cast<int*>(smem + L::ncnt(ring));
     int* s_count = reinterpret_cast<int*>(smem + L::count(ring));
     uint32_t* s_ready = reinterpret_cast<uint32_t*>(smem + L::ready(ring));
     uint32_t* s_done = reinterpret_cast<uint32_t*>(smem + L::done(ring));
@@ -370,7 +384,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     };
     auto publish = [&](int slot, uint32_t seq_plus1) {
         if (lane == 0) {
-            asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+            asm volatile("ds_write_b32 %0, %1"
                          :
                          : "v"((uint32_t)(uintptr_t)(s_ready + slot * kSelProducers + pw)),
                            "v"(seq_plus1)
@@ -381,6 +395,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     lds_barrier();   // s_ent and ring flags ready
 
     uint32_t seq0 = 0;    // ring sequence number of the window's first block
+    uint32_t tgt0 = 0, tgt1 = 0, tgt2 = 0, tgt3 = 0;   // producers: done counts that free each slot
     for (int win_lo = nb_lo; win_lo < nb_range; win_lo += kSelWin) {
         const int win_n = (nb_range - win_lo) < kSelWin ? (nb_range - win_lo) : kSelWin;
         if (WIN && p.dense) {
@@ -418,8 +433,19 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
                 const unsigned long long bal = __ballot(m != 0ull);
                 if (m != 0ull) {
                     const int pos = n + __popcll(bal & ((1ull << lane) - 1ull));
+                    // consumers (m-tiles) that need the block
+                    int nc = 0;
+                    for (int c = 0; c < p.mtiles; ++c) {
+                        const int tf = (c * 16) / G;
+                        int tl = (c * 16 + 15) / G;
+                        tl = tl < ntok - 1 ? tl : ntok - 1;
+                        const unsigned long long hi = tl >= 63 ? ~0ull : ((1ull << (tl + 1)) - 1ull);
+                        const unsigned long long cm = tf > tl ? 0ull : (hi & ~((1ull << tf) - 1ull));
+                        nc += (m & cm) != 0ull ? 1 : 0;
+                    }
                     s_ulist[pos] = win_lo + x;
                     s_umask[pos] = m;
+                    s_ncnt[pos] = nc;
                 }
                 n += __popcll(bal);
             }
@@ -432,55 +458,82 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         const int n = u_end - u_beg;
 
         if (!consumer) {
-            // producer: issue block i, then publish block i - (kSelDepth - 1)
+            // producer: issue block i; publish the oldest unpublished block once
+            // kSelDepth - 1 younger ones are in flight, and publish everything
+            // issued before waiting for a slot, so that a slow consumer never
+            // holds back blocks that have already landed
+            int pub = 0;                                  // next block to publish
+            int ul_v = 0, nc_v = 0;                       // union ids / need counts, 64 at a time
             for (int i = 0; i < n; ++i) {
+                if ((i & 63) == 0) {
+                    int x = u_beg + i + lane;
+                    x = x < kSelWin - 1 ? x : kSelWin - 1;
+                    ul_v = (int)lds_load_sync(s_ulist + x);
+                    nc_v = (int)lds_load_sync(s_ncnt + x);
+                }
                 const uint32_t seq = seq0 + (uint32_t)i;
                 const int slot = (int)(seq % (uint32_t)ring);
-                const uint32_t need_done = kSelConsumers * (seq / (uint32_t)ring);
-                for (int sp = 0; sp < kSpinLimit && lds_load_sync(s_done + slot) < need_done; ++sp)
-                    __builtin_amdgcn_s_sleep(1);
-                const int blk = __builtin_amdgcn_readfirstlane(
-                    (int)lds_load_sync(s_ulist + u_beg + i));
+                // the slot is free once every consumer that needed its earlier blocks is done
+                const uint32_t need_done = slot == 0 ? tgt0 : slot == 1 ? tgt1 : slot == 2 ? tgt2 : tgt3;
+                if (lds_load_sync(s_done + slot) < need_done) {
+                    wait_vmcnt<0>();
+                    for (; pub < i; ++pub) {
+                        const uint32_t ps = seq0 + (uint32_t)pub;
+                        publish((int)(ps % (uint32_t)ring), ps + 1);
+                    }
+                    for (int sp = 0; sp < kSpinLimit && lds_load_sync(s_done + slot) < need_done; ++sp)
+                        __builtin_amdgcn_s_sleep(1);
+                }
+                const int blk = __builtin_amdgcn_readlane(ul_v, i & 63);
+                const uint32_t nc = (uint32_t)__builtin_amdgcn_readlane(nc_v, i & 63);
+                tgt0 += slot == 0 ? nc : 0u;
+                tgt1 += slot == 1 ? nc : 0u;
+                tgt2 += slot == 2 ? nc : 0u;
+                tgt3 += slot == 3 ? nc : 0u;
                 if (pw == 0)
                     produce(std::integral_constant<int, NIP0>{}, 0, blk, slot);
                 else
                     produce(std::integral_constant<int, NIP1>{}, NIP0, blk, slot);
-                if (i >= kSelDepth - 1) {
+                if (i - pub == kSelDepth - 1) {           // exactly kSelDepth - 1 blocks issued after pub
                     if (pw == 0)
                         wait_vmcnt<NIP0 * (kSelDepth - 1)>();
                     else
                         wait_vmcnt<NIP1 * (kSelDepth - 1)>();
-                    const uint32_t ps = seq - (kSelDepth - 1);
+                    const uint32_t ps = seq0 + (uint32_t)pub;
                     publish((int)(ps % (uint32_t)ring), ps + 1);
+                    ++pub;
                 }
             }
             wait_vmcnt<0>();
-            const int first = n > kSelDepth - 1 ? n - (kSelDepth - 1) : 0;
-            for (int i = first; i < n; ++i) {
-                const uint32_t ps = seq0 + (uint32_t)i;
+            for (; pub < n; ++pub) {
+                const uint32_t ps = seq0 + (uint32_t)pub;
                 publish((int)(ps % (uint32_t)ring), ps + 1);
             }
         } else {
-            for (int i = 0; i < n; ++i) {
-                const uint32_t seq = seq0 + (uint32_t)i;
-                const int slot = (int)(seq % (uint32_t)ring);
-                for (int sp = 0; sp < kSpinLimit; ++sp) {
-                    bool ok = true;
-#pragma unroll
-                    for (int q = 0; q < kSelProducers; ++q)
-                        ok = ok && lds_load_sync(s_ready + slot * kSelProducers + q) >= seq + 1;
-                    if (ok) break;
-                    __builtin_amdgcn_s_sleep(1);
+            // only the blocks this m-tile needs: a bit per union position
+#pragma unroll 1
+            for (int k = 0; k < kSelWin / 64; ++k) {
+                const int x = 64 * k + lane;
+                const unsigned long long m = (x >= u_beg && x < u_end) ? s_umask[x] : 0ull;
+                unsigned long long bits = __builtin_amdgcn_ballot_w64((m & mt_tok) != 0ull);
+                while (bits != 0ull) {
+                    const int u = 64 * k + (int)__builtin_ctzll(bits);
+                    bits &= bits - 1ull;
+                    const uint32_t seq = seq0 + (uint32_t)(u - u_beg);
+                    const int slot = (int)(seq % (uint32_t)ring);
+                    const int blk = __builtin_amdgcn_readfirstlane(s_ulist[u]);
+                    const unsigned long long bm = uniform_u64(s_umask[u]);
+                    for (int sp = 0; sp < kSpinLimit; ++sp) {
+                        const u32x2_t r = lds_load2_sync(s_ready + slot * kSelProducers);
+                        if (r[0] >= seq + 1 && r[1] >= seq + 1) break;
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                    compute(smem + slot * L::kSlot, blk, bm);
+                    // done with the slot: its reads have completed before the count
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                    if (lane == 0) __hip_atomic_fetch_add(s_done + slot, 1u, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_WORKGROUP);
                 }
-                const int u = u_beg + i;
-                const int blk = __builtin_amdgcn_readfirstlane(s_ulist[u]);
-                const unsigned long long bm = uniform_u64(s_umask[u]);
-                const int need = __builtin_amdgcn_readfirstlane((bm & mt_tok) != 0ull ? 1 : 0);
-                if (need) compute(smem + slot * L::kSlot, blk, bm);
-                // done with the slot: its reads have completed before the count
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-                if (lane == 0) __hip_atomic_fetch_add(s_done + slot, 1u, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
         seq0 += (uint32_t)n;
