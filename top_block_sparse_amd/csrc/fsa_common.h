@@ -58,6 +58,16 @@ __device__ __forceinline__ uint32_t lds_load_sync(const void* p) {
     return v;
 }
 
+// The same for two adjacent words (8-byte aligned).
+__device__ __forceinline__ u32x2_t lds_load2_sync(const void* p) {
+    u32x2_t v;
+    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(v)
+                 : "v"((uint32_t)(uintptr_t)p)
+                 : "memory");
+    return v;
+}
+
 // Workgroup barrier that orders LDS accesses only: global loads in flight
 // (prefetches) are not waited for.
 __device__ __forceinline__ void lds_barrier() {

@@ -546,7 +546,8 @@ struct DqLds {
     __host__ __device__ static int masks(int ring) { return ring * kSlot; }           // u64 [kBwdWin]
     __host__ __device__ static int umask(int ring) { return masks(ring) + kBwdWin * 8; }  // u64 [kBwdWin]
     __host__ __device__ static int ulist(int ring) { return umask(ring) + kBwdWin * 8; }  // i32 [kBwdWin]
-    __host__ __device__ static int count(int ring) { return ulist(ring) + kBwdWin * 4; }  // i32
+    __host__ __device__ static int ncnt(int ring) { return ulist(ring) + kBwdWin * 4; }   // i32 [kBwdWin]
+    __host__ __device__ static int count(int ring) { return ncnt(ring) + kBwdWin * 4; }   // i32
     __host__ __device__ static int ready(int ring) { return count(ring) + 16; }           // u32 [4][producers]
     __host__ __device__ static int done(int ring) { return ready(ring) + 4 * kBwdDqProducers * 4; }  // u32 [4]
     __host__ __device__ static int ent(int ring) { return done(ring) + 16; }              // i32 [T * topk]
@@ -567,6 +568,7 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
     unsigned long long* s_masks = reinterpret_cast<unsigned long long*>(smem + L::masks(ring));
     unsigned long long* s_umask = reinterpret_cast<unsigned long long*>(smem + L::umask(ring));
     int* s_ulist = reinterpret_cast<int*>(smem + L::ulist(ring));
+    int* s_ncnt = reinterpret_cast<int*>(smem + L::ncnt(ring));
     int* s_count = reinterpret_cast<int*>(smem + L::count(ring));
     uint32_t* s_ready = reinterpret_cast<uint32_t*>(smem + L::ready(ring));
     uint32_t* s_done = reinterpret_cast<uint32_t*>(smem + L::done(ring));
@@ -686,14 +688,15 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
     };
     auto publish = [&](int slot, uint32_t seq_plus1) {
         if (lane == 0) {
-            asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+            asm volatile("ds_write_b32 %0, %1"
                          :
                          : "v"((uint32_t)(uintptr_t)(s_ready + slot * kBwdDqProducers + pw)), "v"(seq_plus1)
                          : "memory");
         }
     };
-    const int depth = ring - 1 < 3 ? ring - 1 : 3;    // blocks in flight per producer
+    constexpr int depth = 2;                          // blocks in flight per producer (ring >= 2)
     uint32_t seq0 = 0;                                // ring sequence number of the window's first block
+    uint32_t tgt0 = 0, tgt1 = 0, tgt2 = 0, tgt3 = 0;  // producers: done counts that free each slot
     __syncthreads();
 
     for (int win_lo = 0; win_lo < nb_range; win_lo += kBwdWin) {
@@ -713,8 +716,18 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
                 const unsigned long long bal = __ballot(m != 0ull);
                 if (m != 0ull) {
                     const int pos = n + __popcll(bal & ((1ull << lane) - 1ull));
+                    int nc = 0;                         // compute waves (m-tiles) that need the block
+                    for (int c = 0; c < p.mtiles; ++c) {
+                        const int tf = (c * 16) / G;
+                        int tl = (c * 16 + 15) / G;
+                        tl = tl < ntok - 1 ? tl : ntok - 1;
+                        const unsigned long long hi = tl >= 63 ? ~0ull : ((1ull << (tl + 1)) - 1ull);
+                        const unsigned long long cm = tf > tl ? 0ull : (hi & ~((1ull << tf) - 1ull));
+                        nc += (m & cm) != 0ull ? 1 : 0;
+                    }
                     s_ulist[pos] = win_lo + x;
                     s_umask[pos] = m;
+                    s_ncnt[pos] = nc;
                 }
                 n += __popcll(bal);
             }
@@ -724,50 +737,76 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
         const int n_u = __builtin_amdgcn_readfirstlane(s_count[0]);
 
         // Ring protocol.  The producers copy the union's blocks in order into
-        // ring slots (up to `depth` blocks in flight) and publish a slot by
-        // writing its sequence number once their loads have landed; each
-        // compute wave waits for the slot, uses it if one of its tokens
-        // selected the block, and counts itself done with it; a producer
-        // refills a slot only after every compute wave is done with it.
-        // Compute waves never wait for one another, so the uneven work of
-        // random selections evens out over the tile.  Every wait is bounded.
+        // ring slots (`depth` blocks in flight) and publish a slot by writing
+        // its sequence number once its loads have landed, publishing all
+        // loaded blocks before they wait for a slot to free up.  Each compute
+        // wave visits only the blocks one of its tokens selected: it waits
+        // for the slot, uses it and counts itself done with it; a producer
+        // refills a slot once as many compute waves as the union build
+        // counted for its block are done with it.  Compute waves never wait
+        // for one another, so the uneven work of random selections evens out
+        // over the tile.  Every wait is bounded.
         if (wave >= kBwdDqWaves) {
+            int pub = 0;                                  // next block to publish
+            int ul_v = 0, nc_v = 0;                       // union ids / need counts, 64 at a time
             for (int i = 0; i < n_u; ++i) {
+                if ((i & 63) == 0) {
+                    int x = i + lane;
+                    x = x < kBwdWin - 1 ? x : kBwdWin - 1;
+                    ul_v = (int)lds_load_sync(s_ulist + x);
+                    nc_v = (int)lds_load_sync(s_ncnt + x);
+                }
                 const uint32_t seq = seq0 + (uint32_t)i;
                 const int slot = (int)(seq % (uint32_t)ring);
-                const uint32_t need_done = kBwdDqWaves * (seq / (uint32_t)ring);
-                for (int sp = 0; sp < kSpinLimit && lds_load_sync(s_done + slot) < need_done; ++sp)
-                    __builtin_amdgcn_s_sleep(1);
-                issue(__builtin_amdgcn_readfirstlane((int)lds_load_sync(s_ulist + i)), slot);
-                if (i >= depth - 1) {
-                    if (depth == 3) wait_vmcnt<2 * PPW>();
-                    else if (depth == 2) wait_vmcnt<PPW>();
-                    else wait_vmcnt<0>();
-                    const uint32_t ps = seq - (uint32_t)(depth - 1);
+                const uint32_t need_done = slot == 0 ? tgt0 : slot == 1 ? tgt1 : slot == 2 ? tgt2 : tgt3;
+                if (lds_load_sync(s_done + slot) < need_done) {
+                    wait_vmcnt<0>();
+                    for (; pub < i; ++pub) {
+                        const uint32_t ps = seq0 + (uint32_t)pub;
+                        publish((int)(ps % (uint32_t)ring), ps + 1);
+                    }
+                    for (int sp = 0; sp < kSpinLimit && lds_load_sync(s_done + slot) < need_done; ++sp)
+                        __builtin_amdgcn_s_sleep(1);
+                }
+                const uint32_t nc = (uint32_t)__builtin_amdgcn_readlane(nc_v, i & 63);
+                tgt0 += slot == 0 ? nc : 0u;
+                tgt1 += slot == 1 ? nc : 0u;
+                tgt2 += slot == 2 ? nc : 0u;
+                tgt3 += slot == 3 ? nc : 0u;
+                issue(__builtin_amdgcn_readlane(ul_v, i & 63), slot);
+                if (i - pub == depth - 1) {
+                    wait_vmcnt<PPW * (depth - 1)>();
+                    const uint32_t ps = seq0 + (uint32_t)pub;
                     publish((int)(ps % (uint32_t)ring), ps + 1);
+                    ++pub;
                 }
             }
             wait_vmcnt<0>();
-            for (int i = n_u > depth - 1 ? n_u - (depth - 1) : 0; i < n_u; ++i) {
-                const uint32_t ps = seq0 + (uint32_t)i;
+            for (; pub < n_u; ++pub) {
+                const uint32_t ps = seq0 + (uint32_t)pub;
                 publish((int)(ps % (uint32_t)ring), ps + 1);
             }
-        } else for (int u = 0; u < n_u; ++u) {
+        } else {
+#pragma unroll 1
+        for (int k = 0; k < kBwdWin / 64; ++k) {
+          const int x = 64 * k + lane;
+          const unsigned long long mx = x < n_u ? s_umask[x] : 0ull;
+          unsigned long long bits = __builtin_amdgcn_ballot_w64((mx & mt_tok) != 0ull);
+          while (bits != 0ull) {
+            const int u = 64 * k + (int)__builtin_ctzll(bits);
+            bits &= bits - 1ull;
             const uint32_t seq = seq0 + (uint32_t)u;
             const int slot = (int)(seq % (uint32_t)ring);
-            for (int sp = 0; sp < kSpinLimit; ++sp) {
-                bool ok = true;
-#pragma unroll
-                for (int q = 0; q < kBwdDqProducers; ++q)
-                    ok = ok && lds_load_sync(s_ready + slot * kBwdDqProducers + q) >= seq + 1;
-                if (ok) break;
-                __builtin_amdgcn_s_sleep(1);
-            }
             const int blk = __builtin_amdgcn_readfirstlane(s_ulist[u]);
             const unsigned long long bm = uniform_u64(s_umask[u]);
+            for (int sp = 0; sp < kSpinLimit; ++sp) {
+                const u32x2_t r = lds_load2_sync(s_ready + slot * kBwdDqProducers);
+                if (r[0] >= seq + 1 && r[1] >= seq + 1) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
             const uint8_t* kslot = smem + slot * L::kSlot;
             const uint8_t* vslot = kslot + L::kPart;
-            if ((bm & mt_tok) != 0ull) {
+            {
                 const bool sel = row_tok < 64 && ((bm >> row_tok) & 1ull) != 0ull;
                 const float msub = sel ? lse2 : INFINITY;      // unselected rows get P = 0
                 // dP^T starts at -D, so the MFMA leaves dP - D
@@ -821,6 +860,8 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
             // done with the slot: its reads have completed before the count
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             if (lane == 0) __hip_atomic_fetch_add(s_done + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+        }
         }
         seq0 += (uint32_t)n_u;
         lds_barrier();   // ring and union buffers free for the next window

@@ -89,15 +89,6 @@ struct SelLds {
     }
 };
 
-__device__ __forceinline__ u32x2_t lds_load2_sync(const void* p) {
-    u32x2_t v;
-    asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(v)
-                 : "v"((uint32_t)(uintptr_t)p)
-                 : "memory");
-    return v;
-}
-
 __device__ __forceinline__ float lane_max4(float x) {
     // max over lanes l, l^16, l^32, l^48 (the four lanes holding one query row)
     auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
