@@ -606,6 +606,8 @@ SELECT_SHAPES = [
     ((517, 20, 0, 300), None, 16, 1, 64, 16, 2, 3),    # a sequence with no window, an empty one
     ((1100,), None, 2, 2, 128, 12, 0, 0),              # no forced blocks
     ((2048,), None, 64, 1, 64, 32, 1, 2),              # group of 64 (one token per tile)
+    ((8256,), None, 2, 1, 64, 48, 1, 2),               # 128 candidates (row-wise picks), 48 entries
+    ((8320,), None, 2, 1, 64, 20, 1, 1),               # 129 candidates (one wave per token)
 ]
 
 

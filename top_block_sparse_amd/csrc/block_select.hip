@@ -28,8 +28,11 @@
 //                     two passes -- row max and sum, then probabilities --
 //                     from chunks of 64 window summaries staged once in LDS,
 //                     adding block masses into an LDS table [T][blocks];
-//                     then one wave per token takes the forced blocks and
-//                     picks the rest by repeated wave-wide argmax.
+//                     then the forced blocks are listed and the rest picked
+//                     by repeated argmax: with at most 128 candidates per
+//                     token, four tokens per wave (one per 16-lane row, the
+//                     candidates in registers, a DPP row maximum per pick),
+//                     otherwise one wave per token over the LDS table.
 #include "fsa_common.h"
 #include "fsa_params.h"
 
@@ -43,6 +46,7 @@ constexpr int kCmpStride = 16;         // window stride
 constexpr int kSelectWaves = 8;
 constexpr int kSelectThreads = kSelectWaves * 64;
 constexpr int kWinChunk = 64;          // windows per MFMA chunk (4 key tiles of 16)
+constexpr int kPickRegs = 8;           // register-held candidates per lane in the row-wise selection
 
 struct Bounds {
     int64_t q0, k0;
@@ -80,19 +84,28 @@ __device__ __forceinline__ float group_sum(float x, int n) {
     return x;
 }
 
-// wave-wide maximum of a 64-bit key: DPP within each 16-lane row, then the
-// gfx950 permlane swaps across rows (all VALU; no LDS round trips)
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
-    auto pick = [](unsigned long long a, unsigned long long b) { return a > b ? a : b; };
 #define FSA_DPP_U64(v, ctrl)                                                                       \
     ((((unsigned long long)(uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)((v) >> 32), ctrl, \
                                                                  0xF, 0xF, false)) << 32) |       \
      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v), ctrl, 0xF, 0xF, false))
+
+// maximum of a 64-bit key over each 16-lane row (every lane of the row gets
+// it): quad swaps, then the half-row and row mirrors
+__device__ __forceinline__ unsigned long long row_max_u64(unsigned long long x) {
+    auto pick = [](unsigned long long a, unsigned long long b) { return a > b ? a : b; };
     x = pick(x, FSA_DPP_U64(x, 0xB1));
     x = pick(x, FSA_DPP_U64(x, 0x4E));
     x = pick(x, FSA_DPP_U64(x, 0x141));
     x = pick(x, FSA_DPP_U64(x, 0x140));
+    return x;
+}
 #undef FSA_DPP_U64
+
+// wave-wide maximum of a 64-bit key: the row maximum, then the gfx950
+// permlane swaps across rows (all VALU; no LDS round trips)
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) {
+    auto pick = [](unsigned long long a, unsigned long long b) { return a > b ? a : b; };
+    x = row_max_u64(x);
     {
         const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
         const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
@@ -319,7 +332,82 @@ __global__ void __launch_bounds__(kSelectThreads) block_select_kernel(const Bloc
         __syncthreads();
     }
 
-    // selection: one wave per token
+    // selection, when a token has at most 16 * kPickRegs candidates: four
+    // tokens per wave, one per 16-lane row.  Each lane keeps its candidates
+    // x = lo + (lane % 16) + 16 j in registers and every pick is a row-wide
+    // argmax (DPP within the row), so a pick costs no LDS round trip.
+    if (nblk - p.init <= 16 * kPickRegs) {
+        const int grp = lane >> 4, l16 = lane & 15;
+        for (int tb = 4 * wave; tb < ntok; tb += 4 * kSelectWaves) {
+            const int t = tb + grp;
+            const bool tv = t < ntok;
+            const int ct = tok0 + t + off;
+            int n = 0;
+            int pick[4] = {-1, -1, -1, -1};             // entry l16 + 16 s of the list
+            auto put = [&](int x) {
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+                    if (n == l16 + 16 * s4) pick[s4] = x;
+                ++n;
+            };
+            int lo = 0, hi = 0;
+            if (tv && ct >= 0) {
+                const int qb = ct / kSelBlock < nblk - 1 ? ct / kSelBlock : nblk - 1;
+                for (int x = 0; x < p.init && x <= qb && n < p.topk; ++x) put(x);
+                for (int y = 0; y < p.local && n < p.topk; ++y) {
+                    const int x = qb - y;
+                    if (x < 0) break;
+                    if (x >= p.init) put(x);            // (smaller ones are listed already)
+                }
+                lo = p.init;
+                hi = qb - p.local + 1;
+            }
+            const float* imp = s_imp + (tv ? t : 0) * nb;
+            float v[kPickRegs];
+#pragma unroll
+            for (int j = 0; j < kPickRegs; ++j) {
+                const int x = lo + l16 + 16 * j;
+                v[j] = x < hi ? imp[x] : -1.f;
+            }
+            bool go = n < p.topk && lo < hi;
+            while (__builtin_amdgcn_ballot_w64(go) != 0ull) {
+                unsigned long long key = 0ull;
+#pragma unroll
+                for (int j = 0; j < kPickRegs; ++j) {
+                    const unsigned long long kj =
+                        v[j] >= 0.f ? ((unsigned long long)__float_as_uint(v[j]) << 32) |
+                                          (0xFFFFFFFFu - (uint32_t)(lo + l16 + 16 * j))
+                                    : 0ull;
+                    key = kj > key ? kj : key;
+                }
+                key = row_max_u64(key);
+                if (go) {
+                    if (key == 0ull) {
+                        go = false;                     // no candidate left
+                    } else {
+                        const int x = (int)(0xFFFFFFFFu - (uint32_t)key);
+                        put(x);
+                        const int r = x - lo;
+#pragma unroll
+                        for (int j = 0; j < kPickRegs; ++j)
+                            if (l16 == (r & 15) && j == (r >> 4)) v[j] = -1.f;   // used
+                        go = n < p.topk;
+                    }
+                }
+            }
+            if (tv) {
+                int32_t* out = p.blk_idx + ((sb.q0 + tok0 + t) * p.Hkv + g) * (int64_t)p.topk;
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int e = l16 + 16 * s4;
+                    if (e < p.topk) out[e] = e < n ? pick[s4] : -1;
+                }
+            }
+        }
+        return;
+    }
+
+    // selection otherwise: one wave per token
     for (int t = wave; t < ntok; t += kSelectWaves) {
         int32_t* out = p.blk_idx + ((sb.q0 + tok0 + t) * p.Hkv + g) * (int64_t)p.topk;
         const int ct = tok0 + t + off;
