@@ -147,6 +147,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const SelBwdParams p) {
 // thousands of same-address global atomics.)
 constexpr int kIdxChunk = 256;
 constexpr int kIdxWin = 8192;
+constexpr int kIdxRegs = 16;
 
 template <bool FILL>
 __global__ void __launch_bounds__(kIdxChunk) bwd_index_kernel(const SelBwdParams p) {
@@ -167,6 +168,26 @@ __global__ void __launch_bounds__(kIdxChunk) bwd_index_kernel(const SelBwdParams
     int32_t* cnt = p.counts + (int64_t)unit * (p.nb_max + 1);
     int32_t* cur = p.cursor + (int64_t)unit * p.nb_max;
     const int64_t tbase = toks_base(p, sb, g);
+    // Lists of up to kIdxRegs entries are read once (16-byte loads) and
+    // filtered in registers; longer ones entry by entry from memory.
+    const bool in_regs = p.topk <= kIdxRegs && (p.topk & 3) == 0 && ((uintptr_t)p.blk_idx & 15) == 0;
+    int ids[kIdxRegs];
+    if (in_regs) {
+#pragma unroll
+        for (int e = 0; e < kIdxRegs; e += 4) {
+            int4 v = make_int4(-1, -1, -1, -1);
+            if (tok_ok && e < p.topk) v = *reinterpret_cast<const int4*>(lst + e);
+            ids[e] = v.x; ids[e + 1] = v.y; ids[e + 2] = v.z; ids[e + 3] = v.w;
+        }
+#pragma unroll
+        for (int e = 0; e < kIdxRegs; ++e) {
+            int id = ids[e];
+            bool ok = id >= 0 && id < nblk && !(p.causal && (long long)id * kBlockKeys > (long long)i + off);
+#pragma unroll
+            for (int e2 = 0; e2 < e; ++e2) ok = ok && ids[e2] != id;
+            ids[e] = ok ? id : -1;      // (the first copy of an id is kept iff it is valid)
+        }
+    }
     // an entry's id if it counts, else -1
     auto entry = [&](int e) -> int {
         const int id = lst[e];
@@ -176,15 +197,27 @@ __global__ void __launch_bounds__(kIdxChunk) bwd_index_kernel(const SelBwdParams
             if (lst[e2] == id) return -1;
         return id;
     };
+    // f(id) for every id of this thread's list that counts
+    auto each = [&](auto f) {
+        if (!tok_ok) return;
+        if (in_regs) {
+#pragma unroll
+            for (int e = 0; e < kIdxRegs; ++e)
+                if (ids[e] >= 0) f(ids[e]);
+        } else {
+            for (int e = 0; e < p.topk; ++e) {
+                const int id = entry(e);
+                if (id >= 0) f(id);
+            }
+        }
+    };
     for (int w0 = 0; w0 < nblk; w0 += kIdxWin) {
         const int wn = (nblk - w0) < kIdxWin ? (nblk - w0) : kIdxWin;
         for (int x = threadIdx.x; x < wn; x += kIdxChunk) hist[x] = 0;
         __syncthreads();
-        if (tok_ok)
-            for (int e = 0; e < p.topk; ++e) {
-                const int id = entry(e);
-                if (id >= w0 && id < w0 + wn) atomicAdd(&hist[id - w0], 1);
-            }
+        each([&](int id) {
+            if (id >= w0 && id < w0 + wn) atomicAdd(&hist[id - w0], 1);
+        });
         __syncthreads();
         for (int x = threadIdx.x; x < wn; x += kIdxChunk) {
             const int h = hist[x];
@@ -196,11 +229,9 @@ __global__ void __launch_bounds__(kIdxChunk) bwd_index_kernel(const SelBwdParams
         }
         if constexpr (FILL) {
             __syncthreads();
-            if (tok_ok)
-                for (int e = 0; e < p.topk; ++e) {
-                    const int id = entry(e);
-                    if (id >= w0 && id < w0 + wn) p.toks[tbase + atomicAdd(&hist[id - w0], 1)] = i;
-                }
+            each([&](int id) {
+                if (id >= w0 && id < w0 + wn) p.toks[tbase + atomicAdd(&hist[id - w0], 1)] = i;
+            });
         }
         __syncthreads();
     }
