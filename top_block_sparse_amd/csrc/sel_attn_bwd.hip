@@ -24,7 +24,7 @@
 //      operands of dV^T = dO^T P and dK^T = Q^T dS (after a fixed reordering of
 //      the 32 rows); dO^T and Q^T come from transposing LDS reads.
 //   4. bwd_dq: query-centric like the forward: a workgroup owns T tokens of
-//      one kv head (eight 16-row m-tiles, one per wave), builds the union of
+//      one kv head (ten 16-row m-tiles, one per compute wave), builds the union of
 //      their blocks and walks it block by block; S^T = K Q^T, dP^T = V dO^T,
 //      dS^T, then dQ^T += K^T dS^T with K^T read by transposing LDS reads.
 // The order in which a block's tokens are summed depends on atomic list
@@ -38,7 +38,7 @@ namespace {
 
 constexpr int kBwdRows = 32;            // query rows per dK/dV step
 constexpr int kBwdKvThreads = 256;      // 4 waves x 16 keys
-constexpr int kBwdDqWaves = 8;          // m-tiles (compute waves) per dq workgroup
+constexpr int kBwdDqWaves = 10;         // m-tiles (compute waves) per dq workgroup
 constexpr int kBwdDqProducers = 2;      // waves that only move K/V blocks into LDS
 constexpr int kBwdDqThreads = (kBwdDqWaves + kBwdDqProducers) * 64;
 constexpr int kBwdWin = 256;            // blocks per union-building window (dq)
