@@ -352,18 +352,22 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(vseq + blk * kBlockKeys * row_bytes), 0, nrec, 0x00020000);
         uint8_t* sl = smem + slot * L::kSlot;
+        // The window instantiation computes the per-lane offsets again per
+        // block: kept live across the loop they would spill to scratch there.
+        int ln = lane;
+        if constexpr (WIN) asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int x = 0; x < NIPW; ++x) {
             const int inst = first + x;                     // which 1 KiB of the slot
             int row, col;                                   // source key row, byte column
             if (inst < NIK) {                               // K fragment (kt, s)
                 const int kt = inst / KS, s = inst % KS;
-                row = kt * 16 + (lane & 15);
-                col = (4 * s + (lane >> 4)) * 16;
+                row = kt * 16 + (ln & 15);
+                col = (4 * s + (ln >> 4)) * 16;
             } else {                                        // V fragments 2q, 2q+1
-                const int f = 2 * (inst - NIK) + (lane >> 5);   // (2ks + h)*DT + dt
+                const int f = 2 * (inst - NIK) + (ln >> 5);   // (2ks + h)*DT + dt
                 const int dt = f % DT, kh = f / DT;             // kh = 2ks + h
-                const int fl = 2 * (lane & 31);                 // first fragment lane served
+                const int fl = 2 * (ln & 31);                 // first fragment lane served
                 const int flr = fl & 15, flg = fl >> 4;
                 row = 16 * kh + 4 * flg + (flr >> 2);
                 col = (dt * 16 + 4 * (flr & 3)) * 2;
