@@ -191,6 +191,23 @@ def test_prefill_all_lists_empty():
     assert np.all(out == 0.0) and np.all(lse == -np.inf)
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_prefill_idle_m_tiles(splits):
+    """Runs of tokens with empty lists next to tokens with long ones: some
+    m-tiles of a tile visit no block at all, others every block, so the ring
+    frees slots on per-block need counts well below the consumer count."""
+    dd = make_case((1200, 700), 8, 2, 128, 16, seed=41, mutate=False)
+    blk = dd["blk_idx"].numpy().copy()
+    total = blk.shape[0]
+    idle = (np.arange(total) // 5) % 3 == 1          # runs of 5 tokens (rows straddle m-tiles)
+    blk[idle] = -1
+    dd["blk_idx"] = torch.from_numpy(blk)
+    out, lse = run_prefill(dd, num_splits=splits)
+    ro, rl = oracle_prefill(dd)
+    assert np.all(out[idle] == 0.0) and np.all(np.isneginf(lse.T[idle]))
+    compare(out, lse, ro, rl, what=f"idle m-tiles, splits={splits}")
+
+
 def test_prefill_zero_batch():
     q = torch.zeros((0, 4, 64), dtype=torch.bfloat16, device=DEV)
     k = torch.zeros((0, 1, 64), dtype=torch.bfloat16, device=DEV)
@@ -521,6 +538,23 @@ def test_bwd_shapes_with_index_edge_cases(case):
     ref = oracle.selected_attn_bwd(dd["q"], dd["k"], dd["v"], do, dd["blk_idx"],
                                    dd["cu_seqlens_q"], dd["cu_seqlens_k"], 64)
     compare_grads(got, ref, what=str(case))
+
+
+def test_bwd_idle_m_tiles():
+    """Runs of tokens with empty lists: some dQ compute waves visit no block,
+    and those rows get zero gradients."""
+    spec = inputs.PrefillSpec("b", (900, 400), 8, 2, 128, 16, seed=43)
+    dd = inputs.make_prefill(spec)
+    blk = dd["blk_idx"].numpy().copy()
+    idle = (np.arange(blk.shape[0]) // 7) % 3 == 2
+    blk[idle] = -1
+    dd["blk_idx"] = torch.from_numpy(blk)
+    do = inputs.randn_bf16(tuple(dd["q"].shape), 9400)
+    got = run_bwd(dd, do)
+    assert np.all(got[0][idle] == 0.0)
+    ref = oracle.selected_attn_bwd(dd["q"], dd["k"], dd["v"], do, dd["blk_idx"],
+                                   dd["cu_seqlens_q"], dd["cu_seqlens_k"], 64)
+    compare_grads(got, ref, what="idle m-tiles")
 
 
 def test_bwd_not_causal():
