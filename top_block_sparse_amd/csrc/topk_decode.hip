@@ -24,8 +24,10 @@
 //   3. the waves stream the workgroup's part in batches of 4*kDecUnroll
 //      entries taken from a shared counter (so they finish together):
 //      sixteen lanes cover one row (16 or 8 bytes each), so a wave loads four
-//      rows per instruction and keeps kDecUnroll such groups of K and V in
-//      flight; each lane group runs its own online softmax; the probabilities are
+//      rows per instruction; a batch is kDecUnroll such groups of K and V, and
+//      each wave keeps two batches in flight (the next one's loads go out
+//      before the current one is consumed); each lane group runs its own
+//      online softmax; the probabilities are
 //      rounded to bf16 for the P.V products (bf16 dot2 with fp32
 //      accumulation), the row sums stay fp32;
 //   4. the lane groups, then the waves, are merged by logsumexp in LDS, and
@@ -36,7 +38,7 @@
 
 namespace fsa {
 
-constexpr int kDecUnroll = 8;            // row groups per batch (halved for G > 4)
+constexpr int kDecUnroll = 4;            // row groups per batch (halved for G > 4)
 constexpr int kDecWavesSmallG = 8;       // waves per workgroup for G <= 4
 constexpr int kDecMaxTopk = 8192;
 constexpr int kDecBtLds = 2048;          // block-table rows up to this length are staged in LDS
@@ -373,12 +375,29 @@ decode_kernel(const DecodeParams p) {
         if (lane == 0) t = __hip_atomic_fetch_add(next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         return __builtin_amdgcn_readfirstlane(t);
     };
+    // two batches in flight per wave: the next one's loads are issued before
+    // the current one is consumed
+    uint32_t kb[U][RW], vb[U][RW];
+    int bn = bi < nbatch ? grab() : nbatch;
+    if (bn < nbatch) issue(kb, vb, r_lo + bn * B);
     while (bi < nbatch) {
-        const uint32_t okm = okmask(r_lo + bi * B);
-        const int bn = grab();                   // next batch, fetched while the loads fly
-        consume(ka, va, okm);
-        bi = bn;
-        if (bi < nbatch) issue(ka, va, r_lo + bi * B);
+        {
+            const uint32_t okm = okmask(r_lo + bi * B);
+            const int bn2 = bn < nbatch ? grab() : nbatch;
+            consume(ka, va, okm);
+            if (bn2 < nbatch) issue(ka, va, r_lo + bn2 * B);
+            bi = bn;
+            bn = bn2;
+        }
+        if (bi >= nbatch) break;
+        {
+            const uint32_t okm = okmask(r_lo + bi * B);
+            const int bn2 = bn < nbatch ? grab() : nbatch;
+            consume(kb, vb, okm);
+            if (bn2 < nbatch) issue(kb, vb, r_lo + bn2 * B);
+            bi = bn;
+            bn = bn2;
+        }
     }
 
     // ---- 4. merge the wave's four lane groups, then the workgroup's waves.
