@@ -163,8 +163,10 @@ __global__ void __launch_bounds__(256) cmp_keys_kernel(const BlockSelectParams p
 // lane l's 16 bytes = C[16kt + l%16][32s + 8(l/16) .. +8] -- so every operand
 // read is one contiguous wave read.  The chunk is loaded once per workgroup
 // (all waves share it), the next one while the current one is used.
+// Six waves per SIMD (80 VGPRs): three workgroups share a CU, as the LDS
+// allows; at the compiler's own choice of 92 VGPRs only two fit.
 template <int D>
-__global__ void __launch_bounds__(kSelectThreads) block_select_kernel(const BlockSelectParams p) {
+__global__ void __launch_bounds__(kSelectThreads, 6) block_select_kernel(const BlockSelectParams p) {
     constexpr int KS = D / 32;
     constexpr int CPR = D / 8;                                   // 16-byte pieces per window
     constexpr int kChunkBytes = kWinChunk * D * 2;
