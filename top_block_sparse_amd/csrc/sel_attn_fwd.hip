@@ -142,7 +142,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: role branches are scalar
     const int lr = lane & 15;        // MFMA column = query row within the m-tile
     const int lg = lane >> 4;        // lane group 0..3
 
