@@ -89,6 +89,12 @@ struct SelLds {
     }
 };
 
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long x, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
 __device__ __forceinline__ float lane_max4(float x) {
     // max over lanes l, l^16, l^32, l^48 (the four lanes holding one query row)
     auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -509,15 +515,18 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
 #pragma unroll 1
             for (int k = 0; k < kSelWin / 64; ++k) {
                 const int x = 64 * k + lane;
-                const unsigned long long m = (x >= u_beg && x < u_end) ? s_umask[x] : 0ull;
+                const bool in = x >= u_beg && x < u_end;
+                const unsigned long long m = in ? s_umask[x] : 0ull;
+                const int ul = in ? s_ulist[x] : 0;       // block ids of the 64 positions
                 unsigned long long bits = __builtin_amdgcn_ballot_w64((m & mt_tok) != 0ull);
                 while (bits != 0ull) {
-                    const int u = 64 * k + (int)__builtin_ctzll(bits);
+                    const int bitp = (int)__builtin_ctzll(bits);
+                    const int u = 64 * k + bitp;
                     bits &= bits - 1ull;
                     const uint32_t seq = seq0 + (uint32_t)(u - u_beg);
                     const int slot = (int)(seq % (uint32_t)ring);
-                    const int blk = __builtin_amdgcn_readfirstlane(s_ulist[u]);
-                    const unsigned long long bm = uniform_u64(s_umask[u]);
+                    const int blk = __builtin_amdgcn_readlane(ul, bitp);
+                    const unsigned long long bm = readlane_u64(m, bitp);
                     for (int sp = 0; sp < kSpinLimit; ++sp) {
                         const u32x2_t r = lds_load2_sync(s_ready + slot * kSelProducers);
                         if (r[0] >= seq + 1 && r[1] >= seq + 1) break;
