@@ -304,6 +304,7 @@ DECODE_SHAPES = [
     (2, 6, 2, 64, 700, 100, 200),      # G = 3, page size not a power of two
     (5, 32, 8, 128, 2048, 256, 2048),
     (1, 8, 1, 128, 9000, 512, 8192),   # largest topk
+    (3, 4, 2, 128, 1500, 128, 512),    # G = 2
 ]
 
 
@@ -521,6 +522,8 @@ BWD_SHAPES = [
     ((300,), (200,), 8, 8, 128, 8),                # S_k < S_q: early rows see nothing
     ((900,), None, 4, 4, 128, 16),                 # G = 1
     ((257,), None, 64, 2, 128, 5),                 # G = 32
+    ((600, 130), None, 8, 4, 128, 12),             # G = 2
+    ((500,), None, 16, 2, 64, 8),                  # G = 8
 ]
 
 
