@@ -342,6 +342,15 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
                 acc[dt] = mfma_16x16x32(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pb[ks], acc[dt]);
             }
         }
+        // schedule the transposing reads two MFMAs ahead (4 reads, then one
+        // MFMA and two reads at a time) instead of waiting for each pair
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int x = 0; x < 2 * DT - 2; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     };
 
     // ---- producer: block -> ring slot with buffer->LDS loads
@@ -349,7 +358,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     const int64_t row_bytes = (int64_t)p.Hkv * D * 2;
     const uint8_t* kseq = reinterpret_cast<const uint8_t*>(p.k + (k0 * p.Hkv + g) * (int64_t)D);
     const uint8_t* vseq = reinterpret_cast<const uint8_t*>(p.v + (k0 * p.Hkv + g) * (int64_t)D);
-    auto produce = [&](auto nip_c, int first, int blk, int slot) {
+    auto produce = [&](auto nip_c, int first, int blk, int slot, int ln) {
         constexpr int NIPW = decltype(nip_c)::value;
         const int rows = Sk - blk * kBlockKeys < kBlockKeys ? Sk - blk * kBlockKeys : kBlockKeys;
         const uint32_t nrec = (uint32_t)((rows - 1) * row_bytes + D * 2);
@@ -360,7 +369,6 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         uint8_t* sl = smem + slot * L::kSlot;
         // The window instantiation computes the per-lane offsets again per
         // block: kept live across the loop they would spill to scratch there.
-        int ln = lane;
         if constexpr (WIN) asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int x = 0; x < NIPW; ++x) {
@@ -464,6 +472,11 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
             // issued before waiting for a slot, so that a slow consumer never
             // holds back blocks that have already landed
             int pub = 0;                                  // next block to publish
+            // the lane index, opaque here: the per-lane DMA offsets derived
+            // from it are computed in this branch (once per window) and so
+            // occupy no registers in the consumers' branch
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
             int ul_v = 0, nc_v = 0;                       // union ids / need counts, 64 at a time
             for (int i = 0; i < n; ++i) {
                 if ((i & 63) == 0) {
@@ -492,9 +505,9 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
                 tgt2 += slot == 2 ? nc : 0u;
                 tgt3 += slot == 3 ? nc : 0u;
                 if (pw == 0)
-                    produce(std::integral_constant<int, NIP0>{}, 0, blk, slot);
+                    produce(std::integral_constant<int, NIP0>{}, 0, blk, slot, ln);
                 else
-                    produce(std::integral_constant<int, NIP1>{}, NIP0, blk, slot);
+                    produce(std::integral_constant<int, NIP1>{}, NIP0, blk, slot, ln);
                 if (i - pub == kSelDepth - 1) {           // exactly kSelDepth - 1 blocks issued after pub
                     if (pw == 0)
                         wait_vmcnt<NIP0 * (kSelDepth - 1)>();
