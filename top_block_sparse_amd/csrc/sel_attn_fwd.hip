@@ -560,7 +560,12 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     // ---- epilogue: normalise, write O (bf16) and LSE, or the split partials
     if (consumer && mt < p.mtiles) {
         const float l = lane_sum4(l_run);
-        const int row = mt * 16 + lr;
+        // The lane index is made opaque so the output addresses are recomputed
+        // here rather than kept live (and spilled) across the ring loop.
+        int eln = lane;
+        asm volatile("" : "+v"(eln));
+        const int lg = eln >> 4;
+        const int row = mt * 16 + (eln & 15);
         const int tl = row / G;
         const int hh = row - tl * G;
         if (tl < ntok) {
