@@ -583,6 +583,54 @@ def test_bwd_medium_gqa_workload():
     compare_grads(got, ref, what="medium")
 
 
+
+def test_bwd_full_size_bench_workload():
+    """The backward at B=2, S=8192, Hq=32, Hkv=8, d=128, topk 16, launched as the
+    benchmark launches it.  The oracle cannot run the whole problem in a test, so:
+
+    * dQ of a row depends on that row alone, and under the causal mask with
+      S_q = S_k the first 2048 tokens of a sequence form a problem of their own;
+      the oracle runs on those prefixes and every dQ element of them is compared.
+    * Every softmax row has sum_j dS_ij = 0, so per (sequence, kv head) the dK
+      rows sum to zero and the dV rows sum to the dO rows of the group's heads
+      (every row sees key 0 here).  Both bounds allow the bf16 rounding of each
+      stored gradient element (2^-9 relative) plus fp32 accumulation.
+    """
+    spec = inputs.PREFILL_WORKLOADS["prefill_b2_s8192_h32_kv8_d128_top16"]
+    print("[gpu] backward full size: generating inputs", flush=True)
+    dd = inputs.make_prefill(spec)
+    do = inputs.randn_bf16(tuple(dd["q"].shape), 9999)
+    print("[gpu] backward full size: HIP path", flush=True)
+    dq, dk, dv = run_bwd(dd, do)
+    for nm, a in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert np.isfinite(a).all(), nm
+    cu = dd["cu_seqlens_q"].numpy().astype(np.int64)
+    Hq, Hkv = dq.shape[1], dk.shape[1]
+    G = Hq // Hkv
+    dof = do.float().numpy().astype(np.float64)
+    for b in range(cu.size - 1):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        for g in range(Hkv):
+            k64 = dk[lo:hi, g].astype(np.float64)
+            v64 = dv[lo:hi, g].astype(np.float64)
+            want_v = dof[lo:hi, g * G:(g + 1) * G].sum(axis=(0, 1))
+            tol_k = 2.0 ** -9 * np.abs(k64).sum(axis=0) + 1e-3
+            tol_v = 2.0 ** -9 * np.abs(v64).sum(axis=0) + 1e-3
+            assert (np.abs(k64.sum(axis=0)) <= tol_k).all(), ("sum dK", b, g)
+            assert (np.abs(v64.sum(axis=0) - want_v) <= tol_v).all(), ("sum dV", b, g)
+    n = 2048
+    rows = np.concatenate([np.arange(int(c), int(c) + n) for c in cu[:-1]])
+    sub = {x: dd[x][torch.from_numpy(rows)] for x in ("q", "k", "v", "blk_idx")}
+    cu_sub = torch.arange(0, (cu.size - 1) * n + 1, n, dtype=torch.int32)
+    print(f"[gpu] backward full size: oracle on the first {n} tokens of each sequence", flush=True)
+    rq, _, _ = oracle.selected_attn_bwd(sub["q"], sub["k"], sub["v"], do[torch.from_numpy(rows)],
+                                        sub["blk_idx"], cu_sub, cu_sub, 64)
+    a = dq[rows]
+    e = np.abs(a - rq)
+    assert (e / (1.0 + np.abs(rq))).max() <= G_REL
+    assert e.mean() <= G_MEAN * max(np.abs(rq).mean(), 1e-3)
+
+
 # ------------------------------------------------------------------ block-index producer
 # The lists are integers decided by floating point: the GPU scores blocks in
 # fp32 (MFMA over the same bf16 compressed keys the oracle rounds to), the
