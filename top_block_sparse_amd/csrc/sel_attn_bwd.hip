@@ -833,7 +833,7 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
             for (int sp = 0; sp < kSpinLimit; ++sp) {
                 const u32x2_t r = lds_load2_sync(s_ready + slot * kBwdDqProducers);
                 if (r[0] >= seq + 1 && r[1] >= seq + 1) break;
-                __builtin_amdgcn_s_sleep(1);
+                __builtin_amdgcn_s_sleep(4);
             }
             const uint8_t* kslot = smem + slot * L::kSlot;
             const uint8_t* vslot = kslot + L::kPart;

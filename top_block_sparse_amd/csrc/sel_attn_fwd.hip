@@ -543,7 +543,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
                     for (int sp = 0; sp < kSpinLimit; ++sp) {
                         const u32x2_t r = lds_load2_sync(s_ready + slot * kSelProducers);
                         if (r[0] >= seq + 1 && r[1] >= seq + 1) break;
-                        __builtin_amdgcn_s_sleep(1);
+                        __builtin_amdgcn_s_sleep(4);
                     }
                     compute(smem + slot * L::kSlot, blk, bm);
                     // done with the slot: its reads have completed before the count
