@@ -779,6 +779,7 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
         // over the tile.  Every wait is bounded.
         if (wave >= kBwdDqWaves) {
             int pub = 0;                                  // next block to publish
+            __builtin_amdgcn_s_setprio(2);   // DMA issue wins the SIMD's arbitration
             int ul_v = 0, nc_v = 0;                       // union ids / need counts, 64 at a time
             for (int i = 0; i < n_u; ++i) {
                 if ((i & 63) == 0) {
@@ -835,6 +836,7 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
                 if (r[0] >= seq + 1 && r[1] >= seq + 1) break;
                 __builtin_amdgcn_s_sleep(4);
             }
+            __builtin_amdgcn_s_setprio(1);   // a computing wave goes before polling ones
             const uint8_t* kslot = smem + slot * L::kSlot;
             const uint8_t* vslot = kslot + L::kPart;
             {
@@ -889,6 +891,7 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
                 }
             }
             // done with the slot: its reads have completed before the count
+            __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             if (lane == 0) __hip_atomic_fetch_add(s_done + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           }

@@ -476,6 +476,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
             // from it are computed in this branch (once per window) and so
             // occupy no registers in the consumers' branch
             int ln = lane;
+            __builtin_amdgcn_s_setprio(2);   // DMA issue wins the SIMD's arbitration
             asm volatile("" : "+v"(ln));
             int ul_v = 0, nc_v = 0;                       // union ids / need counts, 64 at a time
             for (int i = 0; i < n; ++i) {
@@ -545,7 +546,9 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
                         if (r[0] >= seq + 1 && r[1] >= seq + 1) break;
                         __builtin_amdgcn_s_sleep(4);
                     }
+                    __builtin_amdgcn_s_setprio(1);   // a computing consumer goes before polling ones
                     compute(smem + slot * L::kSlot, blk, bm);
+                    __builtin_amdgcn_s_setprio(0);
                     // done with the slot: its reads have completed before the count
                     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
                     if (lane == 0) __hip_atomic_fetch_add(s_done + slot, 1u, __ATOMIC_RELAXED,
