@@ -28,7 +28,9 @@
 // random selections evens out over the tile instead of costing a barrier per
 // block, and a block no token of an m-tile chose costs that m-tile nothing.
 // Every wait is a bounded spin, so a logic error can only produce wrong
-// values, never a hung GPU.
+// values, never a hung GPU.  Waiting consumers sleep between polls; a
+// consumer computes at raised wave priority and the producers run higher
+// still, so a SIMD issues DMA first, then MFMA work, then polls.
 //
 // Per m-tile and block the contraction runs transposed, S^T = K * Q^T with
 // v_mfma_f32_16x16x32_bf16: the key index is the MFMA row, the query row the
