@@ -134,6 +134,9 @@ SHAPES = [
     ((130, 400), 4, 1, 64, 3, (70, 400)),              # S_q > S_k: leading rows see nothing
     ((2100,), 8, 2, 128, 64, None),                    # largest topk
     ((0, 300, 0), 4, 2, 64, 5, None),                  # empty sequences around a real one
+    ((800,), 4, 2, 128, 10, None),                     # G = 2
+    ((260,), 64, 1, 64, 6, None),                      # G = 64: a token spans 4 m-tiles
+    ((130, 70), 224, 1, 64, 5, None),                  # G = 224, the largest group: one token per tile
 ]
 
 
