@@ -450,6 +450,8 @@ WINDOW_CASES = [
     ((600,), None, 8, 1, 64, (-1, 0)),             # causal
     ((333,), (250,), 4, 2, 128, (-1, -1)),         # global
     ((2000,), None, 32, 2, 128, (1023, 0)),        # G = 16 wide window
+    ((300,), None, 64, 1, 64, (127, 0)),           # G = 64
+    ((150, 40), None, 224, 1, 64, (63, 5)),        # G = 224, the largest group
 ]
 
 
