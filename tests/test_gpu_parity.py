@@ -698,6 +698,7 @@ SELECT_SHAPES = [
     ((2048,), None, 64, 1, 64, 32, 1, 2),              # group of 64 (one token per tile)
     ((8256,), None, 2, 1, 64, 48, 1, 2),               # 128 candidates (row-wise picks), 48 entries
     ((8320,), None, 2, 1, 64, 20, 1, 1),               # 129 candidates (one wave per token)
+    ((4200,), None, 128, 1, 64, 64, 1, 2),             # the largest group and topk
 ]
 
 
