@@ -529,6 +529,7 @@ BWD_SHAPES = [
     ((257,), None, 64, 2, 128, 5),                 # G = 32
     ((600, 130), None, 8, 4, 128, 12),             # G = 2
     ((500,), None, 16, 2, 64, 8),                  # G = 8
+    ((2100,), None, 8, 2, 128, 64),                # the largest topk
 ]
 
 
