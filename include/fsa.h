@@ -20,7 +20,9 @@
  *   and a repeated id counts once (the lists are sets).  A query row that
  *   ends up with no visible key gets O = 0 and LSE = -inf.
  * - softmax_scale <= 0 selects the default 1/sqrt(head_dim).
- * - Calls are thread-safe: there is no global mutable state.
+ * - Calls are thread-safe.  The only process-wide state is diagnostic: the
+ *   poll limit of the kernels' bounded waits (fsa_set_wait_poll_limit) and a
+ *   device counter of waits that gave up (fsa_wait_timeouts).
  *
  * Semantics follow the pages this library is built from:
  * - GQA: query head h reads kv head h / (num_heads_q / num_heads_kv);
@@ -65,6 +67,27 @@ const char* fsa_status_string(fsa_status_t status);
 
 /* FSA_ABI_VERSION of the built library. */
 int32_t fsa_abi_version(void);
+
+/*
+ * Diagnostics of the bounded waits inside the prefill, window and backward
+ * kernels.  Their producer and consumer waves hand K/V blocks over through
+ * LDS flags; every wait polls a bounded number of times, so an error in that
+ * hand-over can never hang the GPU.  A wave whose wait runs out gives up for
+ * good (its workgroup stops waiting and its results are wrong) and adds one
+ * to a counter in device memory of the current device.
+ *
+ * fsa_wait_timeouts: *count = that counter (0 after correct runs); a nonzero
+ *   reset clears it.  Synchronous (a device-to-host copy on the null stream);
+ *   FSA_ERROR_INVALID_VALUE for a NULL count, FSA_ERROR_LAUNCH if the copy
+ *   fails.
+ * fsa_set_wait_poll_limit: the number of polls a wait makes before it gives
+ *   up, for calls enqueued afterwards by any thread; 0 restores the default
+ *   (2^22, about half a second; a wait normally ends within ~1e3 polls).  A
+ *   tiny limit makes waits give up on purpose, which exercises this path
+ *   without any out-of-bounds access.  FSA_ERROR_INVALID_VALUE if negative.
+ */
+fsa_status_t fsa_wait_timeouts(uint32_t* count, int32_t reset);
+fsa_status_t fsa_set_wait_poll_limit(int32_t polls);
 
 /*
  * Bytes of device workspace fsa_selected_attn_fwd needs for these arguments
@@ -192,6 +215,17 @@ int32_t fsa_topk_decode_auto_splits(int32_t batch, int32_t num_heads_q, int32_t 
 /*
  * Top-k gathered decode over a paged KV cache: one query token per sequence
  * attends to the cache positions listed for its kv head.
+ *
+ * Defining passages: the flash-sparse-attn page's feature list (main
+ * features: top-k gather KV-cache decoding, paged attention, split-KV for
+ * decode load balance) and its decode example (a [batch, heads, head_dim]
+ * query against the cache); the flash-attention-npu page's
+ * flash_attn_with_kvcache docstring for the paged layout (k_cache / v_cache
+ * [num_blocks, page_block_size, nheads_k, headdim] with block_table
+ * [batch, max_num_blocks_per_seq]), cache_seqlens, softmax_scale, num_splits
+ * and the (batch, nheads) softmax_lse; the Ascend SFA blog for the -1
+ * invalid index and gather-then-attend.  The list is read as a set of
+ * positions (a selection), like the prefill's block lists.
  *
  *   q          bf16 [batch, num_heads_q, head_dim]
  *   k_cache, v_cache  bf16 [num_pages, page_size, num_heads_kv, head_dim]

@@ -12,6 +12,7 @@ q/k/v, int32 for indices) and return float64 numpy arrays.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -37,40 +38,79 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def _bind(path: str) -> ctypes.CDLL:
+    """Open an oracle shared library and declare its entry points."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.oracle_selected_attn_fwd.restype = ctypes.c_int
+    lib.oracle_selected_attn_fwd.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                             f64, i32, P, i64, P, P]
+    lib.oracle_topk_decode.restype = ctypes.c_int
+    lib.oracle_topk_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                       i32, f64, P, i64, P, P]
+    lib.oracle_selected_attn_bwd.restype = ctypes.c_int
+    lib.oracle_selected_attn_bwd.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                             i32, f64, i32, P, P, P]
+    lib.oracle_window_attn_fwd.restype = ctypes.c_int
+    lib.oracle_window_attn_fwd.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, i64, f64,
+                                           P, i64, P, P]
+    lib.oracle_topk_decode_fp8.restype = ctypes.c_int
+    lib.oracle_topk_decode_fp8.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                           i32, i32, i32, f64, P, i64, P, P]
+    lib.oracle_e4m3_value.restype = f64
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_lse_merge.restype = None
+    lib.oracle_lse_merge.argtypes = [i64, i32, P, P, P, P]
+    lib.oracle_block_select.restype = ctypes.c_int
+    lib.oracle_block_select.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32,
+                                        i32, i32, f64, P, i64, P, P]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_set_threads.restype = None
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build(force=False)
-        lib = ctypes.CDLL(_LIB_PATH)
-        P = ctypes.c_void_p
-        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
-        lib.oracle_selected_attn_fwd.restype = ctypes.c_int
-        lib.oracle_selected_attn_fwd.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
-                                                 f64, i32, P, i64, P, P]
-        lib.oracle_topk_decode.restype = ctypes.c_int
-        lib.oracle_topk_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
-                                           i32, f64, P, i64, P, P]
-        lib.oracle_selected_attn_bwd.restype = ctypes.c_int
-        lib.oracle_selected_attn_bwd.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
-                                                 i32, f64, i32, P, P, P]
-        lib.oracle_window_attn_fwd.restype = ctypes.c_int
-        lib.oracle_window_attn_fwd.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i64, i64, f64,
-                                               P, i64, P, P]
-        lib.oracle_topk_decode_fp8.restype = ctypes.c_int
-        lib.oracle_topk_decode_fp8.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
-                                               i32, i32, i32, f64, P, i64, P, P]
-        lib.oracle_e4m3_value.restype = f64
-        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
-        lib.oracle_lse_merge.restype = None
-        lib.oracle_lse_merge.argtypes = [i64, i32, P, P, P, P]
-        lib.oracle_block_select.restype = ctypes.c_int
-        lib.oracle_block_select.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32,
-                                            i32, i32, f64, P, i64, P, P]
-        lib.oracle_max_threads.restype = ctypes.c_int
-        lib.oracle_max_threads.argtypes = []
-        _lib = lib
+        _lib = _bind(_LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Run the wrappers on another build of the oracle source (a copy with a
+    deliberately planted mistake, compiled by a test to show that a pin
+    rejects it); the regular library is restored afterwards."""
+    global _lib
+    saved = _load()
+    _lib = _bind(path)
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def build_variant(source_text: str, out_dir: str, name: str = "liboracle_variant.so") -> str:
+    """Compile ``source_text`` (a modified copy of fsa_oracle.c) like
+    ``build()`` into ``out_dir``; returns the library path."""
+    src = os.path.join(out_dir, name.replace(".so", ".c"))
+    with open(src, "w") as f:
+        f.write(source_text)
+    lib = os.path.join(out_dir, name)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", src, "-o", lib,
+                    "-lm"], check=True)
+    return lib
+
+
+def source() -> str:
+    """The text of fsa_oracle.c."""
+    with open(_SRC) as f:
+        return f.read()
 
 
 def _bits(t: torch.Tensor) -> torch.Tensor:
@@ -86,6 +126,11 @@ def _i32(t) -> np.ndarray:
 
 def max_threads() -> int:
     return int(_load().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of later oracle calls (n <= 0: all cores)."""
+    _load().oracle_set_threads(int(n))
 
 
 def selected_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, blk_idx,

@@ -112,6 +112,15 @@ int oracle_max_threads(void) {
 #endif
 }
 
+/* Threads later oracle calls use (n <= 0: every core OpenMP sees). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : omp_get_num_procs());
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Prefill.  q [total_q, Hq, d], k/v [total_k, Hkv, d] (bf16 bits),
  * blk_idx [total_q, Hkv, topk], cu_q/cu_k [batch + 1].
@@ -532,8 +541,11 @@ int oracle_topk_decode_fp8(const uint16_t* q, const uint8_t* k_cache, const uint
  *  1. Compressed keys.  Window j of a sequence covers keys
  *     [j*stride, j*stride + ksize); windows exist while they fit inside the
  *     sequence.  Its summary is the mean of its ksize keys (per kv head) --
- *     the weight-free form of a learned summary -- rounded to bf16, the
- *     precision in which the kernel takes the selection decision.
+ *     the weight-free form of a learned summary -- stored as bf16 with
+ *     round-to-nearest-even: the quick start runs the whole module, and so
+ *     every tensor it forms, compressed keys included, in torch.bfloat16
+ *     (module .to(torch.bfloat16), bf16 input x), and torch's cast to bf16
+ *     rounds to nearest even.
  *  2. Compressed attention.  Row (token i, q head h) sees window j when the
  *     whole window lies in its causal past: j*stride + ksize - 1 <= i + S_k -
  *     S_q.  p_j = softmax over the visible windows of scale * <q, c_j>; a row

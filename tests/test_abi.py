@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     assert sorted(names) == sorted(_lib.EXPORTS)
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
@@ -291,3 +291,10 @@ def test_block_select_workspace(lib):
     assert f(2, 31, 8, 128, 32, 16) == 0           # no window fits
     assert f(2, 8192, 8, 96, 32, 16) == 0
     assert select(lib, batch=0, q=None) == 0
+
+
+def test_wait_diagnostics_reject_bad_arguments(lib):
+    """Argument checks of the bounded-wait diagnostics (no device access)."""
+    assert lib.fsa_set_wait_poll_limit(-1) == INVALID
+    assert lib.fsa_wait_timeouts(None, 0) == INVALID
+    assert lib.fsa_set_wait_poll_limit(0) == 0          # default restored

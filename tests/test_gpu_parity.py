@@ -28,6 +28,18 @@ def _device():
     yield
 
 
+@pytest.fixture(autouse=True)
+def _no_wait_timeouts(request):
+    """No bounded ring wait may give up in a correct run."""
+    torch.cuda.synchronize()
+    fsa.fsa_wait_timeouts(reset=True)
+    yield
+    if "forced_wait_timeouts" in request.node.name:
+        return
+    torch.cuda.synchronize()
+    assert fsa.fsa_wait_timeouts(reset=True) == 0, "a ring wait gave up"
+
+
 DEV = "cuda:0"
 
 
@@ -452,6 +464,8 @@ WINDOW_CASES = [
     ((2000,), None, 32, 2, 128, (1023, 0)),        # G = 16 wide window
     ((300,), None, 64, 1, 64, (127, 0)),           # G = 64
     ((150, 40), None, 224, 1, 64, (63, 5)),        # G = 224, the largest group
+    ((300,), (100,), 4, 2, 128, (-1, 200)),        # S_q > S_k, right bound > S_k still cuts rows
+    ((300, 90), (100, 20), 8, 4, 64, (40, 150)),   # the same with a left bound, two sequences
 ]
 
 
@@ -761,3 +775,37 @@ def test_block_select_full_size(name):
     exact = check_select(got, ref, sc, cu_q, dd["cu_seqlens_k"].numpy(), toks, 1, 2,
                          spec.num_heads_q // spec.num_heads_kv, name)
     assert exact >= 0.95 * toks.size * spec.num_heads_kv, exact
+
+
+# ------------------------------------------------------------------ bounded waits
+
+def test_forced_wait_timeouts_are_counted_and_end_quickly():
+    """With a poll limit of 1 the ring waits of the prefill and backward give
+    up at once (the results are then wrong, every access stays in bounds):
+    each call still ends, the device counter records the give-ups, and with
+    the default limit restored a call is correct again and counts nothing."""
+    dd = make_case((700, 300), 8, 2, 128, 16, seed=5, mutate=False)
+    g = to_dev(dd, ("q", "k", "v", "blk_idx", "cu_seqlens_q", "cu_seqlens_k"))
+    args = (g["q"], g["k"], g["v"], g["blk_idx"], g["cu_seqlens_q"], g["cu_seqlens_k"],
+            dd["max_seqlen_q"], dd["max_seqlen_k"])
+    torch.cuda.synchronize()
+    fsa.fsa_wait_timeouts(reset=True)
+    try:
+        fsa.fsa_set_wait_poll_limit(1)
+        out, lse = fsa.fsa_selected_attn_fwd(*args)
+        torch.cuda.synchronize()
+        n_fwd = fsa.fsa_wait_timeouts(reset=True)
+        do = torch.randn_like(out)
+        fsa.fsa_selected_attn_bwd(g["q"], g["k"], g["v"], out, lse, do, g["blk_idx"],
+                                  g["cu_seqlens_q"], g["cu_seqlens_k"], dd["max_seqlen_q"],
+                                  dd["max_seqlen_k"])
+        torch.cuda.synchronize()
+        n_bwd = fsa.fsa_wait_timeouts(reset=True)
+    finally:
+        fsa.fsa_set_wait_poll_limit(0)
+    print(f"[gpu] forced give-ups: forward {n_fwd}, backward {n_bwd}", flush=True)
+    assert n_fwd > 0 and n_bwd > 0
+    o, l = run_prefill(dd)
+    ro, rl = oracle_prefill(dd)
+    compare(o, l, ro, rl, what="default poll limit restored")
+    assert fsa.fsa_wait_timeouts(reset=True) == 0

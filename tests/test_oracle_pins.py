@@ -854,3 +854,60 @@ def test_block_select_rejects_bad_arguments():
                {"init_blocks": -1}, {"local_blocks": -1}):
         with pytest.raises(ValueError):
             oracle.block_select(q, k, cu, cu, **kw)
+
+
+def _summary_pin_error():
+    """Largest relative gap between the oracle's block importances and the same
+    importances built from library routines with bf16 summaries:
+    ``avg_pool1d`` (kernel 32, stride 16: the windows that fit) in float64 for
+    the window means, torch's cast to bfloat16 (round to nearest even), a
+    float64 softmax over the windows wholly in each row's causal past,
+    ``conv_transpose1d`` with a 32-wide box of 1/32 (stride 16) to spread each
+    window's probability over its keys, and a sum over each block's keys and
+    the group's heads.  Keys are N(0, 1) bf16 draws, whose 32-key means are
+    almost never bf16 values, so the rounding decides the result."""
+    G, Hkv, d, S, ks, st, bs = 2, 2, 32, 700, 32, 16, 64
+    q = rand_bf16((S, G * Hkv, d), 71)
+    k = rand_bf16((S, Hkv, d), 72)
+    cu = np.array([0, S], dtype=np.int32)
+    _, sc = oracle.block_select(q, k, cu, cu, ks, st, bs, 8, 1, 2, with_scores=True)
+    x = k.to(torch.float64).permute(1, 2, 0)                          # [Hkv, d, S]
+    mean = torch.nn.functional.avg_pool1d(x, kernel_size=ks, stride=st)  # [Hkv, d, ncmp]
+    c = mean.to(torch.bfloat16).to(torch.float64)
+    ncmp = c.shape[2]
+    cg = c.repeat_interleave(G, dim=0)                                # [Hq, d, ncmp]
+    s = torch.einsum("ihd,hdj->hij", q.to(torch.float64), cg) / math.sqrt(d)
+    vis = (st * torch.arange(ncmp)[None, :] + ks - 1) <= torch.arange(S)[:, None]
+    p = torch.softmax(s.masked_fill(~vis, float("-inf")), dim=-1)
+    p = torch.nan_to_num(p, nan=0.0)                                  # rows with no window
+    box = torch.full((1, 1, ks), 1.0 / ks, dtype=torch.float64)
+    per_key = torch.nn.functional.conv_transpose1d(p.reshape(-1, 1, ncmp), box, stride=st)
+    nblk = (S + bs - 1) // bs
+    per_key = torch.nn.functional.pad(per_key, (0, nblk * bs - per_key.shape[-1]))
+    imp = per_key.reshape(Hkv, G, S, nblk, bs).sum(dim=(1, 4)).permute(1, 0, 2)
+    # the pin has power only if the rounding moves many summaries
+    exact = (mean.to(torch.bfloat16).to(torch.float64) == mean).double().mean().item()
+    assert exact < 0.1, exact
+    ref = imp.numpy()
+    return float(np.max(np.abs(sc - ref) / (np.abs(ref) + 1e-300) * (ref > 1e-12)))
+
+
+def test_block_select_summaries_are_bf16_rounded_means():
+    """Reading of the compressed keys: bf16 tensors of a module that runs in
+    torch.bfloat16 (FSA page, quick start), i.e. the key mean rounded to
+    nearest even bf16."""
+    assert _summary_pin_error() <= 1e-10
+
+
+def test_block_select_rounding_pin_rejects_other_roundings(tmp_path):
+    """The pin above fails for an oracle that truncates the window means to
+    bf16, or rounds them half away from zero: each mistake is planted in a
+    copy of the oracle source, built and run on the CPU."""
+    src = oracle.source()
+    rne = "    u += 0x7FFFu + ((u >> 16) & 1u);\n"
+    assert src.count(rne) == 1
+    for name, repl in (("trunc", ""), ("half_away", "    u += 0x8000u;\n")):
+        lib = oracle.build_variant(src.replace(rne, repl), str(tmp_path), f"liboracle_{name}.so")
+        with oracle.using_library(lib):
+            err = _summary_pin_error()
+        assert err > 1e-7, (name, err)

@@ -29,7 +29,8 @@ EXPORTS = ("fsa_status_string", "fsa_abi_version", "fsa_selected_attn_fwd_worksp
            "fsa_topk_decode_auto_splits", "fsa_topk_decode", "fsa_topk_decode_fp8",
            "fsa_sliding_window_fwd_workspace_size", "fsa_sliding_window_fwd",
            "fsa_selected_attn_bwd_workspace_size", "fsa_selected_attn_bwd",
-           "fsa_block_select_workspace_size", "fsa_block_select")
+           "fsa_block_select_workspace_size", "fsa_block_select", "fsa_wait_timeouts",
+           "fsa_set_wait_poll_limit")
 
 _lib = None
 
@@ -86,6 +87,10 @@ def load() -> ctypes.CDLL:
     lib.fsa_block_select.restype = ctypes.c_int
     lib.fsa_block_select.argtypes = [P, P, P, P, i32, i64, i64, i32, i32, i32, i32, i32, i32, i32,
                                      i32, i32, i32, i32, f32, P, sz, P, P]
+    lib.fsa_wait_timeouts.restype = ctypes.c_int
+    lib.fsa_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32]
+    lib.fsa_set_wait_poll_limit.restype = ctypes.c_int
+    lib.fsa_set_wait_poll_limit.argtypes = [i32]
     _lib = lib
     return lib
 
@@ -107,6 +112,31 @@ def _check_dev(name: str, t: torch.Tensor, dtype: torch.dtype, ndim: int):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_buf(name: str, t: torch.Tensor, dtype: torch.dtype, shape: tuple,
+               device: torch.device):
+    """A caller-supplied output buffer: the dtype, shape and device the call
+    writes, contiguous (checked before any launch: a wrong buffer would be an
+    out-of-bounds device write)."""
+    _check_dev(name, t, dtype, len(shape))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must live on {device}, got {t.device}")
+
+
+def _same_device(*ts: torch.Tensor):
+    devs = {t.device for t in ts}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors of one call must live on one GPU, got {sorted(map(str, devs))}")
+
+
+def _check_ws(t: torch.Tensor, device: torch.device):
+    """A caller-supplied workspace: contiguous uint8 on the call's GPU."""
+    _check_dev("workspace", t, torch.uint8, t.dim())
+    if t.device != device:
+        raise ValueError(f"workspace must live on {device}, got {t.device}")
+
+
 def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -117,6 +147,23 @@ def fsa_status_string(status: int) -> str:
 
 def fsa_abi_version() -> int:
     return int(load().fsa_abi_version())
+
+
+def fsa_wait_timeouts(reset: bool = False) -> int:
+    """Ring waits inside the kernels that gave up since the last reset
+    (0 after correct runs); synchronous."""
+    n = ctypes.c_uint32(0)
+    st = load().fsa_wait_timeouts(ctypes.byref(n), int(reset))
+    if st != FSA_SUCCESS:
+        raise FsaError(st, "fsa_wait_timeouts")
+    return int(n.value)
+
+
+def fsa_set_wait_poll_limit(polls: int) -> None:
+    """Polls before a ring wait gives up (0 = the default)."""
+    st = load().fsa_set_wait_poll_limit(int(polls))
+    if st != FSA_SUCCESS:
+        raise FsaError(st, "fsa_set_wait_poll_limit")
 
 
 def fsa_selected_attn_fwd_workspace_size(batch: int, total_q: int, max_seqlen_q: int,
@@ -183,10 +230,17 @@ def fsa_selected_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("k and v must both be [total_k, Hkv, d] with q's d")
     if tuple(blk_idx.shape[:2]) != (total_q, hkv) or cu_seqlens_k.numel() != batch + 1:
         raise ValueError("blk_idx must be [total_q, Hkv, topk]; cu_seqlens_k must match cu_seqlens_q")
+    _same_device(q, k, v, blk_idx, cu_seqlens_q, cu_seqlens_k)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_buf("out", out, torch.bfloat16, tuple(q.shape), q.device)
     if lse is None and return_lse:
         lse = torch.empty((hq, total_q), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_buf("lse", lse, torch.float32, (hq, total_q), q.device)
+    if workspace is not None:
+        _check_ws(workspace, q.device)
     need = lib.fsa_selected_attn_fwd_workspace_size(batch, total_q, max_seqlen_q, hq, hkv, d,
                                                     block_size, topk, num_splits)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
@@ -226,6 +280,9 @@ def fsa_selected_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out
     if tuple(out.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) \
             or tuple(v.shape) != tuple(k.shape) or tuple(lse.shape) != (hq, total_q):
         raise ValueError("out/dout must match q, v must match k, lse must be [Hq, total_q]")
+    _same_device(q, k, v, out, lse, dout, blk_idx, cu_seqlens_q, cu_seqlens_k)
+    if workspace is not None:
+        _check_ws(workspace, q.device)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
@@ -268,10 +325,17 @@ def fsa_sliding_window_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("k and v must both be [total_k, Hkv, d] with q's d")
     if cu_seqlens_k.numel() != batch + 1:
         raise ValueError("cu_seqlens_k must match cu_seqlens_q")
+    _same_device(q, k, v, cu_seqlens_q, cu_seqlens_k)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_buf("out", out, torch.bfloat16, tuple(q.shape), q.device)
     if lse is None and return_lse:
         lse = torch.empty((hq, total_q), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_buf("lse", lse, torch.float32, (hq, total_q), q.device)
+    if workspace is not None:
+        _check_ws(workspace, q.device)
     need = lib.fsa_sliding_window_fwd_workspace_size(batch, total_q, max_seqlen_q, hq, hkv, d,
                                                      num_splits)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
@@ -311,10 +375,18 @@ def _decode(q, k_cache, v_cache, k_descale, v_descale, tok_idx, block_table, cac
             _check_dev(nm, t, torch.float32, 2)
             if tuple(t.shape) != (batch, hkv):
                 raise ValueError(f"{nm} must be [batch, Hkv]")
+    _same_device(q, k_cache, v_cache, tok_idx, block_table, cache_seqlens,
+                 *(t for t in (k_descale, v_descale) if t is not None))
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_buf("out", out, torch.bfloat16, tuple(q.shape), q.device)
     if lse is None and return_lse:
         lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_buf("lse", lse, torch.float32, (batch, hq), q.device)
+    if workspace is not None:
+        _check_ws(workspace, q.device)
     need = lib.fsa_topk_decode_workspace_size(batch, hq, hkv, d, topk, num_splits)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -394,6 +466,9 @@ def fsa_block_select(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tenso
         _check_dev("out", out, torch.int32, 3)
         if tuple(out.shape) != (total_q, hkv, topk):
             raise ValueError("out must be [total_q, Hkv, topk]")
+    _same_device(q, k, cu_seqlens_q, cu_seqlens_k, out)
+    if workspace is not None:
+        _check_ws(workspace, q.device)
     need = lib.fsa_block_select_workspace_size(batch, max_seqlen_k, hkv, d, kernel_size,
                                                kernel_stride)
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):

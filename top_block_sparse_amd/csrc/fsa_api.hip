@@ -4,6 +4,7 @@
 // Nothing here allocates, frees or synchronises device memory; every check
 // runs before the first launch so a rejected call leaves the device
 // untouched.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -22,6 +23,9 @@ constexpr int kMaxTopkDecode = 8192;
 constexpr int kMaxGroupDecode = 16;
 constexpr int kMaxSplitsDecode = 64;
 constexpr size_t kAlign = 256;
+
+// Polls a ring wait makes before it gives up (fsa_set_wait_poll_limit).
+std::atomic<int> g_spin_limit{fsa::kDefaultSpinLimit};
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -292,6 +296,7 @@ static fsa_status_t prefill_impl(const void* q, const void* k, const void* v,
     p.tiles_per_seq = pl.tiles_per_seq;
     p.n_wg = pl.n_wg;
     p.ring = fsa::sel_attn_fwd_ring(head_dim, pl.T, p.topk);
+    p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     if (fsa::sel_attn_fwd_lds_bytes(head_dim, pl.T, p.topk, p.ring) > 160 * 1024)
         return FSA_ERROR_NOT_SUPPORTED;
     p.scale_log2 = resolve_scale(softmax_scale, head_dim) * fsa::kLog2e;
@@ -340,6 +345,23 @@ const char* fsa_status_string(fsa_status_t status) {
 
 int32_t fsa_abi_version(void) { return FSA_ABI_VERSION; }
 
+fsa_status_t fsa_wait_timeouts(uint32_t* count, int32_t reset) {
+    if (count == nullptr) return FSA_ERROR_INVALID_VALUE;
+    unsigned int a = 0, b = 0;
+    (void)hipGetLastError();
+    if (fsa::sel_attn_fwd_wait_timeouts(&a, reset != 0) != hipSuccess ||
+        fsa::sel_attn_bwd_wait_timeouts(&b, reset != 0) != hipSuccess)
+        return FSA_ERROR_LAUNCH;
+    *count = a + b;
+    return FSA_SUCCESS;
+}
+
+fsa_status_t fsa_set_wait_poll_limit(int32_t polls) {
+    if (polls < 0) return FSA_ERROR_INVALID_VALUE;
+    g_spin_limit.store(polls == 0 ? fsa::kDefaultSpinLimit : polls, std::memory_order_relaxed);
+    return FSA_SUCCESS;
+}
+
 size_t fsa_selected_attn_fwd_workspace_size(int32_t batch, int64_t total_q, int32_t max_seqlen_q,
                                              int32_t num_heads_q, int32_t num_heads_kv,
                                              int32_t head_dim, int32_t block_size, int32_t topk,
@@ -384,12 +406,15 @@ fsa_status_t fsa_sliding_window_fwd(const void* q, const void* k, const void* v,
                                     float softmax_scale, int32_t num_splits, void* workspace,
                                     size_t workspace_bytes, void* out, float* lse, void* stream) {
     if (window_left < -1 || window_right < -1 || max_seqlen_k < 0) return FSA_ERROR_INVALID_VALUE;
-    // a window at least as long as every sequence is the same as no limit
+    // A left bound of at least max_seqlen_k keys reaches below key 0 for every
+    // row (i + S_k - S_q - left <= S_k - 1 - left < 0), so it is the same as
+    // no limit.  The right bound is passed on unchanged: when S_q > S_k a
+    // right bound larger than S_k still cuts rows near the start, and every
+    // kernel use of it is 64-bit.
     const int32_t wl = window_left > max_seqlen_k ? max_seqlen_k : window_left;
-    const int32_t wr = window_right > max_seqlen_k ? max_seqlen_k : window_right;
     return prefill_impl(q, k, v, nullptr, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
                         max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim,
-                        fsa::kBlockKeys, 1, softmax_scale, wl, wr, true, num_splits, workspace,
+                        fsa::kBlockKeys, 1, softmax_scale, wl, window_right, true, num_splits, workspace,
                         workspace_bytes, out, lse, stream);
 }
 
@@ -557,6 +582,7 @@ fsa_status_t fsa_selected_attn_bwd(const void* q, const void* k, const void* v, 
     }
     p.T = T;
     p.ring = dq_ring;
+    p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     p.nchunk_q = (max_seqlen_q + fsa::sel_attn_bwd_index_chunk() - 1) / fsa::sel_attn_bwd_index_chunk();
     if (p.nchunk_q < 1) p.nchunk_q = 1;
     p.mtiles = (T * G + 15) / 16;

@@ -29,6 +29,7 @@ struct SelFwdParams {
     int tiles_per_seq;
     int n_wg;
     int ring;           // LDS ring slots of K/V blocks (3 or 4)
+    int spin_limit;     // polls before a ring wait gives up
     float scale_log2;   // softmax_scale * log2(e)
 };
 
@@ -92,6 +93,7 @@ struct SelBwdParams {
     int nparts, part_steps;  // a block's 32-row steps go to <= nparts workgroups of part_steps
     int T, mtiles, tiles_per_seq;   // dq tiling
     int ring;                       // dq LDS ring slots of K/V blocks (2..4)
+    int spin_limit;                 // polls before a ring wait gives up
     int nchunk_q;                   // index workgroups per (sequence, kv head)
     float scale, scale_log2;
 };
@@ -109,6 +111,13 @@ struct MergeParams {
     int64_t ntok;
     const int32_t* ntok_live;   // optional: rows of tokens >= *ntok_live are left untouched
 };
+
+// Polls a ring wait makes before it gives up (normal waits take ~1e3).
+constexpr int kDefaultSpinLimit = 1 << 22;
+// Device counters of ring waits that gave up, per kernel file (read and
+// optionally cleared; synchronous).
+hipError_t sel_attn_fwd_wait_timeouts(unsigned int* n, bool reset);
+hipError_t sel_attn_bwd_wait_timeouts(unsigned int* n, bool reset);
 
 template <int D>
 hipError_t launch_sel_attn_fwd(const SelFwdParams& p, hipStream_t stream);

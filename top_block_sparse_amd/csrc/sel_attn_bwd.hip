@@ -42,7 +42,8 @@ constexpr int kBwdDqWaves = 10;         // m-tiles (compute waves) per dq workgr
 constexpr int kBwdDqProducers = 2;      // waves that only move K/V blocks into LDS
 constexpr int kBwdDqThreads = (kBwdDqWaves + kBwdDqProducers) * 64;
 constexpr int kBwdWin = 256;            // blocks per union-building window (dq)
-constexpr int kSpinLimit = 1 << 22;     // bounded ring waits (normal waits are ~1e3)
+// Ring waits of this file's kernels that gave up (see wait_ready2).
+__device__ unsigned int g_bwd_wait_timeouts;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
@@ -578,7 +579,7 @@ struct DqLds {
     __host__ __device__ static int umask(int ring) { return masks(ring) + kBwdWin * 8; }  // u64 [kBwdWin]
     __host__ __device__ static int ulist(int ring) { return umask(ring) + kBwdWin * 8; }  // i32 [kBwdWin]
     __host__ __device__ static int ncnt(int ring) { return ulist(ring) + kBwdWin * 4; }   // i32 [kBwdWin]
-    __host__ __device__ static int count(int ring) { return ncnt(ring) + kBwdWin * 4; }   // i32
+    __host__ __device__ static int count(int ring) { return ncnt(ring) + kBwdWin * 4; }   // i32, then the abort word
     __host__ __device__ static int ready(int ring) { return count(ring) + 16; }           // u32 [4][producers]
     __host__ __device__ static int done(int ring) { return ready(ring) + 4 * kBwdDqProducers * 4; }  // u32 [4]
     __host__ __device__ static int ent(int ring) { return done(ring) + 16; }              // i32 [T * topk]
@@ -601,6 +602,7 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
     int* s_ulist = reinterpret_cast<int*>(smem + L::ulist(ring));
     int* s_ncnt = reinterpret_cast<int*>(smem + L::ncnt(ring));
     int* s_count = reinterpret_cast<int*>(smem + L::count(ring));
+    uint32_t* s_abort = reinterpret_cast<uint32_t*>(smem + L::count(ring) + 4);
     uint32_t* s_ready = reinterpret_cast<uint32_t*>(smem + L::ready(ring));
     uint32_t* s_done = reinterpret_cast<uint32_t*>(smem + L::done(ring));
     int* s_ent = reinterpret_cast<int*>(smem + L::ent(ring));
@@ -608,6 +610,8 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     if (tid < 4 * (kBwdDqProducers + 1)) s_ready[tid] = 0u;   // s_ready and s_done
+    if (tid == 0) s_abort[0] = 0u;
+    bool gave_up = false;                       // this wave gave up waiting (sticky)
 
     int w = xcd_remap(blockIdx.x, (int)gridDim.x);
     const int j = p.tiles_per_seq - 1 - (w % p.tiles_per_seq);
@@ -797,8 +801,8 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
                         const uint32_t ps = seq0 + (uint32_t)pub;
                         publish((int)(ps % (uint32_t)ring), ps + 1);
                     }
-                    for (int sp = 0; sp < kSpinLimit && lds_load_sync(s_done + slot) < need_done; ++sp)
-                        __builtin_amdgcn_s_sleep(1);
+                    wait_done(s_done + slot, need_done, s_abort, &g_bwd_wait_timeouts, p.spin_limit,
+                              gave_up, lane);
                 }
                 const uint32_t nc = (uint32_t)__builtin_amdgcn_readlane(nc_v, i & 63);
                 tgt0 += slot == 0 ? nc : 0u;
@@ -831,11 +835,8 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
             const int slot = (int)(seq % (uint32_t)ring);
             const int blk = __builtin_amdgcn_readfirstlane(s_ulist[u]);
             const unsigned long long bm = uniform_u64(s_umask[u]);
-            for (int sp = 0; sp < kSpinLimit; ++sp) {
-                const u32x2_t r = lds_load2_sync(s_ready + slot * kBwdDqProducers);
-                if (r[0] >= seq + 1 && r[1] >= seq + 1) break;
-                __builtin_amdgcn_s_sleep(4);
-            }
+            wait_ready2(s_ready + slot * kBwdDqProducers, seq + 1, s_abort, &g_bwd_wait_timeouts,
+                        p.spin_limit, gave_up, lane);
             __builtin_amdgcn_s_setprio(1);   // a computing wave goes before polling ones
             const uint8_t* kslot = smem + slot * L::kSlot;
             const uint8_t* vslot = kslot + L::kPart;
@@ -909,6 +910,15 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
             *reinterpret_cast<u32x2_t*>(o + dt * 16) = u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
         }
     }
+}
+
+hipError_t sel_attn_bwd_wait_timeouts(unsigned int* n, bool reset) {
+    hipError_t e = hipMemcpyFromSymbol(n, HIP_SYMBOL(g_bwd_wait_timeouts), sizeof(unsigned int));
+    if (e == hipSuccess && reset) {
+        const unsigned int zero = 0u;
+        e = hipMemcpyToSymbol(HIP_SYMBOL(g_bwd_wait_timeouts), &zero, sizeof(unsigned int));
+    }
+    return e;
 }
 
 int sel_attn_bwd_rows_per_tile() { return kBwdDqWaves * 16; }

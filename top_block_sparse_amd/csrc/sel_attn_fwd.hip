@@ -27,8 +27,8 @@
 // Consumers never wait for one another, so the uneven per-block work of
 // random selections evens out over the tile instead of costing a barrier per
 // block, and a block no token of an m-tile chose costs that m-tile nothing.
-// Every wait is a bounded spin, so a logic error can only produce wrong
-// values, never a hung GPU.  Waiting consumers sleep between polls; a
+// Every wait is a bounded spin: a logic error can only produce wrong values
+// and a non-zero timeout count (fsa_wait_timeouts), never a hung GPU.  Waiting consumers sleep between polls; a
 // consumer computes at raised wave priority and the producers run higher
 // still, so a SIMD issues DMA first, then MFMA work, then polls.
 //
@@ -56,7 +56,6 @@ constexpr int kSelWin = 256;                       // blocks per union-building 
 constexpr int kSelRingMax = 4;                     // LDS slots of K/V blocks (3 if LDS is short)
 constexpr int kSelDepth = 2;                       // blocks in flight per producer (<= slots)
 constexpr int kLdsBytes = 160 * 1024;
-constexpr int kSpinLimit = 1 << 22;                // bounded waits (normal waits are ~1e3)
 constexpr float kLazy = 8.f;                       // lazy-rescale threshold (log2 units)
 
 // LDS layout (bytes) for head dim D.  A slot holds one 64-key block in
@@ -82,7 +81,7 @@ struct SelLds {
     __host__ __device__ static int umask(int ring) { return masks(ring) + kSelWin * 8; }   // u64 [kSelWin]
     __host__ __device__ static int ulist(int ring) { return umask(ring) + kSelWin * 8; }   // i32 [kSelWin]
     __host__ __device__ static int ncnt(int ring) { return ulist(ring) + kSelWin * 4; }    // i32 [kSelWin]
-    __host__ __device__ static int count(int ring) { return ncnt(ring) + kSelWin * 4; }    // i32
+    __host__ __device__ static int count(int ring) { return ncnt(ring) + kSelWin * 4; }    // i32, then the abort word
     __host__ __device__ static int ready(int ring) { return count(ring) + 16; }            // u32 [ring][producers]
     __host__ __device__ static int done(int ring) { return ready(ring) + kSelRingMax * kSelProducers * 4; }
     __host__ __device__ static int ent(int ring) { return done(ring) + kSelRingMax * 4; }  // i32 [T*topk]
@@ -90,6 +89,9 @@ struct SelLds {
         return (size_t)ent(ring) + (size_t)T * topk * 4;
     }
 };
+
+// Ring waits of this file's kernels that gave up (see wait_ready2).
+__device__ unsigned int g_fwd_wait_timeouts;
 
 __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long x, int l) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
@@ -144,6 +146,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     int* s_ulist = reinterpret_cast<int*>(smem + L::ulist(ring));
     int* s_ncnt = reinterpret_cast<int*>(smem + L::ncnt(ring));
     int* s_count = reinterpret_cast<int*>(smem + L::count(ring));
+    uint32_t* s_abort = reinterpret_cast<uint32_t*>(smem + L::count(ring) + 4);
     uint32_t* s_ready = reinterpret_cast<uint32_t*>(smem + L::ready(ring));
     uint32_t* s_done = reinterpret_cast<uint32_t*>(smem + L::done(ring));
     int* s_ent = reinterpret_cast<int*>(smem + L::ent(ring));
@@ -206,6 +209,8 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         s_ent[e] = ok ? id : -1;
     }
     if (tid < kSelRingMax * (kSelProducers + 1)) s_ready[tid] = 0u;   // s_ready and s_done
+    if (tid == 0) s_abort[0] = 0u;
+    bool gave_up = false;                       // this wave gave up waiting (sticky)
 
     const bool consumer = wave < kSelConsumers;
 
@@ -498,8 +503,8 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
                         const uint32_t ps = seq0 + (uint32_t)pub;
                         publish((int)(ps % (uint32_t)ring), ps + 1);
                     }
-                    for (int sp = 0; sp < kSpinLimit && lds_load_sync(s_done + slot) < need_done; ++sp)
-                        __builtin_amdgcn_s_sleep(1);
+                    wait_done(s_done + slot, need_done, s_abort, &g_fwd_wait_timeouts, p.spin_limit,
+                              gave_up, lane);
                 }
                 const int blk = __builtin_amdgcn_readlane(ul_v, i & 63);
                 const uint32_t nc = (uint32_t)__builtin_amdgcn_readlane(nc_v, i & 63);
@@ -543,11 +548,8 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
                     const int slot = (int)(seq % (uint32_t)ring);
                     const int blk = __builtin_amdgcn_readlane(ul, bitp);
                     const unsigned long long bm = readlane_u64(m, bitp);
-                    for (int sp = 0; sp < kSpinLimit; ++sp) {
-                        const u32x2_t r = lds_load2_sync(s_ready + slot * kSelProducers);
-                        if (r[0] >= seq + 1 && r[1] >= seq + 1) break;
-                        __builtin_amdgcn_s_sleep(4);
-                    }
+                    wait_ready2(s_ready + slot * kSelProducers, seq + 1, s_abort, &g_fwd_wait_timeouts,
+                                p.spin_limit, gave_up, lane);
                     __builtin_amdgcn_s_setprio(1);   // a computing consumer goes before polling ones
                     compute(smem + slot * L::kSlot, blk, bm);
                     __builtin_amdgcn_s_setprio(0);
@@ -624,6 +626,15 @@ template hipError_t launch_sel_attn_fwd<64>(const SelFwdParams&, hipStream_t);
 template hipError_t launch_sel_attn_fwd<128>(const SelFwdParams&, hipStream_t);
 
 int sel_attn_fwd_rows_per_tile() { return kSelConsumers * 16; }
+
+hipError_t sel_attn_fwd_wait_timeouts(unsigned int* n, bool reset) {
+    hipError_t e = hipMemcpyFromSymbol(n, HIP_SYMBOL(g_fwd_wait_timeouts), sizeof(unsigned int));
+    if (e == hipSuccess && reset) {
+        const unsigned int zero = 0u;
+        e = hipMemcpyToSymbol(HIP_SYMBOL(g_fwd_wait_timeouts), &zero, sizeof(unsigned int));
+    }
+    return e;
+}
 
 size_t sel_attn_fwd_lds_bytes(int D, int T, int topk, int ring) {
     return D == 64 ? SelLds<64>::bytes(T, topk, ring) : SelLds<128>::bytes(T, topk, ring);
