@@ -104,8 +104,8 @@ class PrefillLeg:
         self.total_q = self.g["q"].shape[0]
         self.lse = torch.empty((sp.num_heads_q, self.total_q), dtype=torch.float32, device=dev)
         ws = fsa.fsa_selected_attn_fwd_workspace_size(
-            len(sp.seqlens), self.total_q, d["max_seqlen_q"], sp.num_heads_q, sp.num_heads_kv,
-            sp.head_dim, sp.block_size, sp.topk, 0)
+            len(sp.seqlens), self.total_q, d["max_seqlen_q"], d["max_seqlen_k"], sp.num_heads_q,
+            sp.num_heads_kv, sp.head_dim, sp.block_size, sp.topk, 0)
         self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
         self.fsa = fsa
 

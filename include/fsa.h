@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define FSA_ABI_VERSION 1
+#define FSA_ABI_VERSION 2
 
 typedef enum {
     FSA_SUCCESS = 0,
@@ -93,12 +93,15 @@ fsa_status_t fsa_set_wait_poll_limit(int32_t polls);
  * Bytes of device workspace fsa_selected_attn_fwd needs for these arguments
  * (0 when no workspace is needed).  num_splits = 0 prices the automatic
  * choice.  Returns 0 as well for arguments fsa_selected_attn_fwd would reject.
+ * The block-centric schedule (below) needs about
+ * total_q * num_heads_q * topk * (2 * head_dim + 4) bytes of partials plus
+ * the inverted index.
  */
 size_t fsa_selected_attn_fwd_workspace_size(int32_t batch, int64_t total_q,
-                                             int32_t max_seqlen_q, int32_t num_heads_q,
-                                             int32_t num_heads_kv, int32_t head_dim,
-                                             int32_t block_size, int32_t topk,
-                                             int32_t num_splits);
+                                             int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                             int32_t num_heads_q, int32_t num_heads_kv,
+                                             int32_t head_dim, int32_t block_size,
+                                             int32_t topk, int32_t num_splits);
 
 /*
  * Selected block-sparse attention forward (prefill), varlen layout.
@@ -116,9 +119,19 @@ size_t fsa_selected_attn_fwd_workspace_size(int32_t batch, int64_t total_q,
  *   head_dim 64 or 128; block_size 64; 1 <= topk <= 64;
  *   num_heads_q / num_heads_kv <= 224
  *   causal   nonzero: bottom-right causal mask; zero: no mask
- *   num_splits  0 = automatic; n >= 1 splits every tile's selected-block set
- *            into n parts computed by separate workgroups and merged by
- *            logsumexp (needs workspace when n > 1); at most 16
+ *   num_splits  selects the schedule.
+ *            -1: block-centric (the FSA page's loop swap: the lists are
+ *            inverted on the GPU, each key block is computed once against the
+ *            dense 16-row tiles of the query rows that selected it, and the
+ *            per-(token, block) partials are merged by logsumexp; needs
+ *            workspace); num_heads_q / num_heads_kv <= 16, else
+ *            FSA_ERROR_NOT_SUPPORTED.
+ *            n >= 1: query-centric (a workgroup per tile of query tokens
+ *            streams the union of their blocks) with every tile's selected-
+ *            block set split into n parts computed by separate workgroups and
+ *            merged by logsumexp (needs workspace when n > 1); at most 16.
+ *            0: automatic -- block-centric when num_heads_q / num_heads_kv
+ *            <= 2, else query-centric with an automatic split count.
  *   workspace, workspace_bytes  device scratch of at least
  *            fsa_selected_attn_fwd_workspace_size(...) bytes (may be NULL when
  *            that size is 0); contents on entry are ignored

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fsa_abi_version() == 1
+    assert lib.fsa_abi_version() == 2
     for code, name in _lib._STATUS.items():
         assert lib.fsa_status_string(code).decode() == name
     assert lib.fsa_status_string(99).decode() == "FSA_ERROR_UNKNOWN"
@@ -70,7 +70,9 @@ def prefill(lib, **kw):
     (dict(topk=65), NOT_SUPPORTED),
     (dict(hq=512, hkv=1), NOT_SUPPORTED),     # GQA group above 256
     (dict(splits=17), NOT_SUPPORTED),
-    (dict(splits=-1), INVALID),
+    (dict(splits=-2), INVALID),
+    (dict(splits=-1, hq=64, hkv=2), NOT_SUPPORTED),   # block-centric up to G = 16
+    (dict(splits=-1), WORKSPACE),             # block-centric partials need workspace
     (dict(batch=-1), INVALID),
     (dict(total_q=-5), INVALID),
     (dict(q=None), INVALID),
@@ -92,11 +94,20 @@ def test_prefill_nothing_to_do_is_success(lib):
 
 def test_prefill_workspace_sizes(lib):
     f = lib.fsa_selected_attn_fwd_workspace_size
-    assert f(2, 16384, 8192, 32, 8, 128, 64, 16, 1) == 0
+    assert f(2, 16384, 8192, 8192, 32, 8, 128, 64, 16, 1) == 0
     want = 4 * 16384 * 32 * 128 * 4 + 4 * 16384 * 32 * 4
-    assert f(2, 16384, 8192, 32, 8, 128, 64, 16, 4) == want
-    assert f(1, 1024, 1024, 4, 1, 64, 64, 4, 0) > 0          # tiny grid -> automatic splits
-    assert f(2, 16384, 8192, 32, 8, 96, 64, 16, 1) == 0       # rejected shape
+    assert f(2, 16384, 8192, 8192, 32, 8, 128, 64, 16, 4) == want
+    # automatic choice at G = 1: block-centric partials (bf16 O + fp32 max and
+    # sum per row and list slot) dominate the workspace
+    parts = 98304 * 4 * 16 * (2 * 128 + 8)
+    assert parts < f(2, 98304, 65536, 65536, 4, 4, 128, 64, 16, 0) < parts * 1.3
+    # G = 4: query-centric, no split at this size
+    assert f(2, 16384, 8192, 8192, 32, 8, 128, 64, 16, 0) == 0
+    # G = 16: query-centric, a tiny grid gets automatic splits
+    assert f(1, 64, 64, 64, 16, 1, 64, 64, 4, 0) > 0
+    assert f(2, 16384, 8192, 8192, 128, 8, 128, 64, 16, 0) == 0
+    assert f(2, 16384, 8192, 8192, 32, 8, 96, 64, 16, 1) == 0      # rejected shape
+    assert f(2, 16384, 8192, -1, 32, 8, 128, 64, 16, 0) == 0       # rejected size
 
 
 def decode(lib, **kw):
@@ -196,6 +207,7 @@ def window(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
+    (dict(splits=-1), INVALID),                # no block-centric window schedule
     (dict(wl=-2), INVALID),
     (dict(wr=-5), INVALID),
     (dict(hq=6, hkv=4), INVALID),

@@ -125,10 +125,21 @@ def oracle_prefill(dd, tokens=None, causal=True):
 
 # ------------------------------------------------------------------ prefill
 
-def test_prefill_small_workload_every_row():
+# num_splits = 0 takes the automatic schedule (block-centric for a GQA group of
+# at most 2), 1 the query-centric one and -1 the block-centric one: every
+# prefill case below runs through each (block-centric only up to G = 16).
+SCHEDULES = {"auto": 0, "query": 1, "block": -1}
+
+
+def sched_ok(sched, hq, hkv):
+    return not (sched == "block" and hq // hkv > 16)
+
+
+@pytest.mark.parametrize("sched", SCHEDULES)
+def test_prefill_small_workload_every_row(sched):
     spec = inputs.PREFILL_WORKLOADS["prefill_s1024_h4_kv1_d64_top4"]
     dd = inputs.make_prefill(spec)
-    out, lse = run_prefill(dd)
+    out, lse = run_prefill(dd, num_splits=SCHEDULES[sched])
     ro, rl = oracle_prefill(dd)
     compare(out, lse, ro, rl, what=spec.name)
 
@@ -149,33 +160,44 @@ SHAPES = [
     ((800,), 4, 2, 128, 10, None),                     # G = 2
     ((260,), 64, 1, 64, 6, None),                      # G = 64: a token spans 4 m-tiles
     ((130, 70), 224, 1, 64, 5, None),                  # G = 224, the largest group: one token per tile
+    ((610,), 10, 2, 128, 11, None),                    # G = 5: 3 tokens (15 rows) per dense tile
+    ((390, 45), 7, 1, 64, 13, None),                   # G = 7: 2 tokens (14 rows) per dense tile
+    ((4500,), 4, 4, 128, 16, None),                    # G = 1, block 0 spans many dense tasks
 ]
 
 
+@pytest.mark.parametrize("sched", SCHEDULES)
 @pytest.mark.parametrize("case", SHAPES, ids=lambda c: f"s{c[0]}_h{c[1]}_kv{c[2]}_d{c[3]}_k{c[4]}")
-def test_prefill_random_shapes_with_index_edge_cases(case):
+def test_prefill_random_shapes_with_index_edge_cases(case, sched):
     seqlens, hq, hkv, d, topk, sk = case
+    if not sched_ok(sched, hq, hkv):
+        pytest.skip("the block-centric schedule covers GQA groups up to 16")
+    print(f"[gpu] prefill {case} schedule={sched}", flush=True)
     dd = make_case(seqlens, hq, hkv, d, topk, seed=sum(seqlens) + hq + d, seqlens_k=sk)
-    out, lse = run_prefill(dd)
+    out, lse = run_prefill(dd, num_splits=SCHEDULES[sched])
     ro, rl = oracle_prefill(dd)
     compare(out, lse, ro, rl, what=str(case))
 
 
+@pytest.mark.parametrize("sched", SCHEDULES)
 @pytest.mark.parametrize("causal", [True, False])
-def test_prefill_causal_flag(causal):
+def test_prefill_causal_flag(causal, sched):
     dd = make_case((333, 129), 8, 2, 128, 6, seed=77, seqlens_k=(400, 129))
-    out, lse = run_prefill(dd, causal=causal)
+    out, lse = run_prefill(dd, causal=causal, num_splits=SCHEDULES[sched])
     ro, rl = oracle_prefill(dd, causal=causal)
     compare(out, lse, ro, rl, what=f"causal={causal}")
 
 
+@pytest.mark.parametrize("sched", SCHEDULES)
 @pytest.mark.parametrize("case", [((1000, 200), 8, 2, 128, 16), ((777,), 4, 4, 64, 9),
-                                  ((500,), 32, 2, 128, 12)])
-def test_prefill_visible_set_exact(case):
+                                  ((500,), 32, 2, 128, 12), ((640, 3), 6, 2, 64, 7)])
+def test_prefill_visible_set_exact(case, sched):
     """q = 0: LSE = ln|J| exactly; the GPU must keep exactly the oracle's key set."""
     seqlens, hq, hkv, d, topk = case
+    if not sched_ok(sched, hq, hkv):
+        pytest.skip("the block-centric schedule covers GQA groups up to 16")
     dd = make_case(seqlens, hq, hkv, d, topk, seed=5, zero_q=True)
-    out, lse = run_prefill(dd)
+    out, lse = run_prefill(dd, num_splits=SCHEDULES[sched])
     ro, rl = oracle_prefill(dd)
     fin = np.isfinite(rl)
     assert np.array_equal(fin, np.isfinite(lse.T))
@@ -191,22 +213,43 @@ def test_prefill_split_k_matches(splits):
     compare(out, lse, ro, rl, what=f"splits={splits}")
 
 
-def test_prefill_without_lse_output():
+@pytest.mark.parametrize("sched", SCHEDULES)
+def test_prefill_without_lse_output(sched):
     dd = make_case((400,), 8, 2, 128, 8, seed=3)
-    out, lse = run_prefill(dd, lse=False)
+    out, lse = run_prefill(dd, lse=False, num_splits=SCHEDULES[sched])
     assert lse is None
     ro, rl = oracle_prefill(dd)
     compare(out, None, ro, rl)
 
 
-def test_prefill_all_lists_empty():
+@pytest.mark.parametrize("sched", SCHEDULES)
+def test_prefill_all_lists_empty(sched):
     dd = make_case((300, 50), 4, 2, 64, 4, seed=4, mutate=False)
     dd["blk_idx"] = torch.full_like(dd["blk_idx"], -1)
-    out, lse = run_prefill(dd)
+    out, lse = run_prefill(dd, num_splits=SCHEDULES[sched])
     assert np.all(out == 0.0) and np.all(lse == -np.inf)
 
 
-@pytest.mark.parametrize("splits", [1, 3])
+def test_prefill_block_centric_leaves_rows_outside_sequences():
+    """Rows of q past cu_seqlens_q[batch] belong to no sequence: the output
+    and LSE there keep what the caller put in them."""
+    dd = make_case((300, 200), 8, 2, 128, 8, seed=9)
+    g = to_dev(dd, ("q", "k", "v", "blk_idx", "cu_seqlens_q", "cu_seqlens_k"))
+    extra = 37
+    q = torch.cat([g["q"], g["q"][:extra]])
+    blk = torch.cat([g["blk_idx"], g["blk_idx"][:extra]])
+    out = torch.full_like(q, 3.0)
+    lse = torch.full((q.shape[1], q.shape[0]), 7.0, dtype=torch.float32, device=DEV)
+    fsa.fsa_selected_attn_fwd(q, g["k"], g["v"], blk, g["cu_seqlens_q"], g["cu_seqlens_k"],
+                              dd["max_seqlen_q"], dd["max_seqlen_k"], out=out, lse=lse)
+    torch.cuda.synchronize()
+    n = dd["q"].shape[0]
+    assert bool((out[n:] == 3.0).all()) and bool((lse[:, n:] == 7.0).all())
+    ro, rl = oracle_prefill(dd)
+    compare(out[:n].float().cpu().numpy(), lse[:, :n].cpu().numpy(), ro, rl)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
 def test_prefill_idle_m_tiles(splits):
     """Runs of tokens with empty lists next to tokens with long ones: some
     m-tiles of a tile visit no block at all, others every block, so the ring

@@ -57,7 +57,8 @@ def load() -> ctypes.CDLL:
     lib.fsa_abi_version.restype = i32
     lib.fsa_abi_version.argtypes = []
     lib.fsa_selected_attn_fwd_workspace_size.restype = sz
-    lib.fsa_selected_attn_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32, i32]
+    lib.fsa_selected_attn_fwd_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32,
+                                                         i32, i32]
     lib.fsa_selected_attn_fwd.restype = ctypes.c_int
     lib.fsa_selected_attn_fwd.argtypes = [P, P, P, P, P, P, i32, i64, i64, i32, i32, i32, i32, i32,
                                           i32, i32, f32, i32, i32, P, sz, P, P, P]
@@ -167,11 +168,13 @@ def fsa_set_wait_poll_limit(polls: int) -> None:
 
 
 def fsa_selected_attn_fwd_workspace_size(batch: int, total_q: int, max_seqlen_q: int,
-                                         num_heads_q: int, num_heads_kv: int, head_dim: int,
-                                         block_size: int, topk: int, num_splits: int = 0) -> int:
+                                         max_seqlen_k: int, num_heads_q: int, num_heads_kv: int,
+                                         head_dim: int, block_size: int, topk: int,
+                                         num_splits: int = 0) -> int:
     return int(load().fsa_selected_attn_fwd_workspace_size(batch, total_q, max_seqlen_q,
-                                                            num_heads_q, num_heads_kv, head_dim,
-                                                            block_size, topk, num_splits))
+                                                            max_seqlen_k, num_heads_q,
+                                                            num_heads_kv, head_dim, block_size,
+                                                            topk, num_splits))
 
 
 def fsa_selected_attn_bwd_workspace_size(batch: int, total_q: int, total_k: int,
@@ -241,8 +244,8 @@ def fsa_selected_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _check_buf("lse", lse, torch.float32, (hq, total_q), q.device)
     if workspace is not None:
         _check_ws(workspace, q.device)
-    need = lib.fsa_selected_attn_fwd_workspace_size(batch, total_q, max_seqlen_q, hq, hkv, d,
-                                                    block_size, topk, num_splits)
+    need = lib.fsa_selected_attn_fwd_workspace_size(batch, total_q, max_seqlen_q, max_seqlen_k,
+                                                    hq, hkv, d, block_size, topk, num_splits)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

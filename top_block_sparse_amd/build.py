@@ -14,11 +14,11 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libfsa.so")
-SOURCES = ["fsa_api.hip", "sel_attn_fwd.hip", "sel_attn_bwd.hip", "topk_decode.hip", "lse_merge.hip",
-           "block_select.hip"]
-# The prefill kernel never produces or tests NaNs (masked scores are -inf,
+SOURCES = ["fsa_api.hip", "sel_attn_fwd.hip", "sel_attn_fwd_bc.hip", "sel_attn_bwd.hip",
+           "topk_decode.hip", "lse_merge.hip", "block_select.hip"]
+# The prefill kernels never produce or test NaNs (masked scores are -inf,
 # which stays honoured), so fmax there compiles to a single instruction.
-EXTRA_FLAGS = {"sel_attn_fwd.hip": ["-fno-honor-nans"]}
+EXTRA_FLAGS = {"sel_attn_fwd.hip": ["-fno-honor-nans"], "sel_attn_fwd_bc.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 

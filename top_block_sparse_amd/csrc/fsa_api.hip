@@ -34,12 +34,28 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Prefill tiling: T tokens per workgroup so that T*G query rows fill at most
 // 16 MFMA m-tiles, and at most 64 tokens (one bit each in the block masks).
 struct PrefillPlan {
-    int T, mtiles, tiles_per_seq, splits, n_wg;
+    int T, mtiles, tiles_per_seq, splits, n_wg, head_major;
 };
 
+// Tile order of the query-centric kernel.  When one (sequence, kv head) unit's
+// K and V exceed kHeadMajorBytes they cannot stay in one XCD's 4 MiB L2, and
+// the tiles of all units would compete for the 256 MiB Infinity Cache at once;
+// then every XCD works through the same unit at the same time, each on every
+// eighth tile (measured at 131072 tokens x 4 kv heads, d 128: 27.9 ms against
+// 32.8 ms).  Smaller units keep one XCD each.
+constexpr long long kHeadMajorBytes = 8ll << 20;
+
+void set_tile_order(PrefillPlan& pl, int32_t batch, int32_t Hkv, int32_t max_seqlen_k, int32_t D) {
+    if ((long long)max_seqlen_k * D * 2 * 2 <= kHeadMajorBytes) return;
+    pl.head_major = 1;
+    pl.n_wg = (int)((long long)batch * Hkv * pl.splits * ((pl.tiles_per_seq + 7) / 8) * 8);
+}
+
+// num_splits: 0 automatic, n >= 1 query-centric with n splits, -1 block-centric
+// (selected attention only; checked by the caller against the group size).
 fsa_status_t check_prefill_shape(int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_t Hkv,
                                  int32_t D, int32_t bs, int32_t topk, int32_t num_splits) {
-    if (batch < 0 || max_seqlen_q < 0 || Hq <= 0 || Hkv <= 0 || topk <= 0 || num_splits < 0)
+    if (batch < 0 || max_seqlen_q < 0 || Hq <= 0 || Hkv <= 0 || topk <= 0 || num_splits < -1)
         return FSA_ERROR_INVALID_VALUE;
     if (Hq % Hkv != 0) return FSA_ERROR_INVALID_VALUE;
     if (D != 64 && D != 128) return FSA_ERROR_NOT_SUPPORTED;
@@ -72,6 +88,7 @@ PrefillPlan plan_prefill(int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_
     }
     pl.splits = s;
     pl.n_wg = (int)(base * s);
+    pl.head_major = 0;
     return pl;
 }
 
@@ -246,6 +263,126 @@ size_t prefill_workspace(const PrefillPlan& pl, int64_t total_q, int32_t Hq, int
     return align_up((size_t)pl.splits * rows * D * 4) + align_up((size_t)pl.splits * rows * 4);
 }
 
+// Block-centric schedule (sel_attn_fwd_bc.hip): the automatic choice for
+// selected attention with a GQA group of at most kMaxGroupBc, where a token's
+// rows fill a small fraction of an MFMA tile (the FSA page keeps its loop swap
+// for groups below 8 and falls back to the query-centric kernel above).
+// Measured on MI355X: at G = 1 (varlen 65536 + 32768, topk 16) 1.31 ms against
+// 8.8 ms query-centric; at G = 4 (2 x 8192, topk 16) 1.33 ms against 0.90 ms,
+// where the bf16 partial round trip through HBM costs more than the padding
+// it removes.
+constexpr int kMaxGroupBc = 2;
+constexpr int kMaxSeqBc = 1 << 25;      // token index within a sequence << 6 must fit int32
+
+constexpr int kMaxGroupBcForced = 16;   // a 16-row MFMA tile holds at least one token
+constexpr int32_t kSplitsBlockCentric = -1;
+
+bool use_block_centric(int32_t G, int32_t num_splits, int32_t max_seqlen_q) {
+    if (max_seqlen_q >= kMaxSeqBc) return false;
+    if (num_splits == kSplitsBlockCentric) return G <= kMaxGroupBcForced;
+    return num_splits == 0 && G <= kMaxGroupBc;
+}
+
+struct BcLayout {
+    size_t counts, cursor, masks, ents, pos, tasks, ctr, part_ml, part_o, total;
+    int nb_max, tpt, max_tasks;
+};
+
+BcLayout bc_layout(int32_t batch, int64_t total_q, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv,
+                   int32_t D, int32_t topk) {
+    BcLayout l{};
+    const int G = Hq / Hkv;
+    l.tpt = 16 / G;
+    l.nb_max = (max_seqlen_k + fsa::kBlockKeys - 1) / fsa::kBlockKeys;
+    if (l.nb_max < 1) l.nb_max = 1;
+    const size_t units = (size_t)batch * Hkv;
+    const size_t entries = (size_t)total_q * Hkv * topk;
+    // each block's entries make at most n_b / (tpt * tiles per task) + 1 tasks
+    const size_t mt = entries / ((size_t)l.tpt * fsa::kBcTileTasks) + units * l.nb_max + 1;
+    l.max_tasks = mt > (size_t)INT32_MAX ? INT32_MAX : (int)mt;
+    size_t off = 0;
+    l.counts = off;
+    off = align_up(off + units * (l.nb_max + 1) * 4);
+    l.cursor = off;
+    off = align_up(off + units * l.nb_max * 4);
+    l.masks = off;
+    off = align_up(off + (size_t)total_q * Hkv * 8);
+    l.ents = off;
+    off = align_up(off + entries * 4);
+    l.pos = off;
+    off = align_up(off + entries * 4);
+    l.tasks = off;
+    off = align_up(off + (size_t)l.max_tasks * 8);
+    l.ctr = off;
+    off = align_up(off + 16 * 4);
+    // (+16 rows: a dummy partial row per tile row for lanes with no entry)
+    l.part_ml = off;
+    off = align_up(off + (entries * G + 16) * 8);
+    l.part_o = off;
+    off = align_up(off + (entries * G + 16) * D * 2);
+    l.total = off;
+    return l;
+}
+
+static fsa_status_t prefill_bc(const void* q, const void* k, const void* v, const int32_t* blk_idx,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t batch, int64_t total_q, int64_t total_k,
+                               int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_heads_q,
+                               int32_t num_heads_kv, int32_t head_dim, int32_t topk,
+                               float softmax_scale, bool causal,
+                               void* workspace, size_t workspace_bytes, void* out, float* lse,
+                               void* stream) {
+    const BcLayout lay = bc_layout(batch, total_q, max_seqlen_k, num_heads_q, num_heads_kv,
+                                   head_dim, topk);
+    if (workspace == nullptr || workspace_bytes < lay.total ||
+        (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+        return FSA_ERROR_WORKSPACE;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return FSA_ERROR_LAUNCH;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    fsa::SelFwdBcParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.blk_idx = blk_idx;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.out = static_cast<uint16_t*>(out);
+    p.lse = lse;
+    p.counts = reinterpret_cast<int32_t*>(ws + lay.counts);
+    p.cursor = reinterpret_cast<int32_t*>(ws + lay.cursor);
+    p.masks = reinterpret_cast<unsigned long long*>(ws + lay.masks);
+    p.ents = reinterpret_cast<int32_t*>(ws + lay.ents);
+    p.pos = reinterpret_cast<int32_t*>(ws + lay.pos);
+    p.tasks = reinterpret_cast<int2*>(ws + lay.tasks);
+    p.ctr = reinterpret_cast<uint32_t*>(ws + lay.ctr);
+    p.part_ml = reinterpret_cast<float*>(ws + lay.part_ml);
+    p.part_o = reinterpret_cast<uint16_t*>(ws + lay.part_o);
+    p.total_q = total_q;
+    p.total_k = total_k;
+    p.batch = batch;
+    p.Hq = num_heads_q;
+    p.Hkv = num_heads_kv;
+    p.G = num_heads_q / num_heads_kv;
+    p.topk = topk;
+    p.causal = causal ? 1 : 0;
+    p.nb_max = lay.nb_max;
+    p.tpt = lay.tpt;
+    p.max_tasks = lay.max_tasks;
+    p.nchunk_q = (int)((max_seqlen_q + fsa::kBcIndexChunk - 1) / fsa::kBcIndexChunk);
+    const long long nwg = (long long)cus * fsa::kBcWgPerCu;
+    p.n_wg = (int)(nwg < lay.max_tasks ? nwg : lay.max_tasks);
+    if (p.n_wg < 1) p.n_wg = 1;
+    p.scale_log2 = resolve_scale(softmax_scale, head_dim) * fsa::kLog2e;
+    (void)hipGetLastError();
+    if (fsa::launch_sel_attn_fwd_bc(p, head_dim, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return FSA_ERROR_LAUNCH;
+    return FSA_SUCCESS;
+}
+
 static fsa_status_t prefill_impl(const void* q, const void* k, const void* v,
                                  const int32_t* blk_idx, const int32_t* cu_seqlens_q,
                                  const int32_t* cu_seqlens_k, int32_t batch, int64_t total_q,
@@ -265,11 +402,22 @@ static fsa_status_t prefill_impl(const void* q, const void* k, const void* v,
         return FSA_ERROR_INVALID_VALUE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return FSA_ERROR_INVALID_VALUE;
+    const int32_t G = num_heads_q / num_heads_kv;
+    if (num_splits == kSplitsBlockCentric) {
+        if (dense || wl >= 0) return FSA_ERROR_INVALID_VALUE;       // windows have no such schedule
+        if (!use_block_centric(G, num_splits, max_seqlen_q)) return FSA_ERROR_NOT_SUPPORTED;
+    }
+    if (!dense && wl < 0 && use_block_centric(G, num_splits, max_seqlen_q))
+        return prefill_bc(q, k, v, blk_idx, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
+                          max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, topk,
+                          softmax_scale, wr >= 0, workspace, workspace_bytes, out, lse, stream);
     const PrefillPlan pl = plan_prefill(batch, max_seqlen_q, num_heads_q, num_heads_kv, num_splits);
     const size_t need = prefill_workspace(pl, total_q, num_heads_q, head_dim);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
         return FSA_ERROR_WORKSPACE;
     if (pl.n_wg <= 0) return FSA_SUCCESS;
+    PrefillPlan plo = pl;
+    set_tile_order(plo, batch, num_heads_kv, max_seqlen_k, head_dim);
 
     fsa::SelFwdParams p{};
     p.q = static_cast<const uint16_t*>(q);
@@ -294,7 +442,8 @@ static fsa_status_t prefill_impl(const void* q, const void* k, const void* v,
     p.T = pl.T;
     p.mtiles = pl.mtiles;
     p.tiles_per_seq = pl.tiles_per_seq;
-    p.n_wg = pl.n_wg;
+    p.n_wg = plo.n_wg;
+    p.head_major = plo.head_major;
     p.ring = fsa::sel_attn_fwd_ring(head_dim, pl.T, p.topk);
     p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     if (fsa::sel_attn_fwd_lds_bytes(head_dim, pl.T, p.topk, p.ring) > 160 * 1024)
@@ -363,13 +512,18 @@ fsa_status_t fsa_set_wait_poll_limit(int32_t polls) {
 }
 
 size_t fsa_selected_attn_fwd_workspace_size(int32_t batch, int64_t total_q, int32_t max_seqlen_q,
-                                             int32_t num_heads_q, int32_t num_heads_kv,
-                                             int32_t head_dim, int32_t block_size, int32_t topk,
-                                             int32_t num_splits) {
-    if (total_q < 0) return 0;
+                                             int32_t max_seqlen_k, int32_t num_heads_q,
+                                             int32_t num_heads_kv, int32_t head_dim,
+                                             int32_t block_size, int32_t topk, int32_t num_splits) {
+    if (total_q < 0 || max_seqlen_k < 0) return 0;
     if (check_prefill_shape(batch, max_seqlen_q, num_heads_q, num_heads_kv, head_dim, block_size,
                             topk, num_splits) != FSA_SUCCESS)
         return 0;
+    if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return 0;
+    if (use_block_centric(num_heads_q / num_heads_kv, num_splits, max_seqlen_q))
+        return bc_layout(batch, total_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, topk)
+            .total;
+    if (num_splits < 0) return 0;                 // a forced schedule the call would reject
     const PrefillPlan pl = plan_prefill(batch, max_seqlen_q, num_heads_q, num_heads_kv, num_splits);
     return prefill_workspace(pl, total_q, num_heads_q, head_dim);
 }
@@ -392,9 +546,12 @@ size_t fsa_sliding_window_fwd_workspace_size(int32_t batch, int64_t total_q,
                                              int32_t max_seqlen_q, int32_t num_heads_q,
                                              int32_t num_heads_kv, int32_t head_dim,
                                              int32_t num_splits) {
-    return fsa_selected_attn_fwd_workspace_size(batch, total_q, max_seqlen_q, num_heads_q,
-                                                num_heads_kv, head_dim, fsa::kBlockKeys, 1,
-                                                num_splits);
+    if (total_q < 0 || num_splits < 0) return 0;
+    if (check_prefill_shape(batch, max_seqlen_q, num_heads_q, num_heads_kv, head_dim,
+                            fsa::kBlockKeys, 1, num_splits) != FSA_SUCCESS)
+        return 0;
+    const PrefillPlan pl = plan_prefill(batch, max_seqlen_q, num_heads_q, num_heads_kv, num_splits);
+    return prefill_workspace(pl, total_q, num_heads_q, head_dim);
 }
 
 fsa_status_t fsa_sliding_window_fwd(const void* q, const void* k, const void* v,

@@ -28,9 +28,39 @@ struct SelFwdParams {
     int mtiles;         // ceil(T*G/16) 16-row MFMA tiles per tile
     int tiles_per_seq;
     int n_wg;
+    int head_major;     // 1: all XCDs on one (sequence, kv head) unit at a time
     int ring;           // LDS ring slots of K/V blocks (3 or 4)
     int spin_limit;     // polls before a ring wait gives up
     float scale_log2;   // softmax_scale * log2(e)
+};
+
+// Selected-attention prefill, block-centric schedule (sel_attn_fwd_bc.hip).
+struct SelFwdBcParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* blk_idx;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    uint16_t* out;
+    float* lse;
+    // workspace
+    int32_t* counts;             // [units][nb_max + 1]: entries per block, then offsets
+    int32_t* cursor;             // [units][nb_max]: fill cursors
+    unsigned long long* masks;   // [total_q][Hkv]: list slots that count
+    int32_t* ents;               // [total_q * Hkv * topk]: token << 6 | slot, grouped by block
+    int32_t* pos;                // [total_q][Hkv][topk]: where the fill pass put each entry
+    int2* tasks;                 // [max_tasks]: (unit * nb_max + block, first tile)
+    uint32_t* ctr;               // [16]: [0] tasks written, [8 + x] next task of segment x
+    float* part_ml;              // [entry][G][2]: log2-domain max and sum, in ents order
+    uint16_t* part_o;            // [entry][G][D] bf16 partials (not divided by the sum)
+    int64_t total_q, total_k;
+    int batch, Hq, Hkv, G, topk, causal, nb_max;
+    int tpt;                     // tokens per 16-row tile
+    int nchunk_q;                // index workgroups per (sequence, kv head)
+    int max_tasks;
+    int n_wg;                    // main-kernel workgroups (persistent)
+    float scale_log2;
 };
 
 // Top-k paged decode (topk_decode.hip).
@@ -121,6 +151,10 @@ hipError_t sel_attn_bwd_wait_timeouts(unsigned int* n, bool reset);
 
 template <int D>
 hipError_t launch_sel_attn_fwd(const SelFwdParams& p, hipStream_t stream);
+hipError_t launch_sel_attn_fwd_bc(const SelFwdBcParams& p, int D, hipStream_t stream);
+constexpr int kBcTileTasks = 64;      // 16-row tiles per block-centric task
+constexpr int kBcIndexChunk = 256;    // tokens per index workgroup
+constexpr int kBcWgPerCu = 2;         // resident main-kernel workgroups per CU
 size_t sel_attn_fwd_lds_bytes(int D, int T, int topk, int ring);
 int sel_attn_fwd_ring(int D, int T, int topk);   // ring slots that fit in LDS
 int sel_attn_fwd_rows_per_tile();   // query rows (T*G) one workgroup covers

@@ -157,10 +157,23 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     const int lr = lane & 15;        // MFMA column = query row within the m-tile
     const int lg = lane >> 4;        // lane group 0..3
 
-    // ---- which tile: heavy (late) tiles first, tiles of one (seq, kv head) on one XCD
-    int w = xcd_remap(blockIdx.x, p.n_wg);
-    const int j = p.tiles_per_seq - 1 - (w % p.tiles_per_seq);
-    w /= p.tiles_per_seq;
+    // ---- which tile: heavy (late) tiles first.  Workgroups are handed to the
+    // 8 XCDs round-robin; either each XCD takes a contiguous range of units
+    // (the tiles of one (seq, kv head) share its L2), or (head_major) all XCDs
+    // work through one unit together, XCD x on its tiles x, x + 8, ...
+    int w, j;
+    if (p.head_major) {
+        const int per_xcd = (p.tiles_per_seq + 7) / 8;
+        const int kk = blockIdx.x / 8;
+        w = kk / per_xcd;
+        const int jj = (kk % per_xcd) * 8 + (int)(blockIdx.x % 8);
+        if (jj >= p.tiles_per_seq || w >= p.batch * p.Hkv * p.num_splits) return;
+        j = p.tiles_per_seq - 1 - jj;
+    } else {
+        w = xcd_remap(blockIdx.x, p.n_wg);
+        j = p.tiles_per_seq - 1 - (w % p.tiles_per_seq);
+        w /= p.tiles_per_seq;
+    }
     const int split = w % p.num_splits;
     w /= p.num_splits;
     const int g = w % p.Hkv;
