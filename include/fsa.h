@@ -271,6 +271,31 @@ fsa_status_t fsa_topk_decode(const void* q, const void* k_cache, const void* v_c
                              size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
+ * fsa_topk_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without workspace / workspace_bytes, the same kernels
+ * and the same results.  The split partials (its only scratch) go to a
+ * library-owned device array of FSA_NOALLOC_SCRATCH_BYTES per GPU, created
+ * with the library's code object on that GPU and held until the process
+ * ends; the call allocates and frees nothing.  It uses the array of the
+ * calling thread's current device, so `stream` must belong to that device.
+ * Nothing in the array needs clearing: every call overwrites the partials it
+ * reads.  Calls that overlap in time on one GPU (other streams, other
+ * threads) share the array and race.  A call whose partials would exceed
+ * the array (fsa_topk_decode_workspace_size(...) > FSA_NOALLOC_SCRATCH_BYTES)
+ * returns FSA_ERROR_WORKSPACE; other errors are those of fsa_topk_decode,
+ * plus FSA_ERROR_LAUNCH if the array's address cannot be obtained.
+ */
+#define FSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+fsa_status_t fsa_topk_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* tok_idx, const int32_t* block_table,
+                                     const int32_t* cache_seqlens, int32_t batch,
+                                     int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                     int32_t page_size, int32_t max_pages_per_seq,
+                                     int32_t num_pages, int32_t topk, float softmax_scale,
+                                     int32_t num_splits, void* out, float* lse, void* stream);
+
+/*
  * Top-k gathered decode over an FP8 paged KV cache: fsa_topk_decode with K
  * and V stored as FP8 E4M3 bytes (the torch.float8_e4m3fn format the
  * FlashAttention tutorial page lists; the flash-sparse-attn page's fused-quant

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(names) == sorted(_lib.EXPORTS)
     nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
@@ -310,3 +310,22 @@ def test_wait_diagnostics_reject_bad_arguments(lib):
     assert lib.fsa_set_wait_poll_limit(-1) == INVALID
     assert lib.fsa_wait_timeouts(None, 0) == INVALID
     assert lib.fsa_set_wait_poll_limit(0) == 0          # default restored
+
+
+def test_noalloc_decode_rejects_before_touching_the_device(lib):
+    """Argument errors and partials larger than the library's scratch array
+    are rejected on the host (no device is needed for either)."""
+    f = lib.fsa_topk_decode_noalloc
+
+    def call(**kw):
+        a = dict(batch=4, hq=8, hkv=2, d=128, page=256, maxp=8, npages=32, topk=100, splits=0)
+        a.update(kw)
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["batch"], a["hq"], a["hkv"], a["d"],
+                 a["page"], a["maxp"], a["npages"], a["topk"], 0.0, a["splits"], FAKE, None, None)
+
+    assert call(hq=6, hkv=4) == INVALID
+    assert call(d=96) == NOT_SUPPORTED
+    assert call(batch=0) == 0
+    # 64 splits x 4096 sequences x 32 heads x 129 floats > 32 MiB of partials
+    assert call(batch=4096, hq=32, hkv=8, topk=8192, splits=64) == WORKSPACE
+    assert _lib.FSA_NOALLOC_SCRATCH_BYTES == 32 << 20

@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     fsa_topk_decode,
     fsa_topk_decode_auto_splits,
     fsa_topk_decode_fp8,
+    fsa_topk_decode_noalloc,
     fsa_topk_decode_workspace_size,
     fsa_wait_timeouts,
 )
@@ -34,5 +35,5 @@ __all__ = [
     "fsa_selected_attn_fwd_workspace_size", "fsa_sliding_window_fwd",
     "fsa_sliding_window_fwd_workspace_size", "fsa_status_string", "fsa_topk_decode",
     "fsa_topk_decode_auto_splits", "fsa_topk_decode_fp8", "fsa_topk_decode_workspace_size",
-    "fsa_set_wait_poll_limit", "fsa_wait_timeouts",
+    "fsa_set_wait_poll_limit", "fsa_wait_timeouts", "fsa_topk_decode_noalloc",
 ]

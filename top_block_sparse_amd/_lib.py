@@ -30,7 +30,9 @@ EXPORTS = ("fsa_status_string", "fsa_abi_version", "fsa_selected_attn_fwd_worksp
            "fsa_sliding_window_fwd_workspace_size", "fsa_sliding_window_fwd",
            "fsa_selected_attn_bwd_workspace_size", "fsa_selected_attn_bwd",
            "fsa_block_select_workspace_size", "fsa_block_select", "fsa_wait_timeouts",
-           "fsa_set_wait_poll_limit")
+           "fsa_set_wait_poll_limit", "fsa_topk_decode_noalloc")
+
+FSA_NOALLOC_SCRATCH_BYTES = 32 << 20      # include/fsa.h
 
 _lib = None
 
@@ -88,6 +90,9 @@ def load() -> ctypes.CDLL:
     lib.fsa_block_select.restype = ctypes.c_int
     lib.fsa_block_select.argtypes = [P, P, P, P, i32, i64, i64, i32, i32, i32, i32, i32, i32, i32,
                                      i32, i32, i32, i32, f32, P, sz, P, P]
+    lib.fsa_topk_decode_noalloc.restype = ctypes.c_int
+    lib.fsa_topk_decode_noalloc.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                            i32, f32, i32, P, P, P]
     lib.fsa_wait_timeouts.restype = ctypes.c_int
     lib.fsa_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32]
     lib.fsa_set_wait_poll_limit.restype = ctypes.c_int
@@ -417,6 +422,42 @@ def fsa_topk_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     """Top-k gathered paged decode; returns ``(out [B,Hq,d], lse [B,Hq])``."""
     return _decode(q, k_cache, v_cache, None, None, tok_idx, block_table, cache_seqlens,
                    softmax_scale, num_splits, out, lse, workspace, return_lse, fp8=False)
+
+
+def fsa_topk_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            tok_idx: torch.Tensor, block_table: torch.Tensor,
+                            cache_seqlens: torch.Tensor, out: torch.Tensor,
+                            lse: Optional[torch.Tensor] = None,
+                            softmax_scale: Optional[float] = None, num_splits: int = 0) -> None:
+    """``fsa_topk_decode`` into caller-supplied ``out`` (and ``lse``) through the
+    entry point that allocates nothing: its split partials live in the
+    library's own per-GPU scratch array (include/fsa.h)."""
+    lib = load()
+    _check_dev("q", q, torch.bfloat16, 3)
+    _check_dev("k_cache", k_cache, torch.bfloat16, 4)
+    _check_dev("v_cache", v_cache, torch.bfloat16, 4)
+    _check_dev("tok_idx", tok_idx, torch.int32, 3)
+    _check_dev("block_table", block_table, torch.int32, 2)
+    _check_dev("cache_seqlens", cache_seqlens, torch.int32, 1)
+    batch, hq, d = q.shape
+    num_pages, page_size, hkv, _ = k_cache.shape
+    topk = tok_idx.shape[2]
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[3] != d:
+        raise ValueError("k_cache and v_cache must both be [num_pages, page_size, Hkv, d]")
+    if tuple(tok_idx.shape[:2]) != (batch, hkv) or block_table.shape[0] != batch \
+            or cache_seqlens.numel() != batch:
+        raise ValueError("tok_idx [B,Hkv,topk], block_table [B,max_pages], cache_seqlens [B]")
+    _same_device(q, k_cache, v_cache, tok_idx, block_table, cache_seqlens)
+    _check_buf("out", out, torch.bfloat16, tuple(q.shape), q.device)
+    if lse is not None:
+        _check_buf("lse", lse, torch.float32, (batch, hq), q.device)
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    st = lib.fsa_topk_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(tok_idx),
+                                     _ptr(block_table), _ptr(cache_seqlens), batch, hq, hkv, d,
+                                     page_size, block_table.shape[1], num_pages, topk, scale,
+                                     num_splits, _ptr(out), _ptr(lse), _stream(q.device))
+    if st != FSA_SUCCESS:
+        raise FsaError(st, "fsa_topk_decode_noalloc")
 
 
 def fsa_topk_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -183,6 +183,31 @@ SelectPlan plan_select(int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, i
 
 }  // namespace
 
+// ---- fsa_topk_decode_noalloc: the split partials of the decode (the only
+// scratch its kernels use) go to this library-owned array instead of a
+// caller workspace.  Each GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` is only a stand-in for the symbol:
+// its device address (per device) comes from hipGetSymbolAddress on the
+// first call on that device and is the one ever passed to a kernel.
+constexpr size_t kNoAllocScratchBytes = (size_t)FSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+static fsa_status_t noalloc_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FSA_ERROR_LAUNCH;
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        // (racing first calls on one device obtain the same address)
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+            return FSA_ERROR_LAUNCH;
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    *out = ptr;
+    return FSA_SUCCESS;
+}
+
 static fsa_status_t decode_impl(const void* q, const void* k_cache, const void* v_cache,
                                bool kv_fp8, const float* k_descale, const float* v_descale,
                              const int32_t* tok_idx, const int32_t* block_table,
@@ -600,6 +625,33 @@ fsa_status_t fsa_topk_decode(const void* q, const void* k_cache, const void* v_c
                        cache_seqlens, batch, num_heads_q, num_heads_kv, head_dim, page_size,
                        max_pages_per_seq, num_pages, topk, softmax_scale, num_splits, workspace,
                        workspace_bytes, out, lse, stream);
+}
+
+fsa_status_t fsa_topk_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* tok_idx, const int32_t* block_table,
+                                     const int32_t* cache_seqlens, int32_t batch,
+                                     int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                     int32_t page_size, int32_t max_pages_per_seq,
+                                     int32_t num_pages, int32_t topk, float softmax_scale,
+                                     int32_t num_splits, void* out, float* lse, void* stream) {
+    fsa_status_t st = check_decode_shape(batch, num_heads_q, num_heads_kv, head_dim, topk,
+                                         num_splits);
+    if (st != FSA_SUCCESS) return st;
+    if (batch == 0) return FSA_SUCCESS;
+    const DecodeLayout lay = decode_layout(batch, num_heads_q, num_heads_kv, head_dim, topk,
+                                           num_splits);
+    if (lay.total > kNoAllocScratchBytes) return FSA_ERROR_WORKSPACE;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    if (lay.total > 0) {
+        st = noalloc_scratch(&ws);
+        if (st != FSA_SUCCESS) return st;
+        ws_bytes = kNoAllocScratchBytes;
+    }
+    return decode_impl(q, k_cache, v_cache, false, nullptr, nullptr, tok_idx, block_table,
+                       cache_seqlens, batch, num_heads_q, num_heads_kv, head_dim, page_size,
+                       max_pages_per_seq, num_pages, topk, softmax_scale, num_splits, ws,
+                       ws_bytes, out, lse, stream);
 }
 
 fsa_status_t fsa_topk_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
