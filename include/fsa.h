@@ -20,9 +20,16 @@
  *   and a repeated id counts once (the lists are sets).  A query row that
  *   ends up with no visible key gets O = 0 and LSE = -inf.
  * - softmax_scale <= 0 selects the default 1/sqrt(head_dim).
- * - Calls are thread-safe.  The only process-wide state is diagnostic: the
- *   poll limit of the kernels' bounded waits (fsa_set_wait_poll_limit) and a
- *   device counter of waits that gave up (fsa_wait_timeouts).
+ * - max_seqlen_q / max_seqlen_k larger than total_q / total_k are read as
+ *   total_q / total_k (no sequence is longer than its tensor).  A call whose
+ *   kernels would need more than 2^22 workgroups in one launch returns
+ *   FSA_ERROR_NOT_SUPPORTED before launching anything (the query-centric
+ *   prefill, for instance, launches batch * ceil(max_seqlen_q / T) *
+ *   num_heads_kv * splits of them, T >= 1 tokens per workgroup).
+ * - Calls are thread-safe.  Process-wide state: per-device records that a
+ *   kernel's LDS limit has been raised (an idempotent runtime setting), the
+ *   scratch array of fsa_topk_decode_noalloc, and the diagnostics of the
+ *   kernels' bounded waits (fsa_set_wait_poll_limit, fsa_wait_timeouts).
  *
  * Semantics follow the pages this library is built from:
  * - GQA: query head h reads kv head h / (num_heads_q / num_heads_kv);
@@ -352,7 +359,8 @@ fsa_status_t fsa_topk_decode_fp8(const void* q, const void* k_cache, const void*
  *   kernel_size, kernel_stride, block_size  32, 16, 64 (others:
  *            FSA_ERROR_NOT_SUPPORTED)
  *   topk     1..64; init_blocks, local_blocks >= 0
- *            (num_heads_q / num_heads_kv <= 128)
+ *            (num_heads_q / num_heads_kv <= 128; max_seqlen_k <= 2^20, so
+ *            that a tile's block-importance table fits 64 KiB of LDS)
  *   workspace at least fsa_block_select_workspace_size(...) bytes (the
  *            compressed keys), 16-byte aligned; may be NULL when that is 0
  *   blk_idx  int32 [total_q, num_heads_kv, topk], written

@@ -466,15 +466,12 @@ hipError_t launch_block_select(const BlockSelectParams& p, int D, hipStream_t st
         else hipLaunchKernelGGL(cmp_keys_kernel<128>, dim3(gc), dim3(256), 0, stream, p);
     }
     const size_t lds = block_select_lds_bytes(p.T, p.nb_max, D);
-    static bool attr_set[2] = {false, false};
+    static std::atomic<unsigned long long> lds_set[2];     // devices with the LDS limit raised
     const int di = D == 64 ? 0 : 1;
-    if (!attr_set[di]) {
-        const void* f = D == 64 ? reinterpret_cast<const void*>(&block_select_kernel<64>)
-                                : reinterpret_cast<const void*>(&block_select_kernel<128>);
-        hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set[di] = true;
-    }
+    const void* f = D == 64 ? reinterpret_cast<const void*>(&block_select_kernel<64>)
+                            : reinterpret_cast<const void*>(&block_select_kernel<128>);
+    hipError_t e = ensure_lds_limit(f, lds_set[di]);
+    if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)(p.batch * p.Hkv * p.tiles_per_seq);
     if (grid > 0) {
         if (D == 64) hipLaunchKernelGGL(block_select_kernel<64>, dim3(grid), dim3(kSelectThreads), lds, stream, p);

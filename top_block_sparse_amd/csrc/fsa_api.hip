@@ -27,6 +27,19 @@ constexpr size_t kAlign = 256;
 // Polls a ring wait makes before it gives up (fsa_set_wait_poll_limit).
 std::atomic<int> g_spin_limit{fsa::kDefaultSpinLimit};
 
+// Every launch of one call is checked on the host before the first one is
+// enqueued: at most kMaxGroups workgroups (of up to 1024 work-items, so the
+// dispatch size stays within 32 bits).
+constexpr long long kMaxGroups = 1ll << 22;
+bool groups_ok(long long g) { return g >= 0 && g <= kMaxGroups; }
+
+// No sequence is longer than the rows it lives in: the caller's maximum
+// lengths are capped by the totals (which keeps every derived grid and
+// workspace size bounded by the tensors themselves).
+int32_t cap_len(int32_t max_len, int64_t total) {
+    return (int64_t)max_len > total ? (int32_t)total : max_len;
+}
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -47,8 +60,10 @@ constexpr long long kHeadMajorBytes = 8ll << 20;
 
 void set_tile_order(PrefillPlan& pl, int32_t batch, int32_t Hkv, int32_t max_seqlen_k, int32_t D) {
     if ((long long)max_seqlen_k * D * 2 * 2 <= kHeadMajorBytes) return;
+    const long long n = (long long)batch * Hkv * pl.splits * ((pl.tiles_per_seq + 7) / 8) * 8;
+    if (!groups_ok(n)) return;
     pl.head_major = 1;
-    pl.n_wg = (int)((long long)batch * Hkv * pl.splits * ((pl.tiles_per_seq + 7) / 8) * 8);
+    pl.n_wg = (int)n;
 }
 
 // num_splits: 0 automatic, n >= 1 query-centric with n splits, -1 block-centric
@@ -75,7 +90,7 @@ PrefillPlan plan_prefill(int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_
     if (T < 1) T = 1;
     pl.T = T;
     pl.mtiles = (T * G + 15) / 16;
-    pl.tiles_per_seq = (max_seqlen_q + T - 1) / T;
+    pl.tiles_per_seq = (int)(((long long)max_seqlen_q + T - 1) / T);
     const long long base = (long long)batch * pl.tiles_per_seq * Hkv;
     int s = num_splits;
     if (s == 0) {
@@ -87,7 +102,7 @@ PrefillPlan plan_prefill(int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_
         }
     }
     pl.splits = s;
-    pl.n_wg = (int)(base * s);
+    pl.n_wg = groups_ok(base * s) ? (int)(base * s) : -1;      // -1: too many workgroups
     pl.head_major = 0;
     return pl;
 }
@@ -169,7 +184,7 @@ fsa_status_t check_select(int32_t batch, int32_t max_seqlen_q, int32_t max_seqle
 SelectPlan plan_select(int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, int32_t Hkv) {
     SelectPlan pl{};
     const int G = Hq / Hkv;
-    pl.nb_max = (max_seqlen_k + fsa::kBlockKeys - 1) / fsa::kBlockKeys;
+    pl.nb_max = (int)(((long long)max_seqlen_k + fsa::kBlockKeys - 1) / fsa::kBlockKeys);
     if (pl.nb_max < 1) pl.nb_max = 1;
     pl.ncmp_max = max_seqlen_k >= kSelectCmpSize ? (max_seqlen_k - kSelectCmpSize) / kSelectCmpStride + 1 : 0;
     int T = 128 / G;                            // 8 m-tiles of 16 rows
@@ -177,7 +192,7 @@ SelectPlan plan_select(int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, i
     T = T < t_lds ? T : t_lds;
     pl.T = T;                                   // 0: the table does not fit
     pl.mtiles = (T * G + 15) / 16;
-    pl.tiles_per_seq = T > 0 ? (max_seqlen_q + T - 1) / T : 0;
+    pl.tiles_per_seq = T > 0 ? (int)(((long long)max_seqlen_q + T - 1) / T) : 0;
     return pl;
 }
 
@@ -228,6 +243,9 @@ static fsa_status_t decode_impl(const void* q, const void* k_cache, const void* 
         return FSA_ERROR_INVALID_VALUE;
     const DecodeLayout lay = decode_layout(batch, num_heads_q, num_heads_kv, head_dim, topk,
                                            num_splits);
+    if (!groups_ok((long long)batch * num_heads_kv * lay.splits) ||
+        !groups_ok(((long long)batch * num_heads_q + 3) / 4))
+        return FSA_ERROR_NOT_SUPPORTED;
     if (lay.total > 0 && (workspace == nullptr || workspace_bytes < lay.total ||
                           (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0))
         return FSA_ERROR_WORKSPACE;
@@ -302,8 +320,10 @@ constexpr int kMaxSeqBc = 1 << 25;      // token index within a sequence << 6 mu
 constexpr int kMaxGroupBcForced = 16;   // a 16-row MFMA tile holds at least one token
 constexpr int32_t kSplitsBlockCentric = -1;
 
-bool use_block_centric(int32_t G, int32_t num_splits, int32_t max_seqlen_q) {
+bool use_block_centric(int32_t G, int32_t num_splits, int32_t max_seqlen_q, int64_t total_q,
+                       int32_t Hkv, int32_t topk) {
     if (max_seqlen_q >= kMaxSeqBc) return false;
+    if (total_q * Hkv * topk > INT32_MAX) return false;      // entry positions are int32
     if (num_splits == kSplitsBlockCentric) return G <= kMaxGroupBcForced;
     return num_splits == 0 && G <= kMaxGroupBc;
 }
@@ -397,7 +417,11 @@ static fsa_status_t prefill_bc(const void* q, const void* k, const void* v, cons
     p.nb_max = lay.nb_max;
     p.tpt = lay.tpt;
     p.max_tasks = lay.max_tasks;
-    p.nchunk_q = (int)((max_seqlen_q + fsa::kBcIndexChunk - 1) / fsa::kBcIndexChunk);
+    p.nchunk_q = (int)(((long long)max_seqlen_q + fsa::kBcIndexChunk - 1) / fsa::kBcIndexChunk);
+    const int rows_per_merge_wg = 256 / (head_dim / 8);
+    if (!groups_ok((long long)batch * num_heads_kv * p.nchunk_q) ||
+        !groups_ok(((long long)total_q * num_heads_q + rows_per_merge_wg - 1) / rows_per_merge_wg))
+        return FSA_ERROR_NOT_SUPPORTED;
     const long long nwg = (long long)cus * fsa::kBcWgPerCu;
     p.n_wg = (int)(nwg < lay.max_tasks ? nwg : lay.max_tasks);
     if (p.n_wg < 1) p.n_wg = 1;
@@ -422,6 +446,8 @@ static fsa_status_t prefill_impl(const void* q, const void* k, const void* v,
     if (st != FSA_SUCCESS) return st;
     if (total_q < 0 || total_k < 0 || max_seqlen_k < 0) return FSA_ERROR_INVALID_VALUE;
     if (total_q > INT32_MAX || total_k > INT32_MAX) return FSA_ERROR_NOT_SUPPORTED;
+    max_seqlen_q = cap_len(max_seqlen_q, total_q);
+    max_seqlen_k = cap_len(max_seqlen_k, total_k);
     if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FSA_SUCCESS;   // nothing to do
     if (!q || !k || !v || (!dense && !blk_idx) || !cu_seqlens_q || !cu_seqlens_k || !out)
         return FSA_ERROR_INVALID_VALUE;
@@ -430,17 +456,21 @@ static fsa_status_t prefill_impl(const void* q, const void* k, const void* v,
     const int32_t G = num_heads_q / num_heads_kv;
     if (num_splits == kSplitsBlockCentric) {
         if (dense || wl >= 0) return FSA_ERROR_INVALID_VALUE;       // windows have no such schedule
-        if (!use_block_centric(G, num_splits, max_seqlen_q)) return FSA_ERROR_NOT_SUPPORTED;
+        if (!use_block_centric(G, num_splits, max_seqlen_q, total_q, num_heads_kv, topk))
+            return FSA_ERROR_NOT_SUPPORTED;
     }
-    if (!dense && wl < 0 && use_block_centric(G, num_splits, max_seqlen_q))
+    if (!dense && wl < 0 && use_block_centric(G, num_splits, max_seqlen_q, total_q, num_heads_kv, topk))
         return prefill_bc(q, k, v, blk_idx, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k,
                           max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, topk,
                           softmax_scale, wr >= 0, workspace, workspace_bytes, out, lse, stream);
     const PrefillPlan pl = plan_prefill(batch, max_seqlen_q, num_heads_q, num_heads_kv, num_splits);
     const size_t need = prefill_workspace(pl, total_q, num_heads_q, head_dim);
+    if (pl.n_wg < 0) return FSA_ERROR_NOT_SUPPORTED;                // grid too large
+    if (pl.splits > 1 && !groups_ok(((long long)total_q * num_heads_q + 3) / 4))
+        return FSA_ERROR_NOT_SUPPORTED;                             // merge grid
     if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
         return FSA_ERROR_WORKSPACE;
-    if (pl.n_wg <= 0) return FSA_SUCCESS;
+    if (pl.n_wg == 0) return FSA_SUCCESS;
     PrefillPlan plo = pl;
     set_tile_order(plo, batch, num_heads_kv, max_seqlen_k, head_dim);
 
@@ -507,7 +537,12 @@ static fsa_status_t prefill_impl(const void* q, const void* k, const void* v,
 extern "C" {
 
 const char* fsa_status_string(fsa_status_t status) {
-    switch (status) {
+    // Callers may pass any integer; reading it as an int keeps out-of-range
+    // codes defined (a load of an enum outside its values is not).
+    static_assert(sizeof(fsa_status_t) == sizeof(int), "status is passed as an int");
+    int code;
+    std::memcpy(&code, &status, sizeof code);
+    switch (code) {
         case FSA_SUCCESS: return "FSA_SUCCESS";
         case FSA_ERROR_INVALID_VALUE: return "FSA_ERROR_INVALID_VALUE";
         case FSA_ERROR_NOT_SUPPORTED: return "FSA_ERROR_NOT_SUPPORTED";
@@ -544,8 +579,10 @@ size_t fsa_selected_attn_fwd_workspace_size(int32_t batch, int64_t total_q, int3
     if (check_prefill_shape(batch, max_seqlen_q, num_heads_q, num_heads_kv, head_dim, block_size,
                             topk, num_splits) != FSA_SUCCESS)
         return 0;
+    max_seqlen_q = cap_len(max_seqlen_q, total_q);
     if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return 0;
-    if (use_block_centric(num_heads_q / num_heads_kv, num_splits, max_seqlen_q))
+    if (use_block_centric(num_heads_q / num_heads_kv, num_splits, max_seqlen_q, total_q,
+                          num_heads_kv, topk))
         return bc_layout(batch, total_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, topk)
             .total;
     if (num_splits < 0) return 0;                 // a forced schedule the call would reject
@@ -575,6 +612,7 @@ size_t fsa_sliding_window_fwd_workspace_size(int32_t batch, int64_t total_q,
     if (check_prefill_shape(batch, max_seqlen_q, num_heads_q, num_heads_kv, head_dim,
                             fsa::kBlockKeys, 1, num_splits) != FSA_SUCCESS)
         return 0;
+    max_seqlen_q = cap_len(max_seqlen_q, total_q);
     const PrefillPlan pl = plan_prefill(batch, max_seqlen_q, num_heads_q, num_heads_kv, num_splits);
     return prefill_workspace(pl, total_q, num_heads_q, head_dim);
 }
@@ -587,7 +625,8 @@ fsa_status_t fsa_sliding_window_fwd(const void* q, const void* k, const void* v,
                                     int32_t window_left, int32_t window_right,
                                     float softmax_scale, int32_t num_splits, void* workspace,
                                     size_t workspace_bytes, void* out, float* lse, void* stream) {
-    if (window_left < -1 || window_right < -1 || max_seqlen_k < 0) return FSA_ERROR_INVALID_VALUE;
+    if (window_left < -1 || window_right < -1 || max_seqlen_k < 0 || num_splits < 0)
+        return FSA_ERROR_INVALID_VALUE;     // (windows have no block-centric schedule)
     // A left bound of at least max_seqlen_k keys reaches below key 0 for every
     // row (i + S_k - S_q - left <= S_k - 1 - left < 0), so it is the same as
     // no limit.  The right bound is passed on unchanged: when S_q > S_k a
@@ -676,7 +715,7 @@ struct BwdLayout {
 static BwdLayout bwd_layout(int32_t batch, int64_t total_q, int64_t total_k, int32_t max_seqlen_k,
                             int32_t Hq, int32_t Hkv, int32_t D, int32_t topk) {
     BwdLayout l{};
-    l.nb_max = (max_seqlen_k + fsa::kBlockKeys - 1) / fsa::kBlockKeys;
+    l.nb_max = (int)(((long long)max_seqlen_k + fsa::kBlockKeys - 1) / fsa::kBlockKeys);
     if (l.nb_max < 1) l.nb_max = 1;
     size_t off = 0;
     l.dvec = off;
@@ -711,6 +750,7 @@ size_t fsa_selected_attn_bwd_workspace_size(int32_t batch, int64_t total_q, int6
         check_bwd_shape(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv,
                         head_dim, block_size, topk) != FSA_SUCCESS)
         return 0;
+    max_seqlen_k = cap_len(max_seqlen_k, total_k);
     return bwd_layout(batch, total_q, total_k, max_seqlen_k, num_heads_q, num_heads_kv, head_dim,
                       topk).total;
 }
@@ -729,6 +769,8 @@ fsa_status_t fsa_selected_attn_bwd(const void* q, const void* k, const void* v, 
     if (st != FSA_SUCCESS) return st;
     if (total_k < 0) return FSA_ERROR_INVALID_VALUE;
     if (total_q > INT32_MAX || total_k > INT32_MAX) return FSA_ERROR_NOT_SUPPORTED;
+    max_seqlen_q = cap_len(max_seqlen_q, total_q);
+    max_seqlen_k = cap_len(max_seqlen_k, total_k);
     if (batch == 0 || (total_q == 0 && total_k == 0)) return FSA_SUCCESS;
     if (!q || !k || !v || !out || !lse || !dout || !blk_idx || !cu_seqlens_q || !cu_seqlens_k ||
         !dq || !dk || !dv)
@@ -792,11 +834,19 @@ fsa_status_t fsa_selected_attn_bwd(const void* q, const void* k, const void* v, 
     p.T = T;
     p.ring = dq_ring;
     p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-    p.nchunk_q = (max_seqlen_q + fsa::sel_attn_bwd_index_chunk() - 1) / fsa::sel_attn_bwd_index_chunk();
+    const int chunk = fsa::sel_attn_bwd_index_chunk();
+    p.nchunk_q = (int)(((long long)max_seqlen_q + chunk - 1) / chunk);
     if (p.nchunk_q < 1) p.nchunk_q = 1;
     p.mtiles = (T * G + 15) / 16;
-    p.tiles_per_seq = (max_seqlen_q + T - 1) / T;
+    p.tiles_per_seq = (int)(((long long)max_seqlen_q + T - 1) / T);
     if (p.tiles_per_seq < 1) p.tiles_per_seq = 1;
+    {
+        const long long units = (long long)batch * num_heads_kv;
+        if (!groups_ok(((long long)total_q * num_heads_q + 15) / 16) ||
+            !groups_ok(units * p.nchunk_q) || !groups_ok(units * lay.nb_max * p.nparts) ||
+            !groups_ok(units * p.tiles_per_seq))
+            return FSA_ERROR_NOT_SUPPORTED;
+    }
     p.scale = resolve_scale(softmax_scale, head_dim);
     p.scale_log2 = p.scale * fsa::kLog2e;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -828,11 +878,16 @@ fsa_status_t fsa_block_select(const void* q, const void* k, const int32_t* cu_se
     if (st != FSA_SUCCESS) return st;
     if (total_q < 0 || total_k < 0) return FSA_ERROR_INVALID_VALUE;
     if (total_q > INT32_MAX || total_k > INT32_MAX) return FSA_ERROR_NOT_SUPPORTED;
+    max_seqlen_q = cap_len(max_seqlen_q, total_q);
+    max_seqlen_k = cap_len(max_seqlen_k, total_k);
     if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return FSA_SUCCESS;   // nothing to do
     if (!q || !k || !cu_seqlens_q || !cu_seqlens_k || !blk_idx) return FSA_ERROR_INVALID_VALUE;
     if (!aligned16(q) || !aligned16(k)) return FSA_ERROR_INVALID_VALUE;
     const SelectPlan pl = plan_select(max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv);
     if (pl.T < 1) return FSA_ERROR_NOT_SUPPORTED;
+    if (!groups_ok((long long)batch * num_heads_kv * pl.tiles_per_seq) ||
+        !groups_ok(((long long)batch * pl.ncmp_max * num_heads_kv * (head_dim / 8) + 255) / 256))
+        return FSA_ERROR_NOT_SUPPORTED;
     const size_t need = fsa_block_select_workspace_size(batch, max_seqlen_k, num_heads_kv, head_dim,
                                                         kernel_size, kernel_stride);
     if (pl.ncmp_max > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fsa {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;   // MFMA 16x16x32 operand
@@ -137,6 +139,21 @@ __device__ __forceinline__ bool wait_done(const uint32_t* done, uint32_t target,
     gave_up = true;
     note_wait_timeout(abort_word, counter, lane);
     return false;
+}
+
+// Raise a kernel's dynamic LDS limit to 160 KiB on the calling thread's
+// current device.  The runtime keeps the attribute per device, so `done`
+// holds one bit per device id (< 64) on which it has been set; racing
+// threads set the same value.
+inline hipError_t ensure_lds_limit(const void* fn, std::atomic<unsigned long long>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned long long bit = (dev >= 0 && dev < 64) ? 1ull << dev : 0ull;
+    if (bit != 0ull && (done.load(std::memory_order_acquire) & bit) != 0ull) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e == hipSuccess && bit != 0ull) done.fetch_or(bit, std::memory_order_release);
+    return e;
 }
 
 // Workgroups are handed to the 8 XCDs round-robin (id % 8).  Give each XCD a

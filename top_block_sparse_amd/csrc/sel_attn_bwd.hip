@@ -948,13 +948,9 @@ static hipError_t launch_bwd_d(const SelBwdParams& p, hipStream_t stream) {
                        dim3(kBwdKvThreads), 0, stream, p);
     hipLaunchKernelGGL(bwd_dkv_finish_kernel<D>, dim3((unsigned)(p.batch * p.Hkv * p.nb_max)),
                        dim3(256), 0, stream, p);
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_kernel<D>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<unsigned long long> lds_set{0ull};   // devices with the LDS limit raised
+    hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&bwd_dq_kernel<D>), lds_set);
+    if (e != hipSuccess) return e;
     const size_t lds = DqLds<D>::bytes(p.T, p.topk, p.ring);
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)(p.batch * p.Hkv * p.tiles_per_seq)),
                        dim3(kBwdDqThreads), lds, stream, p);

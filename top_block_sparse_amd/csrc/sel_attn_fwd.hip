@@ -618,13 +618,9 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
 template <int D, bool WIN>
 static hipError_t launch_sel_attn_fwd_t(const SelFwdParams& p, hipStream_t stream) {
     const size_t lds = SelLds<D>::bytes(p.T, p.topk, p.ring);
-    static bool attr_set = false;   // idempotent; racing threads set the same value
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sel_attn_fwd_kernel<D, WIN>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<unsigned long long> lds_set{0ull};   // devices with the LDS limit raised
+    hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&sel_attn_fwd_kernel<D, WIN>), lds_set);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((sel_attn_fwd_kernel<D, WIN>), dim3(p.n_wg), dim3(kSelThreads), lds, stream, p);
     return hipGetLastError();
 }

@@ -459,13 +459,9 @@ decode_kernel(const DecodeParams p) {
 
 template <int D, int GM, bool F8>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
-    static bool attr_set = false;   // idempotent; racing threads set the same value
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<D, GM, F8>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<unsigned long long> lds_set{0ull};   // devices with the LDS limit raised
+    hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(&decode_kernel<D, GM, F8>), lds_set);
+    if (e != hipSuccess) return e;
     const size_t lds = DecLds<D, GM>::bytes(p.ts, p.topk);
     hipLaunchKernelGGL((decode_kernel<D, GM, F8>), dim3(p.batch * p.Hkv * p.splits),
                        dim3(DecLds<D, GM>::NW * 64), lds, stream, p);
