@@ -89,6 +89,9 @@ def settle(want, got, may_be_big):
 def test_prefill_planning(lib, a):
     hq = a["hkv"] * a["G"]
     want = expected_prefill(a["G"], a["D"], a["topk"], a["splits"])
+    # (the size query has no total_k to cap max_seqlen_k by, so it is given a
+    # max_seqlen_k that respects it, as a caller's does: total_k = total_q here)
+    a = dict(a, max_seqlen_k=min(a["max_seqlen_k"], a["total_q"]))
     ws = lib.fsa_selected_attn_fwd_workspace_size(a["batch"], a["total_q"], a["max_seqlen_q"],
                                                   a["max_seqlen_k"], hq, a["hkv"], a["D"], 64,
                                                   a["topk"], a["splits"])
