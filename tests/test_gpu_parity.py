@@ -363,6 +363,8 @@ DECODE_SHAPES = [
     (5, 32, 8, 128, 2048, 256, 2048),
     (1, 8, 1, 128, 9000, 512, 8192),   # largest topk
     (3, 4, 2, 128, 1500, 128, 512),    # G = 2
+    (2, 16, 2, 64, 1200, 32, 400),     # G = 8, d = 64
+    (2, 32, 2, 64, 800, 64, 256),      # G = 16, d = 64
 ]
 
 
@@ -409,6 +411,24 @@ def test_decode_without_lse_output():
     o, l, ro, rl = run_decode(dd, lse=False)
     assert l is None
     compare_decode(o, None, ro, rl)
+
+
+def test_decode_with_an_empty_cache():
+    """num_pages = 0: no list entry can be valid, so every row is empty
+    (O = 0, LSE = -inf) and no cache row is read."""
+    spec = inputs.DecodeSpec("t", 3, 8, 2, 128, 600, 64, 200, seed=13)
+    dd = inputs.make_decode(spec)
+    q, kc, vc = dd["q"].to(DEV), dd["k_cache"].to(DEV), dd["v_cache"].to(DEV)
+    tok, bt, cs = dd["tok_idx"].to(DEV), dd["block_table"].to(DEV), dd["cache_seqlens"].to(DEV)
+    out = torch.full_like(q, 7.0)
+    lse = torch.zeros((3, 8), dtype=torch.float32, device=DEV)
+    lib = fsa._lib.load()
+    P = fsa._lib._ptr
+    st = lib.fsa_topk_decode(P(q), P(kc), P(vc), P(tok), P(bt), P(cs), 3, 8, 2, 128, 64,
+                             bt.shape[1], 0, 200, 0.0, 1, None, 0, P(out), P(lse), None)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert bool((out == 0).all()) and bool((lse == -math.inf).all())
 
 
 def test_decode_full_size_workload():

@@ -16,42 +16,54 @@
 //   1. validate and translate: every list entry is checked (0 <= t <
 //      cache_seqlens[b], page slot and page id in range) and translated
 //      through the block table to a physical cache row, all in LDS;
-//   2. set semantics: an LDS hash table keyed by position keeps, for every
-//      distinct valid position, its first list entry (open addressing with
-//      linear probing, at most a quarter full when LDS allows); every other
-//      entry is marked skipped.  A split list is cut by entry index, so the
-//      parts are disjoint whatever the list holds;
-//   3. the waves stream the workgroup's part in batches of 4*kDecUnroll
-//      entries taken from a shared counter (so they finish together):
-//      sixteen lanes cover one row (16 or 8 bytes each), so a wave loads four
-//      rows per instruction; a batch is kDecUnroll such groups of K and V, and
-//      each wave keeps two batches in flight (the next one's loads go out
-//      before the current one is consumed); each lane group runs its own
-//      online softmax; the probabilities are
-//      rounded to bf16 for the P.V products (bf16 dot2 with fp32
-//      accumulation), the row sums stay fp32;
-//   4. the lane groups, then the waves, are merged by logsumexp in LDS, and
-//      the workgroup writes O and LSE (or, for a split list, its normalised
-//      partial, combined afterwards by lse_merge.hip).
+//   2. set semantics: an LDS hash table of positions (open addressing with
+//      linear probing, at most a quarter full when LDS allows) admits each
+//      distinct valid position once.  A wave claims the positions of the
+//      entries it is about to load with one compare-and-swap each, just
+//      before loading them, so there is no separate de-duplication pass: the
+//      entry whose claim lands first is streamed and every other entry of
+//      that position is skipped.  A split list is cut by entry index, and a
+//      part first enters the positions of all earlier entries, so a position
+//      is streamed by the part that holds its first occurrence only;
+//   3. the waves stream the workgroup's part in pairs of batches taken
+//      from a shared counter (so they finish together): 16 lanes cover a
+//      bf16 row and 8 an E4M3 row (16 for more than 4 query heads), so a wave
+//      loads 4 (or 8) rows per instruction; a batch is two such row groups of
+//      K and V, and each wave holds two batches with fixed roles, one in
+//      flight while the other is consumed; each row group runs its own online
+//      softmax with a lazily moved maximum; the probabilities are rounded to
+//      bf16 for the P.V products (bf16 dot2 with fp32 accumulation), the row
+//      sums stay fp32;
+//   4. the row groups (with cross-lane swaps), then the waves (in LDS) are
+//      merged by logsumexp, and the workgroup writes O and LSE (or, for a
+//      split list, its normalised partial, combined afterwards by
+//      lse_merge.hip).
 #include "fsa_common.h"
 #include "fsa_params.h"
 
 namespace fsa {
 
-constexpr int kDecUnroll = 4;            // row groups per batch (halved for G > 4)
+constexpr int kDecRowsPerLane = 2;       // rows each lane holds in one batch
+constexpr float kDecLazyMax = 8.f;       // running-max slack before a rescale (log2 units)
 constexpr int kDecWavesSmallG = 8;       // waves per workgroup for G <= 4
 constexpr int kDecMaxTopk = 8192;
 constexpr int kDecBtLds = 2048;          // block-table rows up to this length are staged in LDS
-constexpr unsigned long long kDecEmpty = ~0ull;
+constexpr uint32_t kDecEmpty = ~0u;        // free hash slot (positions are below 2^31)
 
 __host__ __device__ constexpr int dec_waves(int GM) { return GM <= 4 ? kDecWavesSmallG : (GM == 8 ? 8 : 4); }
+// Lanes that share one cache row.  A 256-byte bf16 row is read by 16 lanes
+// (16 bytes each, one instruction per row group).  A 128-byte E4M3 row is
+// read by 8 lanes when the accumulators of all query heads fit in registers
+// (up to 4 heads): half the load instructions and shorter cross-lane sums.
+__host__ __device__ constexpr int dec_lanes_per_row(int GM, bool F8) { return F8 && GM <= 4 ? 8 : 16; }
 
 // LDS layout (bytes) of the decode workgroup for a hash table of ts slots.
-//   region 0: u64 table[ts] (steps 1-2): slot = position << 32 | list entry,
+//   region 0: u32 table[ts] (steps 2-3): claimed positions,
 //             reused for the wave partials (step 4): NW * GM records of D
 //             accumulator values + max + sum (fp32)
 //   i32 rows[topk]          physical cache row of each entry (-1: skipped)
-//   i32 next                next batch of entries to stream
+//   i32 pos[topk]           position of each valid entry (-1: invalid)
+//   i32 next                next pair of batches to stream
 //   i32 btl[kDecBtLds]      the sequence's block-table row (when it fits)
 template <int D, int GM>
 struct DecLds {
@@ -59,11 +71,12 @@ struct DecLds {
     static constexpr int KMAX = kDecMaxTopk / (NW * 64);
     static constexpr int kRec = D + 2;
     __host__ __device__ static int region0(int ts) {
-        const int a = ts * 8, b = NW * GM * kRec * 4;
+        const int a = ts * 4, b = NW * GM * kRec * 4;
         return ((a > b ? a : b) + 15) & ~15;
     }
     __host__ __device__ static int rows(int ts) { return region0(ts); }
-    __host__ __device__ static int next(int ts, int topk) { return rows(ts) + ((topk * 4 + 15) & ~15); }
+    __host__ __device__ static int pos(int ts, int topk) { return rows(ts) + ((topk * 4 + 15) & ~15); }
+    __host__ __device__ static int next(int ts, int topk) { return pos(ts, topk) + ((topk * 4 + 15) & ~15); }
     __host__ __device__ static int btl(int ts, int topk) { return next(ts, topk) + 16; }
     __host__ __device__ static int bytes(int ts, int topk) { return btl(ts, topk) + kDecBtLds * 4; }
 };
@@ -74,19 +87,74 @@ __device__ __forceinline__ int dec_hash(int x, int ts) {
     return (int)(((unsigned long long)((uint32_t)x * 0x9E3779B1u) * (uint32_t)ts) >> 32);
 }
 
-// Sum over the 16 lanes of a row of the wave (every lane gets the total):
-// swap neighbours, swap pairs, mirror within 8, mirror within 16.
-__device__ __forceinline__ float row16_sum(float x) {
+// Sum over N (8 or 16) aligned lanes of the wave, every lane getting the
+// total: swap neighbours, swap pairs, mirror within 8, then mirror within 16.
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+    if constexpr (N == 16)
+        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+    return x;
+}
+
+// Combine x over the lanes l ^ O, l ^ 2O, ..., l ^ 32 (O = 8 or 16), every
+// lane getting the result: a half-row rotation for 8, then the gfx950
+// permlane swaps across 16-lane rows (VALU only).
+template <int O, bool MAX>
+__device__ __forceinline__ float lanes_combine(float x) {
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+    if constexpr (O == 8)
+        x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
+    {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
     return x;
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Raw words of one lane's part of a cache or query row (aligned to their size).
+template <int N>
+__device__ __forceinline__ void load_words(const uint8_t* ptr, uint32_t (&w)[N]) {
+    if constexpr (N == 8) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ptr);
+        const u32x4_t b = *reinterpret_cast<const u32x4_t*>(ptr + 16);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) { w[x] = a[x]; w[4 + x] = b[x]; }
+    } else if constexpr (N == 4) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(ptr);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) w[x] = a[x];
+    } else if constexpr (N == 2) {
+        const u32x2_t a = *reinterpret_cast<const u32x2_t*>(ptr);
+        w[0] = a[0];
+        w[1] = a[1];
+    } else {
+        w[0] = *reinterpret_cast<const uint32_t*>(ptr);
+    }
+}
+
+// NCH chunks of N / NCH words each, chunk c at p + c * stride bytes.
+template <int NCH, int N>
+__device__ __forceinline__ void load_chunks(const uint8_t* ptr, int stride, uint32_t (&w)[N]) {
+    constexpr int M = N / NCH;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        uint32_t t[M];
+        load_words<M>(ptr + c * stride, t);
+#pragma unroll
+        for (int x = 0; x < M; ++x) w[c * M + x] = t[x];
+    }
 }
 
 // D: head dim (64 or 128); GM: query heads handled per kv head (>= G);
@@ -97,26 +165,38 @@ decode_kernel(const DecodeParams p) {
     using L = DecLds<D, GM>;
     constexpr int NW = L::NW;
     constexpr int NT = NW * 64;
-    constexpr int DPL = D / 16;              // dims per lane (8 or 4)
+    constexpr int LPR = dec_lanes_per_row(GM, F8);   // lanes sharing one cache row
+    constexpr int RPW = 64 / LPR;            // rows a wave covers per load instruction
+    constexpr int DPL = D / LPR;             // dims per lane (4 to 16)
     constexpr int WPL = DPL / 2;             // bf16 pairs per lane and row
     constexpr int EB = F8 ? 1 : 2;           // bytes per cache element
-    constexpr int RW = DPL * EB / 4;         // raw 32-bit words per lane and row
-    constexpr int U = GM > 4 ? kDecUnroll / 2 : kDecUnroll;
+    constexpr int RW = DPL * EB / 4;         // raw 32-bit words per lane and row (1 to 8)
+    // A lane's part of a row is NCH chunks of CE elements (at most 16 bytes
+    // of cache each); the LPR lanes' chunks c are adjacent, so one load
+    // instruction reads whole contiguous stretches of its rows.  Element j of
+    // the lane is head dim (j / CE) * CE * LPR + CE * lr + j % CE.
+    constexpr int CH = 16 / EB;              // cache elements per 16 bytes
+    constexpr int NCH = DPL > CH ? DPL / CH : 1;
+    constexpr int CE = DPL / NCH;
+    constexpr int U = kDecRowsPerLane;       // rows per lane in one batch
+    constexpr int B = U * RPW;               // list entries per batch
+    static_assert(2 * B <= 64, "a pair's entries are claimed by one lane each");
 
     constexpr int KMAX = L::KMAX;            // list entries per thread, at most
 
     extern __shared__ __align__(16) uint8_t smem[];
     const int ts = p.ts;
     const int topk = p.topk;
-    unsigned long long* table = reinterpret_cast<unsigned long long*>(smem);
+    uint32_t* table = reinterpret_cast<uint32_t*>(smem);
     int* rows = reinterpret_cast<int*>(smem + L::rows(ts));
+    int* pos = reinterpret_cast<int*>(smem + L::pos(ts, topk));
     int* next = reinterpret_cast<int*>(smem + L::next(ts, topk));
     int* btl = reinterpret_cast<int*>(smem + L::btl(ts, topk));
     float* mrg = reinterpret_cast<float*>(smem);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lr = lane & 15;                // 16 lanes share one cache row
-    const int lg = lane >> 4;                // which of the wave's 4 rows
+    const int lr = lane % LPR;               // LPR lanes share one cache row
+    const int lg = lane / LPR;               // which of the wave's RPW rows
     const int unit = blockIdx.x / p.splits;  // b * Hkv + g
     const int split = blockIdx.x % p.splits;
     const int b = unit / p.Hkv;
@@ -126,17 +206,40 @@ decode_kernel(const DecodeParams p) {
     const int32_t* lst = p.tok_idx + (int64_t)unit * topk;
     const int32_t* bt = p.block_table + (int64_t)b * p.max_pages;
     const int nchunk = (topk + NT - 1) / NT;     // <= KMAX
+    const int r_lo = (int)(((long long)topk * split) / p.splits);
+    const int r_hi = (int)(((long long)topk * (split + 1)) / p.splits);
+
+    // This lane's dims of the G query rows (bf16 pairs), loaded first: every
+    // later load is a cache row, so the streaming loop's waits count only those.
+    uint32_t qw[GM][WPL];
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+        if (h < G) {
+            const uint16_t* qr = p.q + ((int64_t)b * p.Hq + g * G + h) * D + CE * lr;
+            load_chunks<NCH>(reinterpret_cast<const uint8_t*>(qr), CE * LPR * 2, qw[h]);
+        } else {
+#pragma unroll
+            for (int x = 0; x < WPL; ++x) qw[h][x] = 0u;
+        }
+    }
+    // scale (log2 units) including the K dequantisation factor; V's factor
+    // scales the output
+    float c_log2 = p.scale_log2, v_scale = 1.f;
+    if constexpr (F8) {
+        if (p.k_descale != nullptr) c_log2 *= p.k_descale[unit];
+        if (p.v_descale != nullptr) v_scale = p.v_descale[unit];
+    }
 
     // ---- 1. validate and translate this thread's entries e = k*NT + tid.
     // Straight-line passes (all list loads together with the block-table row,
     // then the lookups) so the loads of different entries are in flight
-    // together.
+    // together; chunks past the list are skipped (a uniform test).
     for (int i = tid; i < ts; i += NT) table[i] = kDecEmpty;
     int key[KMAX], phys[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         const int e = k * NT + tid;
-        key[k] = lst[e < topk ? e : topk - 1];
+        key[k] = k < nchunk ? lst[e < topk ? e : topk - 1] : -1;
     }
     const bool bt_in_lds = p.max_pages <= kDecBtLds;
     if (bt_in_lds)
@@ -152,138 +255,103 @@ decode_kernel(const DecodeParams p) {
     if (bt_in_lds) {
         __syncthreads();
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) phys[k] = btl[phys[k]];   // page id, checked below
+        for (int k = 0; k < KMAX; ++k)
+            if (k < nchunk) phys[k] = btl[phys[k]];   // page id, checked below
     } else {
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) phys[k] = bt[phys[k]];
+        for (int k = 0; k < KMAX; ++k)
+            if (k < nchunk) phys[k] = bt[phys[k]];
     }
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-        const int x = key[k];
-        const int page = phys[k];
-        const bool ok = x >= 0 && page >= 0 && page < p.num_pages;
-        const int slot = x / p.page_size;
-        phys[k] = ok ? page * p.page_size + (x - slot * p.page_size) : 0;
-        key[k] = ok ? x : -1;
-        const int e = k * NT + tid;
-        if (k < nchunk && e < topk) rows[e] = ok ? phys[k] : -1;
+        if (k < nchunk) {
+            const int x = key[k];
+            const int page = phys[k];
+            const bool ok = x >= 0 && page >= 0 && page < p.num_pages;
+            const int slot = x / p.page_size;
+            const int e = k * NT + tid;
+            if (e < topk) {
+                rows[e] = ok ? page * p.page_size + (x - slot * p.page_size) : -1;
+                pos[e] = ok ? x : -1;
+            }
+        }
     }
-    if (tid == 0) *next = NW;                    // batches 0..NW-1: each wave's first
+    if (tid == 0) *next = NW;                    // pairs 0..NW-1: each wave's first
     __syncthreads();
 
-    // ---- 3 (start). The waves stream the workgroup's part of the list in
-    // batches of 4*U entries taken from a shared counter, so they finish
-    // together.  Each wave's first batch is loaded now, so its loads are in
-    // flight during the set computation; its repeats are masked afterwards.
-    const int r_lo = (int)(((long long)topk * split) / p.splits);
-    const int r_hi = (int)(((long long)topk * (split + 1)) / p.splits);
-    constexpr int B = 4 * U;                 // entries per batch
-    const int nbatch = (r_hi - r_lo + B - 1) / B;
+    // ---- 2. Claim position x in the hash table; true when this call made
+    // the claim (x was not there).  A slot's position never changes once
+    // claimed, so all claims of one position meet in the same slot; probes
+    // are bounded by the table size (which exceeds topk).
+    auto claim = [&](int x) {
+        int h = dec_hash(x, ts);
+        for (int probe = 0; probe < ts; ++probe) {
+            const uint32_t old = atomicCAS(&table[h], kDecEmpty, (uint32_t)x);
+            if (old == kDecEmpty) return true;
+            if (old == (uint32_t)x) return false;
+            h = h + 1 == ts ? 0 : h + 1;
+        }
+        return false;
+    };
+    // A later part of a split list first enters the positions of all earlier
+    // entries, which belong to earlier parts.
+    if (r_lo > 0) {
+        for (int e = tid; e < r_lo; e += NT) {
+            const int x = pos[e];
+            if (x >= 0) (void)claim(x);
+        }
+        __syncthreads();
+    }
+
+    // ---- 3. The waves stream the workgroup's part of the list in pairs of
+    // batches of B entries taken from a shared counter, so they finish
+    // together.  LPR lanes cover one row, so a wave loads RPW rows per
+    // instruction, and a batch is U such row groups of K and V.  Each wave
+    // holds two batches in registers with fixed roles: while one is consumed
+    // the other's loads are in flight, and a consumed batch is refilled at
+    // once from the next pair.  Batches past the end load cache row 0 (the
+    // same bytes for every lane, so one cache line) and are masked; this keeps
+    // every iteration's loads unconditional, so each wait covers exactly the
+    // batch about to be consumed.
+    // (an empty cache has no row 0 to stand in for skipped entries)
+    const int nbatch = p.num_pages > 0 ? (r_hi - r_lo + B - 1) / B : 0;
+    const int npair = (nbatch + 1) / 2;
     const int64_t row_stride = (int64_t)p.Hkv * D * EB;   // bytes between cache rows
-    const uint8_t* kbase = static_cast<const uint8_t*>(p.kc) + ((int64_t)g * D + lr * DPL) * EB;
-    const uint8_t* vbase = static_cast<const uint8_t*>(p.vc) + ((int64_t)g * D + lr * DPL) * EB;
-    // Entries r0 + 4u + lg, u < U, are one batch.  Bit u of the mask: that
-    // entry is a row to attend to (inside the part, valid and not a repeat).
-    auto okmask = [&](int r0) {
+    const uint8_t* kbase = static_cast<const uint8_t*>(p.kc) + ((int64_t)g * D + CE * lr) * EB;
+    const uint8_t* vbase = static_cast<const uint8_t*>(p.vc) + ((int64_t)g * D + CE * lr) * EB;
+    struct Batch {
+        uint32_t k[U][RW], v[U][RW];
+        uint32_t okm;        // bit u: row group u holds a row to attend to
+    };
+    // The pair's entries, one per lane: each valid entry claims its position,
+    // and an entry whose position is already claimed is skipped.  The wave's
+    // later reads of rows[] see its own writes.
+    auto claim_pair = [&](int pn) {
+        const int e = r_lo + pn * 2 * B + lane;
+        if (lane < 2 * B && pn < npair && e < r_hi) {
+            const int x = pos[e];
+            if (x >= 0 && !claim(x)) rows[e] = -1;
+        }
+    };
+    // Entry r0 + u*RPW + lg is row group u of batch bidx; an entry outside
+    // the part, invalid or repeated is skipped.
+    auto entry_row = [&](int bidx, int u) {
+        const int r = r_lo + bidx * B + u * RPW + lg;
+        const int rc = r < r_hi ? r : r_hi - 1;
+        return (bidx < nbatch && r < r_hi) ? rows[rc] : -1;
+    };
+    auto issue = [&](Batch& t, int bidx) {
         uint32_t okm = 0u;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int r = r0 + u * 4 + lg;
-            okm |= (uint32_t)(r < r_hi && rows[r] >= 0) << u;
+            const int row = entry_row(bidx, u);
+            okm |= (uint32_t)(row >= 0) << u;
+            const int64_t off = (int64_t)(row >= 0 ? row : 0) * row_stride;
+            load_chunks<NCH>(kbase + off, CE * LPR * EB, t.k[u]);
+            load_chunks<NCH>(vbase + off, CE * LPR * EB, t.v[u]);
         }
-        return okm;
+        t.okm = okm;
     };
-    // Raw cache words of a batch (bf16 pairs, or four E4M3 bytes per word).
-    auto issue = [&](uint32_t (&kw)[U][RW], uint32_t (&vw)[U][RW], int r0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int r = r0 + u * 4 + lg;
-            const int row = r < r_hi ? rows[r] : -1;
-            const int64_t cr = row >= 0 ? row : 0;     // skipped entries read row 0, ignored
-            const uint8_t* kp = kbase + cr * row_stride;
-            const uint8_t* vp = vbase + cr * row_stride;
-            if constexpr (RW == 4) {
-                const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kp);
-                const u32x4_t c = *reinterpret_cast<const u32x4_t*>(vp);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) { kw[u][x] = a[x]; vw[u][x] = c[x]; }
-            } else if constexpr (RW == 2) {
-                const u32x2_t a = *reinterpret_cast<const u32x2_t*>(kp);
-                const u32x2_t c = *reinterpret_cast<const u32x2_t*>(vp);
-#pragma unroll
-                for (int x = 0; x < 2; ++x) { kw[u][x] = a[x]; vw[u][x] = c[x]; }
-            } else {
-                kw[u][0] = *reinterpret_cast<const uint32_t*>(kp);
-                vw[u][0] = *reinterpret_cast<const uint32_t*>(vp);
-            }
-        }
-    };
-    uint32_t ka[U][RW], va[U][RW];
-    int bi = wave;
-    if (bi < nbatch) issue(ka, va, r_lo + bi * B);
-
-    // ---- 2. hash table: position -> (position, smallest list entry holding
-    // it).  A slot's position never changes once claimed, so all entries of
-    // one position meet in the same slot; probes are bounded by the table
-    // size (which exceeds topk).  Each entry remembers its slot.
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        const int x = key[k];
-        int h = -1;
-        if (x >= 0) {
-            const unsigned long long mine =
-                ((unsigned long long)(uint32_t)x << 32) | (uint32_t)(k * NT + tid);
-            h = dec_hash(x, ts);
-            for (int probe = 0; probe < ts; ++probe) {
-                const unsigned long long old = atomicCAS(&table[h], kDecEmpty, mine);
-                if (old == kDecEmpty) break;
-                if ((uint32_t)(old >> 32) == (uint32_t)x) {
-                    atomicMin(&table[h], mine);
-                    break;
-                }
-                h = h + 1 == ts ? 0 : h + 1;
-            }
-        }
-        key[k] = h;                              // now: the entry's slot, or -1
-    }
-    __syncthreads();
-
-    // ---- keep each position's first entry: a valid entry that repeats an
-    // earlier one is marked skipped (rows[e] = -1)
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        const int e = k * NT + tid;
-        if (key[k] >= 0 && (uint32_t)table[key[k]] != (uint32_t)e) rows[e] = -1;
-    }
-    __syncthreads();
-
-    // scale (log2 units) including the K dequantisation factor; V's factor
-    // scales the output
-    float c_log2 = p.scale_log2, v_scale = 1.f;
-    if constexpr (F8) {
-        if (p.k_descale != nullptr) c_log2 *= p.k_descale[unit];
-        if (p.v_descale != nullptr) v_scale = p.v_descale[unit];
-    }
-
-    uint32_t qw[GM][WPL];                    // this lane's dims of the G query rows (bf16 pairs)
-#pragma unroll
-    for (int h = 0; h < GM; ++h) {
-        if (h < G) {
-            const uint16_t* qr = p.q + ((int64_t)b * p.Hq + g * G + h) * D + lr * DPL;
-            if constexpr (WPL == 4) {
-                const u32x4_t w = *reinterpret_cast<const u32x4_t*>(qr);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) qw[h][x] = w[x];
-            } else {
-                const u32x2_t w = *reinterpret_cast<const u32x2_t*>(qr);
-#pragma unroll
-                for (int x = 0; x < 2; ++x) qw[h][x] = w[x];
-            }
-        } else {
-#pragma unroll
-            for (int x = 0; x < WPL; ++x) qw[h][x] = 0u;
-        }
-    }
 
     float m_run[GM], l_run[GM], acc[GM][DPL];
 #pragma unroll
@@ -294,7 +362,11 @@ decode_kernel(const DecodeParams p) {
         for (int x = 0; x < DPL; ++x) acc[h][x] = 0.f;
     }
 
-    auto consume = [&](const uint32_t (&kr)[U][RW], const uint32_t (&vr)[U][RW], uint32_t okm) {
+    // One batch into the row group's online softmax.  The running max moves
+    // only when a score exceeds it by more than kDecLazyMax (log2 units), so
+    // the accumulators are rarely rescaled; the probabilities stay below
+    // 2^kDecLazyMax, and the final division by the row sum is unchanged.
+    auto consume = [&](const Batch& t) {
         // bf16 pairs of the rows (E4M3 -> bf16 is exact)
         uint32_t kw[U][WPL], vw[U][WPL];
 #pragma unroll
@@ -302,17 +374,17 @@ decode_kernel(const DecodeParams p) {
 #pragma unroll
             for (int x = 0; x < RW; ++x) {
                 if constexpr (F8) {
-                    kw[u][2 * x] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[u][x], 1.f, false));
-                    kw[u][2 * x + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kr[u][x], 1.f, true));
-                    vw[u][2 * x] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vr[u][x], 1.f, false));
-                    vw[u][2 * x + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vr[u][x], 1.f, true));
+                    kw[u][2 * x] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(t.k[u][x], 1.f, false));
+                    kw[u][2 * x + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(t.k[u][x], 1.f, true));
+                    vw[u][2 * x] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(t.v[u][x], 1.f, false));
+                    vw[u][2 * x + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(t.v[u][x], 1.f, true));
                 } else {
-                    kw[u][x] = kr[u][x];
-                    vw[u][x] = vr[u][x];
+                    kw[u][x] = t.k[u][x];
+                    vw[u][x] = t.v[u][x];
                 }
             }
         }
-        // raw scores q.k of the lane group's rows, one per query head
+        // raw scores q.k of the row group's rows, one per query head
         float s[U][GM];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -321,16 +393,39 @@ decode_kernel(const DecodeParams p) {
                 float d = 0.f;
 #pragma unroll
                 for (int x = 0; x < WPL; ++x) d = dot2_bf16(qw[h][x], kw[u][x], d);
-                s[u][h] = row16_sum(d);
+                s[u][h] = row_sum<LPR>(d);
             }
         }
-        if (__builtin_amdgcn_ballot_w64(okm != (1u << U) - 1u) != 0ull) {   // skipped entries
+        if (__builtin_amdgcn_ballot_w64(t.okm != (1u << U) - 1u) != 0ull) {   // skipped entries
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (((okm >> u) & 1u) == 0u) {
+                if (((t.okm >> u) & 1u) == 0u) {
 #pragma unroll
                     for (int h = 0; h < GM; ++h) s[u][h] = -INFINITY;
                 }
+        }
+        const float c = c_log2;                  // > 0: the max commutes with the scaling
+        float cand[GM];
+        bool grow = false;
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            float mb = s[0][h];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mb = fmaxf(mb, s[u][h]);
+            cand[h] = mb * c;
+            grow |= cand[h] > m_run[h] + kDecLazyMax;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
+#pragma unroll
+            for (int h = 0; h < GM; ++h) {
+                const float m_new = fmaxf(m_run[h], cand[h]);
+                const float msub = m_new == -INFINITY ? 0.f : m_new;
+                const float alpha = fast_exp2(m_run[h] - msub);
+                m_run[h] = m_new;
+                l_run[h] *= alpha;
+#pragma unroll
+                for (int x = 0; x < DPL; ++x) acc[h][x] *= alpha;
+            }
         }
         // V of rows 2j and 2j+1 interleaved per dim: bf16 pairs for dot2
         uint32_t vlo[U / 2][WPL], vhi[U / 2][WPL];
@@ -342,19 +437,10 @@ decode_kernel(const DecodeParams p) {
                 vhi[j][x] = __builtin_amdgcn_perm(vw[2 * j + 1][x], vw[2 * j][x], 0x07060302u);
             }
         }
-        const float c = c_log2;                  // > 0: the max commutes with the scaling
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
-            float mb = s[0][h];
-#pragma unroll
-            for (int u = 1; u < U; ++u) mb = fmaxf(mb, s[u][h]);
-            const float m_new = fmaxf(m_run[h], mb * c);
-            const float msub = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run[h] - msub);
-            m_run[h] = m_new;
+            const float msub = m_run[h] == -INFINITY ? 0.f : m_run[h];
             float ls = 0.f;
-#pragma unroll
-            for (int x = 0; x < DPL; ++x) acc[h][x] *= alpha;
 #pragma unroll
             for (int j = 0; j < U / 2; ++j) {
                 const float p0 = fast_exp2(fmaf(s[2 * j][h], c, -msub));
@@ -367,7 +453,7 @@ decode_kernel(const DecodeParams p) {
                     acc[h][2 * x + 1] = dot2_bf16(pp, vhi[j][x], acc[h][2 * x + 1]);
                 }
             }
-            l_run[h] = l_run[h] * alpha + ls;
+            l_run[h] += ls;
         }
     };
     auto grab = [&]() {
@@ -375,51 +461,37 @@ decode_kernel(const DecodeParams p) {
         if (lane == 0) t = __hip_atomic_fetch_add(next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         return __builtin_amdgcn_readfirstlane(t);
     };
-    // two batches in flight per wave: the next one's loads are issued before
-    // the current one is consumed
-    uint32_t kb[U][RW], vb[U][RW];
-    int bn = bi < nbatch ? grab() : nbatch;
-    if (bn < nbatch) issue(kb, vb, r_lo + bn * B);
-    while (bi < nbatch) {
-        {
-            const uint32_t okm = okmask(r_lo + bi * B);
-            const int bn2 = bn < nbatch ? grab() : nbatch;
-            consume(ka, va, okm);
-            if (bn2 < nbatch) issue(ka, va, r_lo + bn2 * B);
-            bi = bn;
-            bn = bn2;
-        }
-        if (bi >= nbatch) break;
-        {
-            const uint32_t okm = okmask(r_lo + bi * B);
-            const int bn2 = bn < nbatch ? grab() : nbatch;
-            consume(kb, vb, okm);
-            if (bn2 < nbatch) issue(kb, vb, r_lo + bn2 * B);
-            bi = bn;
-            bn = bn2;
+    if (nbatch > 0) {
+        Batch ta, tb;
+        claim_pair(wave);
+        issue(ta, 2 * wave);
+        issue(tb, 2 * wave + 1);
+        int pc = wave;
+        while (pc < npair) {
+            const int pn = grab();
+            claim_pair(pn);
+            consume(ta);
+            issue(ta, 2 * pn);
+            consume(tb);
+            issue(tb, 2 * pn + 1);
+            pc = pn;
         }
     }
 
-    // ---- 4. merge the wave's four lane groups, then the workgroup's waves.
-    // Region 0 (the hash table) is free: its last reads precede the barrier
-    // that ended step 2's compaction.
+    // ---- 4. merge the wave's row groups, then the workgroup's waves.
+    // Region 0 (the hash table) is reused: every claim precedes the barrier.
+    __syncthreads();
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
-        float m = m_run[h];
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
+        const float m = lanes_combine<LPR, true>(m_run[h]);
         const float msub = m == -INFINITY ? 0.f : m;
         const float sc = fast_exp2(m_run[h] - msub);
-        float l = l_run[h] * sc;
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        const float l = lanes_combine<LPR, false>(l_run[h] * sc);
         float* rec = mrg + (wave * GM + h) * L::kRec;
 #pragma unroll
         for (int x = 0; x < DPL; ++x) {
-            float a = acc[h][x] * sc;
-            a += __shfl_xor(a, 16);
-            a += __shfl_xor(a, 32);
-            if (lg == 0) rec[lr * DPL + x] = a;
+            const float a = lanes_combine<LPR, false>(acc[h][x] * sc);
+            if (lg == 0) rec[(x / CE) * CE * LPR + CE * lr + x % CE] = a;
         }
         if (lane == 0) {
             rec[D] = m;
