@@ -10,16 +10,18 @@ One step = one pass of the hot path over resident synthetic inputs:
     of 32768 tokens in pages of 256, topk 2048 (last 128 + uniform rest),
     alternating between two cache copies so a call does not find its rows
     still on chip from the previous one.
-``value`` is that prefill's effective TFLOP/s over the K timed calls (wall
-clock; 4*d*64*G flops per distinct selected (token, kv head, block) triple).
-The other prefill workloads (B=2 x 8192 tokens at G=4; varlen 65536+32768 at
-G=1) are timed as legs with their own roofline objects, and so are the FP8
-decode, the sliding window, the backward and the block selection.  Each phase
-is timed over exactly K calls bracketed by device synchronisation, after W
-warm-up steps; per-launch durations come from HIP events recorded on the
-stream the kernels run on (mean and median reported).  The fp64 CPU oracle is
-timed on a bounded token sample of the headline prefill on the host cores,
-plus the small prefill single-threaded and the whole decode workload.
+``value`` is that prefill's effective TFLOP/s over the K timed calls
+(4*d*64*G flops per distinct selected (token, kv head, block) triple).  The
+other prefill workloads (B=2 x 8192 tokens at G=4; varlen 65536+32768 at G=1)
+are timed as legs with their own roofline objects, and so are the FP8 decode,
+the sliding window, the backward and the block selection.  Each phase is timed
+over exactly K calls issued back to back between one pair of HIP events on the
+stream the kernels run on, bracketed by device synchronisation, after W
+warm-up steps: the mean per call is that region divided by K (the host clock
+around the region is reported too).  A second pass of K calls, each between
+its own events, supplies the per-call median.  The fp64 CPU oracle is timed on
+a bounded token sample of the headline prefill on the host cores, plus the
+small prefill single-threaded and the whole decode workload.
 """
 
 import argparse
@@ -98,6 +100,15 @@ class PrefillLeg:
         self.pairs = inputs.count_valid_pairs(d["blk_idx"].numpy(), d["cu_seqlens_q"].numpy(),
                                               d["cu_seqlens_k"].numpy(), sp.block_size)
         self.flops = 4.0 * sp.head_dim * sp.block_size * self.G * self.pairs
+        # the automatic schedule: block-centric (inverted index, partials,
+        # merge) for GQA groups of at most 2 query heads, else query-centric
+        if self.G <= 2:
+            self.kernel = (f"fwd_bc_main_kernel<{sp.head_dim}> (whole call: prep, inverted index, "
+                           f"main and merge kernels)")
+            self.src = "sel_attn_fwd_bc.hip"
+        else:
+            self.kernel = f"sel_attn_fwd_kernel<{sp.head_dim}, false>"
+            self.src = "sel_attn_fwd.hip"
         self.g = {k: d[k].to(dev) for k in ("q", "k", "v", "blk_idx", "cu_seqlens_q",
                                             "cu_seqlens_k")}
         self.out = torch.empty_like(self.g["q"])
@@ -124,29 +135,50 @@ class PrefillLeg:
                 "causal": True, "selected_pairs": self.pairs, "flops_per_call": self.flops}
 
 
+class Timing:
+    """One leg's timing.  `mean` (ms per call) is the timed region: K calls
+    issued back to back between one pair of HIP events on `stream`, with a
+    device synchronisation on both sides; `wall` is the host clock around the
+    same region.  `median` comes from a second pass of K calls, each between
+    its own pair of events (event records add a little time per call, so that
+    pass only supplies the distribution)."""
+
+    def __init__(self, mean, wall, per_call):
+        self.mean, self.wall, self.per_call = mean, wall, per_call
+
+    @property
+    def median(self):
+        return float(np.median(self.per_call))
+
+
 def timed(fn, K, stream):
-    """K calls of fn(i) between device synchronisations; returns (per-call ms
-    from HIP events on `stream`, wall seconds)."""
-    import numpy as np
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+    """K calls of fn(i) timed as one region, then K calls timed one by one."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    a.record(stream)
+    for i in range(K):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean = a.elapsed_time(b) / K
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
     for i in range(K):
         evs[i][0].record(stream)
         fn(i)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return np.array([a.elapsed_time(b) for a, b in evs]), wall
+    return Timing(mean, wall, np.array([x.elapsed_time(y) for x, y in evs]))
 
 
-def mfma_roofline(flops, ms, traffic, kernel, extra=None):
-    ach = flops / (ms.mean() * 1e-3) / 1e12
+def mfma_roofline(flops, t, traffic, kernel, extra=None):
+    ach = flops / (t.mean * 1e-3) / 1e12
     r = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
          "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": kernel,
-         "flops_per_launch": flops, "avg_launch_ms": round(float(ms.mean()), 4),
-         "median_launch_ms": round(float(np.median(ms)), 4)}
+         "flops_per_launch": flops, "avg_launch_ms": round(t.mean, 4),
+         "median_launch_ms": round(t.median, 4)}
     if extra:
         r.update(extra)
     return r
@@ -157,7 +189,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="approximate CPU time budget of the oracle's sampled prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=("full", "prefill", "decode", "decode_fp8", "window",
@@ -202,9 +234,11 @@ def main():
 
     if args.mode == "prefill":
         leg = PrefillLeg(args.workload, dev, fsa, inputs)
-        ms, _ = timed(leg, W + K, stream)
-        log(f"prefill {args.workload}: {W + K} launches, median {np.median(ms[W:]):.3f} ms, "
-            f"{leg.flops / (np.median(ms[W:]) * 1e-3) / 1e12:.1f} TFLOP/s")
+        for i in range(W):
+            leg(i)
+        t = timed(leg, K, stream)
+        log(f"prefill {args.workload}: {W} + 2 x {K} launches, mean {t.mean:.3f} ms, "
+            f"{leg.flops / (t.mean * 1e-3) / 1e12:.1f} TFLOP/s")
         return
 
     # ---------------- inputs (generated on the host, then resident in HBM)
@@ -330,15 +364,15 @@ def main():
         log(f"timing {K} prefill calls of {name}")
         res[name] = timed(leg, K, stream)
     log(f"timing {K} decode calls")
-    d_ms, t_decode = timed(decode, K, stream)
+    d_t = timed(decode, K, stream)
     log(f"timing {K} FP8 decode calls")
-    f_ms, t_f8 = timed(decode_fp8, K, stream)
+    f_t = timed(decode_fp8, K, stream)
     log(f"timing {K} sliding-window calls")
-    w_ms, _ = timed(window, K, stream)
+    w_t = timed(window, K, stream)
     log(f"timing {K} backward calls")
-    b_ms, _ = timed(backward, K, stream)
+    b_t = timed(backward, K, stream)
     log(f"timing {K} block-selection calls")
-    s_ms, _ = timed(select, K, stream)
+    s_t = timed(select, K, stream)
     timeouts = fsa.fsa_wait_timeouts(reset=True)
     if timeouts:
         log(f"WARNING: {timeouts} ring waits gave up during the timed calls")
@@ -346,39 +380,39 @@ def main():
     kern_fwd = "sel_attn_fwd.hip"
     prefill_objs = {}
     for name, leg in legs.items():
-        ms, wall = res[name]
-        r = mfma_roofline(leg.flops, ms, measured_traffic(kern_fwd, name),
-                          "sel_attn_fwd_kernel<128, false>")
-        log(f"prefill {name}: mean {ms.mean():.3f} ms  median {np.median(ms):.3f} ms  "
-            f"{r['achieved']:.1f} TFLOP/s (events), {leg.flops * K / wall / 1e12:.1f} (wall)")
-        prefill_objs[name] = {"value": round(leg.flops * K / wall / 1e12, 2), "unit": "TFLOP/s",
-                              "ms_per_call": round(float(ms.mean()), 4),
-                              "median_ms": round(float(np.median(ms)), 4),
+        t = res[name]
+        r = mfma_roofline(leg.flops, t, measured_traffic(leg.src, name), leg.kernel)
+        log(f"prefill {name}: mean {t.mean:.3f} ms  median {t.median:.3f} ms  "
+            f"{r['achieved']:.1f} TFLOP/s (events), {leg.flops * K / t.wall / 1e12:.1f} (wall)")
+        prefill_objs[name] = {"value": round(leg.flops / (t.mean * 1e-3) / 1e12, 2),
+                              "unit": "TFLOP/s", "ms_per_call": round(t.mean, 4),
+                              "median_ms": round(t.median, 4),
+                              "wall_tflops": round(leg.flops * K / t.wall / 1e12, 2),
                               "config": leg.config(), "roofline": r}
     head = legs[HEADLINE]
-    t_head = res[HEADLINE][1]
+    t_head = res[HEADLINE]
 
     dec_src = "topk_decode.hip"
-    d_gbs = d_bytes / (d_ms.mean() * 1e-3) / 1e9
-    log(f"decode : mean {d_ms.mean() * 1e3:.1f} us  median {np.median(d_ms) * 1e3:.1f} us  "
-        f"{d_gbs:.0f} GB/s (events), {d_bytes * K / t_decode / 1e9:.0f} (wall)")
+    d_gbs = d_bytes / (d_t.mean * 1e-3) / 1e9
+    log(f"decode : mean {d_t.mean * 1e3:.1f} us  median {d_t.median * 1e3:.1f} us  "
+        f"{d_gbs:.0f} GB/s (events), {d_bytes * K / d_t.wall / 1e9:.0f} (wall)")
     decode_obj = {
         "value": round(d_gbs, 1), "unit": "GB/s", "workload": DECODE,
-        "us_per_call": round(float(d_ms.mean()) * 1e3, 2),
-        "median_us": round(float(np.median(d_ms)) * 1e3, 2),
-        "gbs_wall": round(d_bytes * K / t_decode / 1e9, 1),
+        "us_per_call": round(d_t.mean * 1e3, 2),
+        "median_us": round(d_t.median * 1e3, 2),
+        "gbs_wall": round(d_bytes * K / d_t.wall / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(d_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(d_gbs / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(dec_src, DECODE), "bytes_per_call": d_bytes,
                      "scope": "whole call: the fused decode kernel (plus the LSE merge when split)"},
     }
-    f_gbs = f8_bytes / (f_ms.mean() * 1e-3) / 1e9
-    log(f"decode8: mean {f_ms.mean() * 1e3:.1f} us  {f_gbs:.0f} GB/s (events)")
+    f_gbs = f8_bytes / (f_t.mean * 1e-3) / 1e9
+    log(f"decode8: mean {f_t.mean * 1e3:.1f} us  {f_gbs:.0f} GB/s (events)")
     decode_fp8_obj = {
         "value": round(f_gbs, 1), "unit": "GB/s", "workload": DECODE + "_fp8_e4m3",
-        "us_per_call": round(float(f_ms.mean()) * 1e3, 2),
-        "median_us": round(float(np.median(f_ms)) * 1e3, 2),
-        "gbs_wall": round(f8_bytes * K / t_f8 / 1e9, 1),
+        "us_per_call": round(f_t.mean * 1e3, 2),
+        "median_us": round(f_t.median * 1e3, 2),
+        "gbs_wall": round(f8_bytes * K / f_t.wall / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(f_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(f_gbs / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(dec_src, DECODE + "_fp8"),
@@ -386,22 +420,22 @@ def main():
                      "scope": "whole call; K/V rows 1 byte per element"},
     }
 
-    def leg_obj(flops, ms, workload, src, scope=None):
-        t = flops / (ms.mean() * 1e-3) / 1e12
+    def leg_obj(flops, tm, workload, src, scope=None):
+        t = flops / (tm.mean * 1e-3) / 1e12
         r = {"bound": "mfma", "achieved": round(t, 2), "peak": PEAK_BF16_TFLOPS,
              "unit": "TFLOP/s", "frac": round(t / PEAK_BF16_TFLOPS, 4),
              "traffic": measured_traffic(src, workload), "flops_per_call": flops}
         if scope:
             r["scope"] = scope
         return {"value": round(t, 2), "unit": "TFLOP/s", "workload": workload,
-                "ms_per_call": round(float(ms.mean()), 4),
-                "median_ms": round(float(np.median(ms)), 4), "roofline": r}
+                "ms_per_call": round(tm.mean, 4),
+                "median_ms": round(tm.median, 4), "roofline": r}
 
-    window_obj = leg_obj(w_flops, w_ms, WINDOW_WL, kern_fwd)
+    window_obj = leg_obj(w_flops, w_t, WINDOW_WL, kern_fwd)
     b_flops = 2.5 * b2.flops                  # five products per selected block against two
-    backward_obj = leg_obj(b_flops, b_ms, PREFILL_B2 + "_backward", "sel_attn_bwd.hip",
+    backward_obj = leg_obj(b_flops, b_t, PREFILL_B2 + "_backward", "sel_attn_bwd.hip",
                            "whole call: D prep, block index, dK/dV and dQ kernels")
-    select_obj = leg_obj(s_flops, s_ms, SELECT_WL, "block_select.hip",
+    select_obj = leg_obj(s_flops, s_t, SELECT_WL, "block_select.hip",
                          "whole call: key-window means + compressed attention, block importance "
                          "and top-k (flops: one q.c product per row and visible window)")
     for nm, o in (("window", window_obj), ("backward", backward_obj), ("select", select_obj)):
@@ -409,12 +443,12 @@ def main():
 
     result = {
         "metric": METRIC,
-        "value": round(head.flops * K / t_head / 1e12, 2),
+        "value": round(head.flops / (t_head.mean * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round((t_head + t_decode) * 1e3 / K, 4),
+        "ms_per_step": round(t_head.mean + d_t.mean, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

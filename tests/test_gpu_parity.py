@@ -669,11 +669,19 @@ def test_bwd_medium_gqa_workload():
 
 def test_bwd_full_size_bench_workload():
     """The backward at B=2, S=8192, Hq=32, Hkv=8, d=128, topk 16, launched as the
-    benchmark launches it.  The oracle cannot run the whole problem in a test, so:
+    benchmark launches it, compared element by element where the oracle can
+    compute the exact answer from a part of the problem:
 
     * dQ of a row depends on that row alone, and under the causal mask with
-      S_q = S_k the first 2048 tokens of a sequence form a problem of their own;
-      the oracle runs on those prefixes and every dQ element of them is compared.
+      S_q = S_k the first n tokens of a sequence form a problem of their own:
+      the oracle runs on those prefixes and every dQ element of them is
+      compared.
+    * Key j is visible only to queries i >= j, so the keys of the last n
+      positions of a sequence receive gradient from the last n queries only.
+      The oracle runs those queries against the whole key range (S_k > S_q,
+      the causal diagonal aligned at the end, so every query sees exactly the
+      keys it sees in the full problem): their dQ rows and the dK, dV rows of
+      the last n keys are exact there and every element is compared.
     * Every softmax row has sum_j dS_ij = 0, so per (sequence, kv head) the dK
       rows sum to zero and the dV rows sum to the dO rows of the group's heads
       (every row sees key 0 here).  Both bounds allow the bf16 rounding of each
@@ -688,10 +696,11 @@ def test_bwd_full_size_bench_workload():
     for nm, a in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert np.isfinite(a).all(), nm
     cu = dd["cu_seqlens_q"].numpy().astype(np.int64)
+    nseq = cu.size - 1
     Hq, Hkv = dq.shape[1], dk.shape[1]
     G = Hq // Hkv
     dof = do.float().numpy().astype(np.float64)
-    for b in range(cu.size - 1):
+    for b in range(nseq):
         lo, hi = int(cu[b]), int(cu[b + 1])
         for g in range(Hkv):
             k64 = dk[lo:hi, g].astype(np.float64)
@@ -701,17 +710,31 @@ def test_bwd_full_size_bench_workload():
             tol_v = 2.0 ** -9 * np.abs(v64).sum(axis=0) + 1e-3
             assert (np.abs(k64.sum(axis=0)) <= tol_k).all(), ("sum dK", b, g)
             assert (np.abs(v64.sum(axis=0) - want_v) <= tol_v).all(), ("sum dV", b, g)
+
+    def close(a, r, what):
+        e = np.abs(a - r)
+        assert (e / (1.0 + np.abs(r))).max() <= G_REL, what
+        assert e.mean() <= G_MEAN * max(np.abs(r).mean(), 1e-3), what
+
     n = 2048
+    dot = torch.from_numpy
     rows = np.concatenate([np.arange(int(c), int(c) + n) for c in cu[:-1]])
-    sub = {x: dd[x][torch.from_numpy(rows)] for x in ("q", "k", "v", "blk_idx")}
-    cu_sub = torch.arange(0, (cu.size - 1) * n + 1, n, dtype=torch.int32)
+    sub = {x: dd[x][dot(rows)] for x in ("q", "k", "v", "blk_idx")}
+    cu_sub = torch.arange(0, nseq * n + 1, n, dtype=torch.int32)
     print(f"[gpu] backward full size: oracle on the first {n} tokens of each sequence", flush=True)
-    rq, _, _ = oracle.selected_attn_bwd(sub["q"], sub["k"], sub["v"], do[torch.from_numpy(rows)],
+    rq, _, _ = oracle.selected_attn_bwd(sub["q"], sub["k"], sub["v"], do[dot(rows)],
                                         sub["blk_idx"], cu_sub, cu_sub, 64)
-    a = dq[rows]
-    e = np.abs(a - rq)
-    assert (e / (1.0 + np.abs(rq))).max() <= G_REL
-    assert e.mean() <= G_MEAN * max(np.abs(rq).mean(), 1e-3)
+    close(dq[rows], rq, "dQ of the prefixes")
+
+    last = np.concatenate([np.arange(int(c) - n, int(c)) for c in cu[1:]])
+    cu_q_sub = torch.arange(0, nseq * n + 1, n, dtype=torch.int32)
+    print(f"[gpu] backward full size: oracle on the last {n} queries of each sequence", flush=True)
+    rq, rk, rv = oracle.selected_attn_bwd(dd["q"][dot(last)], dd["k"], dd["v"], do[dot(last)],
+                                          dd["blk_idx"][dot(last)], cu_q_sub,
+                                          dd["cu_seqlens_k"], 64)
+    close(dq[last], rq, "dQ of the last queries")
+    close(dk[last], rk[last], "dK of the last keys")
+    close(dv[last], rv[last], "dV of the last keys")
 
 
 # ------------------------------------------------------------------ block-index producer
