@@ -126,7 +126,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(const SelBwdParams p) {
         p.dvec[(int64_t)h * p.total_q + t] = acc;
     }
     // block counters and fill cursors (the split-block accumulators are
-    // cleared by the scan, once the counts say which blocks split)
+    // cleared by the fill pass, once the counts say which blocks split)
     const int64_t nc = (int64_t)p.batch * p.Hkv * (p.nb_max + 1);
     const int64_t nu = (int64_t)p.batch * p.Hkv * p.nb_max;
     for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < nc; x += (int64_t)gridDim.x * 256) {
@@ -148,7 +148,7 @@ constexpr int kIdxChunk = 256;
 constexpr int kIdxWin = 8192;
 constexpr int kIdxRegs = 16;
 
-template <bool FILL>
+template <bool FILL, int D>
 __global__ void __launch_bounds__(kIdxChunk) bwd_index_kernel(const SelBwdParams p) {
     __shared__ int hist[kIdxWin];
     const int nchunk = p.nchunk_q;
@@ -156,6 +156,27 @@ __global__ void __launch_bounds__(kIdxChunk) bwd_index_kernel(const SelBwdParams
     const int unit = blockIdx.x / nchunk;               // b * Hkv + g
     const int g = unit % p.Hkv, b = unit / p.Hkv;
     const SeqBounds sb = bounds(p, b);
+    if constexpr (FILL) {
+        // Clear the fp32 accumulators of the blocks that the dK/dV pass
+        // splits over several workgroups (it adds their partials there); the
+        // other blocks are written directly and need none.  The counts are
+        // final (the scan ran); block blk of the unit is this workgroup's when
+        // blk = chunk (mod nchunk).
+        const int32_t* cs = p.counts + (int64_t)unit * (p.nb_max + 1);
+        int nb = (sb.Sk + kBlockKeys - 1) / kBlockKeys;
+        nb = nb < p.nb_max ? nb : p.nb_max;
+        const int tpc = kBwdRows / p.G;
+        for (int blk = chunk; blk < nb; blk += nchunk) {
+            const int nsteps = (cs[blk + 1] - cs[blk] + tpc - 1) / tpc;
+            if (nsteps <= p.part_steps) continue;
+            const int nkeys = sb.Sk - blk * kBlockKeys < kBlockKeys ? sb.Sk - blk * kBlockKeys : kBlockKeys;
+            for (int x = threadIdx.x; x < nkeys * (D / 2); x += kIdxChunk) {
+                const int key = x / (D / 2), c = x - key * (D / 2);   // 16-byte chunks of the dK and dV sums
+                const int64_t krow = (sb.k0 + blk * kBlockKeys + key) * p.Hkv + g;
+                reinterpret_cast<f32x4_t*>(p.kv_acc + krow * 2 * D)[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    }
     const int i0 = chunk * kIdxChunk;
     if (i0 >= sb.Sq) return;
     const int i = i0 + (int)threadIdx.x;                // this thread's token (in the sequence)
@@ -237,7 +258,6 @@ __global__ void __launch_bounds__(kIdxChunk) bwd_index_kernel(const SelBwdParams
 }
 
 // exclusive scan of the counts of one (sequence, kv head): counts -> offsets
-template <int D>
 __global__ void __launch_bounds__(256) bwd_scan_kernel(const SelBwdParams p) {
     __shared__ int wsum[4];
     const int unit = blockIdx.x;
@@ -265,24 +285,6 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(const SelBwdParams p) {
         if (x < n) c[x] = carry + wb + incl - v;
         carry += tot;
         __syncthreads();
-    }
-    // Clear the fp32 accumulators of the blocks that the dK/dV pass splits
-    // over several workgroups (it adds their partials there); the other
-    // blocks are written directly and need none.  The counts just written
-    // are visible to the workgroup after the barrier above.
-    const int b = unit / p.Hkv, g = unit % p.Hkv;
-    const SeqBounds sb = bounds(p, b);
-    const int nblk = (sb.Sk + kBlockKeys - 1) / kBlockKeys;
-    const int tpc = kBwdRows / p.G;
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int nsteps = (c[blk + 1] - c[blk] + tpc - 1) / tpc;
-        if (nsteps <= p.part_steps) continue;
-        const int nkeys = sb.Sk - blk * kBlockKeys < kBlockKeys ? sb.Sk - blk * kBlockKeys : kBlockKeys;
-        for (int x = threadIdx.x; x < nkeys * (D / 2); x += 256) {
-            const int key = x / (D / 2), ch = x - key * (D / 2);   // 16-byte chunks of the dK and dV sums
-            const int64_t krow = (sb.k0 + blk * kBlockKeys + key) * p.Hkv + g;
-            reinterpret_cast<f32x4_t*>(p.kv_acc + krow * 2 * D)[ch] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
     }
 }
 
@@ -958,9 +960,9 @@ static hipError_t launch_bwd_d(const SelBwdParams& p, hipStream_t stream) {
     const unsigned gp = (unsigned)((nrows + 15) / 16 > 0 ? (nrows + 15) / 16 : 1);
     hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(gp), dim3(256), 0, stream, p);
     const unsigned gl = (unsigned)(p.batch * p.Hkv * p.nchunk_q);
-    hipLaunchKernelGGL(bwd_index_kernel<false>, dim3(gl), dim3(kIdxChunk), 0, stream, p);
-    hipLaunchKernelGGL(bwd_scan_kernel<D>, dim3(p.batch * p.Hkv), dim3(256), 0, stream, p);
-    hipLaunchKernelGGL(bwd_index_kernel<true>, dim3(gl), dim3(kIdxChunk), 0, stream, p);
+    hipLaunchKernelGGL((bwd_index_kernel<false, D>), dim3(gl), dim3(kIdxChunk), 0, stream, p);
+    hipLaunchKernelGGL(bwd_scan_kernel, dim3(p.batch * p.Hkv), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((bwd_index_kernel<true, D>), dim3(gl), dim3(kIdxChunk), 0, stream, p);
     hipLaunchKernelGGL(bwd_dkv_kernel<D>, dim3((unsigned)(p.batch * p.Hkv * p.nb_max * p.nparts)),
                        dim3(kBwdKvThreads), 0, stream, p);
     hipLaunchKernelGGL(bwd_dkv_finish_kernel<D>, dim3((unsigned)(p.batch * p.Hkv * p.nb_max)),
