@@ -79,9 +79,10 @@ int32_t fsa_abi_version(void);
  * Diagnostics of the bounded waits inside the prefill, window and backward
  * kernels.  Their producer and consumer waves hand K/V blocks over through
  * LDS flags; every wait polls a bounded number of times, so an error in that
- * hand-over can never hang the GPU.  A wave whose wait runs out gives up for
- * good (its workgroup stops waiting and its results are wrong) and adds one
- * to a counter in device memory of the current device.
+ * hand-over can never hang the GPU.  A wave whose wait runs out gives up:
+ * it goes on with whatever LDS holds (its results are then wrong; every
+ * access stays in bounds), adds one to a counter in device memory of the
+ * current device, and makes each of its later waits a single poll.
  *
  * fsa_wait_timeouts: *count = that counter (0 after correct runs); a nonzero
  *   reset clears it.  Synchronous (a device-to-host copy on the null stream);

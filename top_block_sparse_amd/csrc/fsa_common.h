@@ -86,58 +86,40 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Bounded waits of the LDS ring protocols.  Every wait polls at most
-// `limit` times (a consistent protocol never comes close).  A wave whose wait
-// runs out gives up for good: it raises the workgroup's abort word, skips
-// every later wait (its `gave_up` flag is wave-uniform and sticky) and adds
-// one to the kernel file's device counter of timeouts, which the host reads
-// back (fsa_wait_timeouts).  Other waves see the abort word within a few
-// hundred polls and give up too without counting, so a protocol error costs
-// one bounded stall per workgroup and a non-zero count, never a hang.
-// `abort_word` and the counter are written only from lane 0 (vector LDS and
-// global atomics).
-__device__ __forceinline__ void note_wait_timeout(uint32_t* abort_word, unsigned int* counter,
-                                                  int lane) {
-    if (lane == 0) {
-        __hip_atomic_store(abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+// `limit` times (a consistent protocol never comes close), so a protocol
+// error can only give wrong values, never a hung GPU.  A wait that runs out
+// returns false, adds one to the kernel file's device counter of timeouts
+// (lane 0, a vector global atomic; the host reads it back with
+// fsa_wait_timeouts) and lowers the wave's own limit to one poll, so its
+// later waits cannot each stall for the full limit.  The wave-uniform limit
+// is the loops' only extra state: an abort word checked while polling and a
+// sticky per-lane flag cost the ring kernels 6-8 % (the extra live state
+// spilled scalar registers into their loops).
+__device__ __forceinline__ void note_wait_timeout(unsigned int* counter, int& limit, int lane) {
+    if (lane == 0) __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    limit = 1;
 }
 
 // Wait until two adjacent ready words (one per producer) both reach `target`.
-// Returns false when the wave gave up (or had given up before).
 __device__ __forceinline__ bool wait_ready2(const uint32_t* ready, uint32_t target,
-                                            uint32_t* abort_word, unsigned int* counter,
-                                            int limit, bool& gave_up, int lane) {
-    if (gave_up) return false;
+                                            unsigned int* counter, int& limit, int lane) {
     for (int sp = 0; sp < limit; ++sp) {
         const u32x2_t r = lds_load2_sync(ready);
         if (r[0] >= target && r[1] >= target) return true;
-        if ((sp & 255) == 255 && lds_load_sync(abort_word) != 0u) {
-            gave_up = true;
-            return false;
-        }
         __builtin_amdgcn_s_sleep(4);
     }
-    gave_up = true;
-    note_wait_timeout(abort_word, counter, lane);
+    note_wait_timeout(counter, limit, lane);
     return false;
 }
 
 // Wait until a done counter reaches `target` (producers: the slot is free).
 __device__ __forceinline__ bool wait_done(const uint32_t* done, uint32_t target,
-                                          uint32_t* abort_word, unsigned int* counter, int limit,
-                                          bool& gave_up, int lane) {
-    if (gave_up) return false;
+                                          unsigned int* counter, int& limit, int lane) {
     for (int sp = 0; sp < limit; ++sp) {
         if (lds_load_sync(done) >= target) return true;
-        if ((sp & 1023) == 1023 && lds_load_sync(abort_word) != 0u) {
-            gave_up = true;
-            return false;
-        }
         __builtin_amdgcn_s_sleep(1);
     }
-    gave_up = true;
-    note_wait_timeout(abort_word, counter, lane);
+    note_wait_timeout(counter, limit, lane);
     return false;
 }
 
