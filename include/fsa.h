@@ -82,7 +82,8 @@ int32_t fsa_abi_version(void);
  * hand-over can never hang the GPU.  A wave whose wait runs out gives up:
  * it goes on with whatever LDS holds (its results are then wrong; every
  * access stays in bounds), adds one to a counter in device memory of the
- * current device, and makes each of its later waits a single poll.
+ * current device, makes each of its later waits a single poll and tells the
+ * other waves of its workgroup, which stop waiting within ~1024 polls.
  *
  * fsa_wait_timeouts: *count = that counter (0 after correct runs); a nonzero
  *   reset clears it.  Synchronous (a device-to-host copy on the null stream);

@@ -90,36 +90,52 @@ __device__ __forceinline__ void wait_vmcnt() {
 // error can only give wrong values, never a hung GPU.  A wait that runs out
 // returns false, adds one to the kernel file's device counter of timeouts
 // (lane 0, a vector global atomic; the host reads it back with
-// fsa_wait_timeouts) and lowers the wave's own limit to one poll, so its
-// later waits cannot each stall for the full limit.  The wave-uniform limit
-// is the loops' only extra state: an abort word checked while polling and a
-// sticky per-lane flag cost the ring kernels 6-8 % (the extra live state
-// spilled scalar registers into their loops).
-__device__ __forceinline__ void note_wait_timeout(unsigned int* counter, int& limit, int lane) {
-    if (lane == 0) __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// fsa_wait_timeouts), raises the workgroup's abort word and lowers the
+// wave's own limit to one poll.  A wave still waiting looks at the abort
+// word every 1024 polls and gives up too (without counting), so one
+// protocol error costs a workgroup about one full wait, not one per block.
+// The wave-uniform limit is the loops' only extra live state: a sticky
+// per-lane flag and an abort check every 256 polls cost the ring kernels
+// 6-8 % (the extra state spilled scalar registers into their loops).
+__device__ __forceinline__ void note_wait_timeout(unsigned int* counter, uint32_t* abort_word,
+                                                  int& limit, int lane) {
+    if (lane == 0) {
+        __hip_atomic_store(abort_word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     limit = 1;
 }
 
 // Wait until two adjacent ready words (one per producer) both reach `target`.
 __device__ __forceinline__ bool wait_ready2(const uint32_t* ready, uint32_t target,
-                                            unsigned int* counter, int& limit, int lane) {
+                                            unsigned int* counter, uint32_t* abort_word,
+                                            int& limit, int lane) {
     for (int sp = 0; sp < limit; ++sp) {
         const u32x2_t r = lds_load2_sync(ready);
         if (r[0] >= target && r[1] >= target) return true;
+        if ((sp & 1023) == 1023 && lds_load_sync(abort_word) != 0u) {
+            limit = 1;
+            return false;
+        }
         __builtin_amdgcn_s_sleep(4);
     }
-    note_wait_timeout(counter, limit, lane);
+    note_wait_timeout(counter, abort_word, limit, lane);
     return false;
 }
 
 // Wait until a done counter reaches `target` (producers: the slot is free).
 __device__ __forceinline__ bool wait_done(const uint32_t* done, uint32_t target,
-                                          unsigned int* counter, int& limit, int lane) {
+                                          unsigned int* counter, uint32_t* abort_word, int& limit,
+                                          int lane) {
     for (int sp = 0; sp < limit; ++sp) {
         if (lds_load_sync(done) >= target) return true;
+        if ((sp & 1023) == 1023 && lds_load_sync(abort_word) != 0u) {
+            limit = 1;
+            return false;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
-    note_wait_timeout(counter, limit, lane);
+    note_wait_timeout(counter, abort_word, limit, lane);
     return false;
 }
 

@@ -598,7 +598,7 @@ struct DqLds {
     __host__ __device__ static int umask(int ring) { return masks(ring) + kBwdWin * 8; }  // u64 [kBwdWin]
     __host__ __device__ static int ulist(int ring) { return umask(ring) + kBwdWin * 8; }  // i32 [kBwdWin]
     __host__ __device__ static int ncnt(int ring) { return ulist(ring) + kBwdWin * 4; }   // i32 [kBwdWin]
-    __host__ __device__ static int count(int ring) { return ncnt(ring) + kBwdWin * 4; }   // i32
+    __host__ __device__ static int count(int ring) { return ncnt(ring) + kBwdWin * 4; }   // i32, then the abort word
     __host__ __device__ static int ready(int ring) { return count(ring) + 16; }           // u32 [4][producers]
     __host__ __device__ static int done(int ring) { return ready(ring) + 4 * kBwdDqProducers * 4; }  // u32 [4]
     __host__ __device__ static int ent(int ring) { return done(ring) + 16; }              // i32 [T * topk]
@@ -621,6 +621,7 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
     int* s_ulist = reinterpret_cast<int*>(smem + L::ulist(ring));
     int* s_ncnt = reinterpret_cast<int*>(smem + L::ncnt(ring));
     int* s_count = reinterpret_cast<int*>(smem + L::count(ring));
+    uint32_t* s_abort = reinterpret_cast<uint32_t*>(smem + L::count(ring) + 4);
     uint32_t* s_ready = reinterpret_cast<uint32_t*>(smem + L::ready(ring));
     uint32_t* s_done = reinterpret_cast<uint32_t*>(smem + L::done(ring));
     int* s_ent = reinterpret_cast<int*>(smem + L::ent(ring));
@@ -629,6 +630,7 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
     const int lr = lane & 15, lg = lane >> 4;
     if (tid < 4 * (kBwdDqProducers + 1)) s_ready[tid] = 0u;   // s_ready and s_done
     int poll_limit = p.spin_limit;              // this wave's bound on a ring wait (drops after a give-up)
+    if (tid == 0) s_abort[0] = 0u;             // raised by a wave whose wait gave up
 
     int w = xcd_remap(blockIdx.x, (int)gridDim.x);
     const int j = p.tiles_per_seq - 1 - (w % p.tiles_per_seq);
@@ -818,7 +820,7 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
                         const uint32_t ps = seq0 + (uint32_t)pub;
                         publish((int)(ps % (uint32_t)ring), ps + 1);
                     }
-                    wait_done(s_done + slot, need_done, &g_bwd_wait_timeouts, poll_limit, lane);
+                    wait_done(s_done + slot, need_done, &g_bwd_wait_timeouts, s_abort, poll_limit, lane);
                 }
                 const uint32_t nc = (uint32_t)__builtin_amdgcn_readlane(nc_v, i & 63);
                 tgt0 += slot == 0 ? nc : 0u;
@@ -851,7 +853,7 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
             const int slot = (int)(seq % (uint32_t)ring);
             const int blk = __builtin_amdgcn_readfirstlane(s_ulist[u]);
             const unsigned long long bm = uniform_u64(s_umask[u]);
-            wait_ready2(s_ready + slot * kBwdDqProducers, seq + 1, &g_bwd_wait_timeouts, poll_limit, lane);
+            wait_ready2(s_ready + slot * kBwdDqProducers, seq + 1, &g_bwd_wait_timeouts, s_abort, poll_limit, lane);
             __builtin_amdgcn_s_setprio(1);   // a computing wave goes before polling ones
             const uint8_t* kslot = smem + slot * L::kSlot;
             const uint8_t* vslot = kslot + L::kPart;

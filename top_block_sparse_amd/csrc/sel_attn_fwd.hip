@@ -82,7 +82,7 @@ struct SelLds {
     __host__ __device__ static int umask(int ring) { return masks(ring) + kSelWin * 8; }   // u64 [kSelWin]
     __host__ __device__ static int ulist(int ring) { return umask(ring) + kSelWin * 8; }   // i32 [kSelWin]
     __host__ __device__ static int ncnt(int ring) { return ulist(ring) + kSelWin * 4; }    // i32 [kSelWin]
-    __host__ __device__ static int count(int ring) { return ncnt(ring) + kSelWin * 4; }    // i32
+    __host__ __device__ static int count(int ring) { return ncnt(ring) + kSelWin * 4; }    // i32, then the abort word
     __host__ __device__ static int ready(int ring) { return count(ring) + 16; }            // u32 [ring][producers]
     __host__ __device__ static int done(int ring) { return ready(ring) + kSelRingMax * kSelProducers * 4; }
     __host__ __device__ static int ent(int ring) { return done(ring) + kSelRingMax * 4; }  // i32 [T*topk]
@@ -147,6 +147,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     int* s_ulist = reinterpret_cast<int*>(smem + L::ulist(ring));
     int* s_ncnt = reinterpret_cast<int*>(smem + L::ncnt(ring));
     int* s_count = reinterpret_cast<int*>(smem + L::count(ring));
+    uint32_t* s_abort = reinterpret_cast<uint32_t*>(smem + L::count(ring) + 4);
     uint32_t* s_ready = reinterpret_cast<uint32_t*>(smem + L::ready(ring));
     uint32_t* s_done = reinterpret_cast<uint32_t*>(smem + L::done(ring));
     int* s_ent = reinterpret_cast<int*>(smem + L::ent(ring));
@@ -225,6 +226,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
 
     const bool consumer = wave < kSelConsumers;
     int poll_limit = p.spin_limit;              // this wave's bound on a ring wait (drops after a give-up)
+    if (tid == 0) s_abort[0] = 0u;             // raised by a wave whose wait gave up
 
     // ---- consumer bookkeeping for its m-tile (row = mt*16 + lr)
     const int mt = wave;
@@ -515,7 +517,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
                         const uint32_t ps = seq0 + (uint32_t)pub;
                         publish((int)(ps % (uint32_t)ring), ps + 1);
                     }
-                    wait_done(s_done + slot, need_done, &g_fwd_wait_timeouts, poll_limit, lane);
+                    wait_done(s_done + slot, need_done, &g_fwd_wait_timeouts, s_abort, poll_limit, lane);
                 }
                 const int blk = __builtin_amdgcn_readlane(ul_v, i & 63);
                 const uint32_t nc = (uint32_t)__builtin_amdgcn_readlane(nc_v, i & 63);
@@ -559,7 +561,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
                     const int slot = (int)(seq % (uint32_t)ring);
                     const int blk = __builtin_amdgcn_readlane(ul, bitp);
                     const unsigned long long bm = readlane_u64(m, bitp);
-                    wait_ready2(s_ready + slot * kSelProducers, seq + 1, &g_fwd_wait_timeouts, poll_limit, lane);
+                    wait_ready2(s_ready + slot * kSelProducers, seq + 1, &g_fwd_wait_timeouts, s_abort, poll_limit, lane);
                     __builtin_amdgcn_s_setprio(1);   // a computing consumer goes before polling ones
                     compute(smem + slot * L::kSlot, blk, bm);
                     __builtin_amdgcn_s_setprio(0);
