@@ -85,6 +85,31 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// The tokens of m-tile c of a tile of ntok tokens with G query rows each
+// (its 16 rows hold tokens 16c/G .. (16c+15)/G), as a bit mask; 0 for
+// c >= mtiles.  A union builder computes it once per tile, for c = lane.
+__device__ __forceinline__ unsigned long long mtile_token_mask(int c, int G, int ntok, int mtiles) {
+    if (c >= mtiles) return 0ull;
+    const int tf = (c * 16) / G;
+    int tl = (c * 16 + 15) / G;
+    tl = tl < ntok - 1 ? tl : ntok - 1;
+    const unsigned long long hi = tl >= 63 ? ~0ull : ((1ull << (tl + 1)) - 1ull);
+    return tf > tl ? 0ull : (hi & ~((1ull << tf) - 1ull));
+}
+
+// The number of m-tiles with a token in m, from the per-lane masks above
+// (lane c holds m-tile c's).
+__device__ __forceinline__ int mtiles_meeting(unsigned long long m, unsigned long long cm_lane,
+                                              int mtiles) {
+    int nc = 0;
+    for (int c = 0; c < mtiles; ++c) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cm_lane, c);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(cm_lane >> 32), c);
+        nc += (m & (((unsigned long long)hi << 32) | lo)) != 0ull ? 1 : 0;
+    }
+    return nc;
+}
+
 // Bounded waits of the LDS ring protocols.  Every wait polls at most
 // `limit` times (a consistent protocol never comes close), so a protocol
 // error can only give wrong values, never a hung GPU.  A wait that runs out

@@ -763,6 +763,9 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
         }
         __syncthreads();
         if (wave == 0) {
+            // m-tile `lane`'s tokens, for the need counts (per window, so
+            // that nothing stays live across the ring loop)
+            const unsigned long long cm_lane = mtile_token_mask(lane, G, ntok, p.mtiles);
             int n = 0;
             for (int c = 0; c < win_n; c += 64) {
                 const int x = c + lane;
@@ -770,15 +773,8 @@ __global__ void __launch_bounds__(kBwdDqThreads) bwd_dq_kernel(const SelBwdParam
                 const unsigned long long bal = __ballot(m != 0ull);
                 if (m != 0ull) {
                     const int pos = n + __popcll(bal & ((1ull << lane) - 1ull));
-                    int nc = 0;                         // compute waves (m-tiles) that need the block
-                    for (int c = 0; c < p.mtiles; ++c) {
-                        const int tf = (c * 16) / G;
-                        int tl = (c * 16 + 15) / G;
-                        tl = tl < ntok - 1 ? tl : ntok - 1;
-                        const unsigned long long hi = tl >= 63 ? ~0ull : ((1ull << (tl + 1)) - 1ull);
-                        const unsigned long long cm = tf > tl ? 0ull : (hi & ~((1ull << tf) - 1ull));
-                        nc += (m & cm) != 0ull ? 1 : 0;
-                    }
+                    // compute waves (m-tiles) that need the block
+                    const int nc = mtiles_meeting(m, cm_lane, p.mtiles);
                     s_ulist[pos] = win_lo + x;
                     s_umask[pos] = m;
                     s_ncnt[pos] = nc;

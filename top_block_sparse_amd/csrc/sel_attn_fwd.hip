@@ -53,7 +53,7 @@ constexpr int kSelConsumers = 14;                  // waves that own an m-tile
 constexpr int kSelProducers = 2;                   // waves that stream K/V
 constexpr int kSelWaves = kSelConsumers + kSelProducers;
 constexpr int kSelThreads = kSelWaves * 64;
-constexpr int kSelWin = 256;                       // blocks per union-building window
+constexpr int kSelWin = 1024;                      // blocks per union-building window
 constexpr int kSelRingMax = 4;                     // LDS slots of K/V blocks (3 if LDS is short)
 constexpr int kSelDepth = 2;                       // blocks in flight per producer (<= slots)
 constexpr int kLdsBytes = 160 * 1024;
@@ -430,9 +430,9 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         const int win_n = (nb_range - win_lo) < kSelWin ? (nb_range - win_lo) : kSelWin;
         if (WIN && p.dense) {
             // every block of the window: the tokens whose key range meets it
-            for (int x = tid; x < kSelWin; x += kSelThreads) {
+            for (int x = tid; x < win_n; x += kSelThreads) {
                 unsigned long long mk = 0ull;
-                if (x < win_n) {
+                {
                     const long long bk = (long long)(win_lo + x) * kBlockKeys;
                     long long t_lo = 0, t_hi = ntok - 1;
                     if (p.wr >= 0 && bk - p.wr - tok0 - off > t_lo) t_lo = bk - p.wr - tok0 - off;
@@ -447,7 +447,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
             }
             lds_barrier();
         } else {
-            for (int x = tid; x < kSelWin; x += kSelThreads) s_masks[x] = 0ull;
+            for (int x = tid; x < win_n; x += kSelThreads) s_masks[x] = 0ull;   // (only these are read)
             lds_barrier();
             for (int e = tid; e < nent; e += kSelThreads) {
                 const int id = s_ent[e];
@@ -456,6 +456,9 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         }
         lds_barrier();
         if (wave == 0) {      // ascending compaction of the non-empty blocks
+            // m-tile `lane`'s tokens, for the need counts (per window, so
+            // that nothing stays live across the ring loop)
+            const unsigned long long cm_lane = mtile_token_mask(lane, G, ntok, p.mtiles);
             int n = 0;
             for (int c = 0; c < win_n; c += 64) {
                 const int x = c + lane;
@@ -464,15 +467,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
                 if (m != 0ull) {
                     const int pos = n + __popcll(bal & ((1ull << lane) - 1ull));
                     // consumers (m-tiles) that need the block
-                    int nc = 0;
-                    for (int c = 0; c < p.mtiles; ++c) {
-                        const int tf = (c * 16) / G;
-                        int tl = (c * 16 + 15) / G;
-                        tl = tl < ntok - 1 ? tl : ntok - 1;
-                        const unsigned long long hi = tl >= 63 ? ~0ull : ((1ull << (tl + 1)) - 1ull);
-                        const unsigned long long cm = tf > tl ? 0ull : (hi & ~((1ull << tf) - 1ull));
-                        nc += (m & cm) != 0ull ? 1 : 0;
-                    }
+                    const int nc = mtiles_meeting(m, cm_lane, p.mtiles);
                     s_ulist[pos] = win_lo + x;
                     s_umask[pos] = m;
                     s_ncnt[pos] = nc;
@@ -547,7 +542,7 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         } else {
             // only the blocks this m-tile needs: a bit per union position
 #pragma unroll 1
-            for (int k = 0; k < kSelWin / 64; ++k) {
+            for (int k = u_beg / 64; k < (u_end + 63) / 64; ++k) {
                 const int x = 64 * k + lane;
                 const bool in = x >= u_beg && x < u_end;
                 const unsigned long long m = in ? s_umask[x] : 0ull;
