@@ -800,6 +800,8 @@ SELECT_SHAPES = [
     ((8256,), None, 2, 1, 64, 48, 1, 2),               # 128 candidates (row-wise picks), 48 entries
     ((8320,), None, 2, 1, 64, 20, 1, 1),               # 129 candidates (one wave per token)
     ((4200,), None, 128, 1, 64, 64, 1, 2),             # the largest group and topk
+    ((8208,), None, 8, 2, 128, 24, 1, 2),              # 512 windows: eight full chunks, the last
+                                                       # window's half in block 128
 ]
 
 
@@ -845,6 +847,28 @@ def test_block_select_planted_block():
         qb = i // 64
         if 1 <= star < qb - 1:
             assert got[i, 0, 3] == star, (i, got[i, 0])
+
+
+def test_block_select_rising_scores():
+    """Scores that grow along the keys by far more than 2^8 per 64 windows:
+    each chunk raises the row maximum, so every held block mass is rescaled
+    again and again before the sums are taken."""
+    S = 4000
+    spec = inputs.PrefillSpec("selrise", (S, 1500), 8, 2, 128, 12, seed=92)
+    dd = inputs.make_prefill(spec)
+    q = dd["q"].float() * 0.02
+    q[:, :, 0] = 8.0                                   # about 15 (log2 units) more per 1024 keys
+    k = dd["k"].float() * 0.02
+    for b0, b1 in ((0, S), (S, S + 1500)):
+        k[b0:b1, :, 0] = torch.linspace(0.0, 60.0, b1 - b0).unsqueeze(1)
+    dd["q"], dd["k"] = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    got = run_select(dd, 12)
+    ref, sc = oracle.block_select(dd["q"], dd["k"], dd["cu_seqlens_q"], dd["cu_seqlens_k"],
+                                  topk=12, with_scores=True)
+    cu_q, cu_k = dd["cu_seqlens_q"].numpy(), dd["cu_seqlens_k"].numpy()
+    toks = np.arange(int(cu_q[-1]))
+    exact = check_select(got, ref, sc, cu_q, cu_k, toks, 1, 2, 4, "rising")
+    assert exact >= 0.97 * toks.size * 2, exact
 
 
 @pytest.mark.parametrize("name", ["prefill_b2_s8192_h32_kv8_d128_top16",

@@ -18,7 +18,8 @@ SOURCES = ["fsa_api.hip", "sel_attn_fwd.hip", "sel_attn_fwd_bc.hip", "sel_attn_b
            "topk_decode.hip", "lse_merge.hip", "block_select.hip"]
 # The prefill kernels never produce or test NaNs (masked scores are -inf,
 # which stays honoured), so fmax there compiles to a single instruction.
-EXTRA_FLAGS = {"sel_attn_fwd.hip": ["-fno-honor-nans"], "sel_attn_fwd_bc.hip": ["-fno-honor-nans"]}
+EXTRA_FLAGS = {"sel_attn_fwd.hip": ["-fno-honor-nans"], "sel_attn_fwd_bc.hip": ["-fno-honor-nans"],
+               "block_select.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 

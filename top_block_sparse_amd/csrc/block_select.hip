@@ -47,6 +47,9 @@ constexpr int kSelectWaves = 8;
 constexpr int kSelectThreads = kSelectWaves * 64;
 constexpr int kWinChunk = 64;          // windows per MFMA chunk (4 key tiles of 16)
 constexpr int kPickRegs = 8;           // register-held candidates per lane in the row-wise selection
+constexpr int kOnePassChunks = 8;      // rows of at most this many chunks take the one-pass kernel
+constexpr float kSelLazy = 8.f;        // the one-pass maximum moves when passed by more than this (log2)
+constexpr float kSelFar = -1e30f;      // its start: finite, so 2^(-inf - m) is 0 without a test
 
 struct Bounds {
     int64_t q0, k0;
@@ -84,22 +87,38 @@ __device__ __forceinline__ float group_sum(float x, int n) {
     return x;
 }
 
-#define FSA_DPP_U64(v, ctrl)                                                                       \
-    ((((unsigned long long)(uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)((v) >> 32), ctrl, \
-                                                                 0xF, 0xF, false)) << 32) |       \
-     (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v), ctrl, 0xF, 0xF, false))
-
-// maximum of a 64-bit key over each 16-lane row (every lane of the row gets
-// it): quad swaps, then the half-row and row mirrors
-__device__ __forceinline__ unsigned long long row_max_u64(unsigned long long x) {
-    auto pick = [](unsigned long long a, unsigned long long b) { return a > b ? a : b; };
-    x = pick(x, FSA_DPP_U64(x, 0xB1));
-    x = pick(x, FSA_DPP_U64(x, 0x4E));
-    x = pick(x, FSA_DPP_U64(x, 0x141));
-    x = pick(x, FSA_DPP_U64(x, 0x140));
+// maximum (MAX) or sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four rows),
+// every lane getting it: the gfx950 permlane16 and permlane32 swaps
+template <bool MAX>
+__device__ __forceinline__ float rows4_combine(float x) {
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+    {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
     return x;
 }
-#undef FSA_DPP_U64
+
+// maximum of a 64-bit key over each 16-lane row (every lane of the row gets
+// it): the row maximum of the high words, then of the low words of the lanes
+// that hold it -- quad swaps, then the half-row and row mirrors, each step one
+// max with a DPP operand
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));
+    return x;
+}
+__device__ __forceinline__ unsigned long long row_max_u64(unsigned long long x) {
+    const uint32_t hi = row_max_u32((uint32_t)(x >> 32));
+    const uint32_t lo = row_max_u32((uint32_t)(x >> 32) == hi ? (uint32_t)x : 0u);
+    return ((unsigned long long)hi << 32) | lo;
+}
 
 // wave-wide maximum of a 64-bit key: the row maximum, then the gfx950
 // permlane swaps across rows (all VALU; no LDS round trips)
@@ -158,15 +177,15 @@ __global__ void __launch_bounds__(256) cmp_keys_kernel(const BlockSelectParams p
 }
 
 // ---- 2. compressed attention, block importance and selection
-// LDS: the importance table [T][nb_max] fp32, then two buffers of one chunk
+// LDS: the importance table [T][row stride] fp32, then two buffers of one chunk
 // of 64 window summaries in MFMA A-operand order -- fragment (kt, s), 1 KiB,
 // lane l's 16 bytes = C[16kt + l%16][32s + 8(l/16) .. +8] -- so every operand
 // read is one contiguous wave read.  The chunk is loaded once per workgroup
 // (all waves share it), the next one while the current one is used.
 // Six waves per SIMD (80 VGPRs): three workgroups share a CU, as the LDS
 // allows; at the compiler's own choice of 92 VGPRs only two fit.
-template <int D>
-__global__ void __launch_bounds__(kSelectThreads, 6) block_select_kernel(const BlockSelectParams p) {
+template <int D, int NCH>
+__global__ void __launch_bounds__(kSelectThreads, NCH == 0 ? 6 : 4) block_select_kernel(const BlockSelectParams p) {
     constexpr int KS = D / 32;
     constexpr int CPR = D / 8;                                   // 16-byte pieces per window
     constexpr int kChunkBytes = kWinChunk * D * 2;
@@ -192,10 +211,11 @@ __global__ void __launch_bounds__(kSelectThreads, 6) block_select_kernel(const B
     int ncmp = n_windows(sb.Sk);
     ncmp = ncmp < p.ncmp_max ? ncmp : p.ncmp_max;
     const int G = p.G;
-    float* s_imp = reinterpret_cast<float*>(smem);                 // [T][nb]
-    uint8_t* cbuf = smem + (((size_t)p.T * nb * 4 + 15) & ~(size_t)15);
+    const int nbs = select_row_stride(nb);
+    float* s_imp = reinterpret_cast<float*>(smem);                 // [T][nbs]
+    uint8_t* cbuf = smem + (((size_t)p.T * nbs * 4 + 15) & ~(size_t)15);
 
-    for (int x = tid; x < p.T * nb; x += kSelectThreads) s_imp[x] = 0.f;
+    for (int x = tid; x < p.T * nbs; x += kSelectThreads) s_imp[x] = 0.f;
 
     // this wave's m-tile: row = wave*16 + lr -> (token t_l, head hh)
     const int row = wave * 16 + lr;
@@ -222,30 +242,36 @@ __global__ void __launch_bounds__(kSelectThreads, 6) block_select_kernel(const B
     const int64_t cstride = (int64_t)p.Hkv * D;        // elements between windows
     const float c2 = p.scale_log2;
 
-    // chunk staging: piece x = tid + 256 n -> window x / CPR, 8-dim piece x % CPR
+    // chunk staging: piece y = tid + n * threads is lane y % 64 of fragment
+    // f = y / 64 = (kt, s) = (f / KS, f % KS), i.e. window 16 kt + y % 16 of
+    // the chunk, 8-dim piece 4 s + (y % 64) / 16; its LDS place is y * 16, so
+    // each wave's store fills one whole fragment (no bank conflicts)
     u32x4_t stg[NL];
+    auto piece_window = [&](int n) {
+        const int y = tid + n * kSelectThreads;
+        return 16 * ((y / 64) / KS) + (y & 15);
+    };
+    auto piece_dims = [&](int n) {                      // first of the piece's 8 dims
+        const int y = tid + n * kSelectThreads;
+        return 8 * (4 * ((y / 64) % KS) + ((y & 63) >> 4));
+    };
     auto fetch = [&](int ch) {
 #pragma unroll
         for (int n = 0; n < NL; ++n) {
-            const int x = tid + n * kSelectThreads;
-            int wi = ch * kWinChunk + x / CPR;
+            int wi = ch * kWinChunk + piece_window(n);
             wi = wi < p.ncmp_max ? wi : p.ncmp_max - 1;          // (masked below)
-            stg[n] = *reinterpret_cast<const u32x4_t*>(cbase + wi * cstride + (x % CPR) * 8);
+            stg[n] = *reinterpret_cast<const u32x4_t*>(cbase + wi * cstride + piece_dims(n));
         }
     };
     auto stage = [&](int buf) {
         uint8_t* dst = cbuf + buf * kChunkBytes;
 #pragma unroll
-        for (int n = 0; n < NL; ++n) {
-            const int x = tid + n * kSelectThreads;
-            const int wr = x / CPR, pc = x % CPR;                 // window in chunk, piece
-            const int kt = wr / 16, s = pc / 4;
-            const int l = (pc % 4) * 16 + wr % 16;                // fragment lane
-            *reinterpret_cast<u32x4_t*>(dst + (kt * KS + s) * 1024 + l * 16) = stg[n];
-        }
+        for (int n = 0; n < NL; ++n)
+            *reinterpret_cast<u32x4_t*>(dst + (tid + n * kSelectThreads) * 16) = stg[n];
     };
-    // S^T of chunk ch from buffer buf: st[kt][i] = window ch*64 + 16kt + 4lg + i (log2 units)
-    auto scores = [&](int ch, int buf, f32x4_t (&st)[4]) {
+    // S^T of the chunk in buffer buf: st[kt][i] = <q_row, c_w> for window
+    // w = ch*64 + 16kt + 4lg + i of chunk ch
+    auto products = [&](int buf, f32x4_t (&st)[4]) {
         const uint8_t* src = cbuf + buf * kChunkBytes + lane * 16;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -254,6 +280,20 @@ __global__ void __launch_bounds__(kSelectThreads, 6) block_select_kernel(const B
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
                 st[kt] = mfma_16x16x32(*reinterpret_cast<const u32x4_t*>(src + (kt * KS + s) * 1024), qf[s], st[kt]);
+    };
+    // windows the row does not see -> -inf
+    auto mask = [&](int ch, f32x4_t (&st)[4]) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int wi = ch * kWinChunk + kt * 16 + lg * 4 + i;
+                st[kt][i] = wi < nvis ? st[kt][i] : -INFINITY;
+            }
+    };
+    // the same in log2 units, masked
+    auto scores = [&](int ch, int buf, f32x4_t (&st)[4]) {
+        products(buf, st);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -263,14 +303,15 @@ __global__ void __launch_bounds__(kSelectThreads, 6) block_select_kernel(const B
             }
     };
 
+    float* imp_row = s_imp + (valid ? t_l : 0) * nbs;
+    // lanes summed before an atomic: a token's rows within the m-tile (G
+    // dividing 16), all 16 rows (G a multiple of 16), else none
+    const int gsum = (16 % G == 0) ? G : (G % 16 == 0 ? 16 : 1);
+    if constexpr (NCH == 0) {
     // Two passes over the chunks: row max and sum, then probabilities ->
     // block masses of token t_l.  Step st_i runs chunk st_i % nch from buffer
     // st_i & 1 while the next step's chunk is fetched.
     float m = -INFINITY, l = 0.f, inv = 0.f;
-    float* imp_row = s_imp + (valid ? t_l : 0) * nb;
-    // lanes summed before an atomic: a token's rows within the m-tile (G
-    // dividing 16), all 16 rows (G a multiple of 16), else none
-    const int gsum = (16 % G == 0) ? G : (G % 16 == 0 ? 16 : 1);
     const int nsteps = 2 * nch;
     if (nsteps > 0) {
         fetch(0);
@@ -333,6 +374,114 @@ __global__ void __launch_bounds__(kSelectThreads, 6) block_select_kernel(const B
         if (si + 1 < nsteps) stage((si + 1) & 1);
         __syncthreads();
     }
+    } else {
+    // One pass, for rows of at most NCH chunks.  A row's windows are spread
+    // over its four lanes (lg); the four share a lazily moved maximum m (log2
+    // units) that moves only when a chunk's row maximum passes it by more
+    // than kSelLazy, every mass held so far being scaled by 2^(m_old - m_new)
+    // then, so each exponential is at most 2^kSelLazy.  mass[ch][kt] of lane
+    // (lr, lg) is the unnormalised mass of block b = ch*16 + kt*4 + lg: its
+    // windows 4b .. 4b+2, half of 4b+3, and half of 4b-1, which the lane of
+    // block b-1 (16 lanes down, the last row passing into the next key tile or
+    // chunk) hands over.  The masses reach the table once, after the loop.
+    float mass[NCH][4];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) mass[c][kt] = 0.f;
+    float carry = 0.f;                                 // lanes lg = 0: half of the last window so far
+    float m = kSelFar, lsum = 0.f;
+    // the wave's first row has its fewest visible windows: chunks it sees
+    // whole need no mask
+    const int nvis0 = __builtin_amdgcn_readfirstlane(nvis);
+    const int down = ((lane + 48) & 63) << 2;          // ds_bpermute address of lane - 16
+    const int nc = nch < NCH ? nch : NCH;              // (the launcher keeps nch <= NCH)
+    // Chunk loads through a buffer resource over this sequence's windows: a
+    // window past the last reads as zeros, so every load is issued without a
+    // clamp or a condition (the chunk after the last is fetched and staged
+    // unused), and the wait counts stay exact across iterations.
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)cbase, 0, p.ncmp_max > 0 ? (uint32_t)(((int64_t)p.ncmp_max - 1) * cstride * 2 + D * 2) : 0u,
+        0x00020000);
+    int voff[NL];                                      // this thread's bytes within a chunk
+#pragma unroll
+    for (int n = 0; n < NL; ++n) voff[n] = piece_window(n) * (int)cstride * 2 + piece_dims(n) * 2;
+    const int chunk_bytes = kWinChunk * (int)cstride * 2;
+    auto fetch1 = [&](int ch) {
+#pragma unroll
+        for (int n = 0; n < NL; ++n) stg[n] = __builtin_amdgcn_raw_buffer_load_b128(crs, voff[n], ch * chunk_bytes, 0);
+    };
+    if (nc > 0) {
+        fetch1(0);
+        stage(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0): the q fragments are in
+    __syncthreads();                                   // table cleared, chunk 0 staged
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+        if (ch >= nc) break;
+        {
+            fetch1(ch + 1);
+            if (wave < p.mtiles) {
+                f32x4_t st[4];
+                products(ch & 1, st);
+                if ((ch + 1) * kWinChunk > nvis0) mask(ch, st);
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+                    mx = fmaxf(mx, fmaxf(fmaxf(st[kt][0], st[kt][1]), fmaxf(st[kt][2], st[kt][3])));
+                mx = rows4_combine<true>(mx) * c2;     // (c2 > 0; -inf stays -inf)
+                if (mx > m + kSelLazy) {
+                    const float f = fast_exp2(m - mx);
+#pragma unroll
+                    for (int c = 0; c < ch; ++c)
+#pragma unroll
+                        for (int kt = 0; kt < 4; ++kt) mass[c][kt] *= f;
+                    carry *= f;
+                    lsum *= f;
+                    m = mx;
+                }
+                float own[4], sh[4];
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    float pr[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(st[kt][i], c2, -m));
+                    const float s3 = pr[0] + pr[1] + pr[2];
+                    lsum += s3 + pr[3];
+                    own[kt] = fmaf(0.5f, pr[3], s3);
+                    sh[kt] = __int_as_float(__builtin_amdgcn_ds_bpermute(down, __float_as_int(0.5f * pr[3])));
+                }
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+                    mass[ch][kt] = own[kt] + (lg > 0 ? sh[kt] : (kt > 0 ? sh[kt - 1] : carry));
+                carry = sh[3];
+            }
+            stage((ch + 1) & 1);
+            __syncthreads();
+        }
+    }
+    if (wave < p.mtiles) {
+        const float l = rows4_combine<false>(lsum);
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const bool writer = valid && (lr % gsum) == 0;
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch) {
+            if (ch < nc) {
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    const int blk = ch * (kWinChunk / 4) + kt * 4 + lg;
+                    const float v = group_sum(mass[ch][kt] * inv, gsum);
+                    if (writer && v != 0.f && blk < nb) atomicAdd(imp_row + blk, v);
+                }
+            }
+        }
+        const int blk = nc * (kWinChunk / 4);          // half of the last window, lanes lg = 0
+        const float v = group_sum(carry * inv, gsum);
+        if (writer && lg == 0 && v != 0.f && blk < nb) atomicAdd(imp_row + blk, v);
+    }
+    __syncthreads();
+    }
 
     // selection, when a token has at most 16 * kPickRegs candidates: four
     // tokens per wave, one per 16-lane row.  Each lane keeps its candidates
@@ -364,35 +513,46 @@ __global__ void __launch_bounds__(kSelectThreads, 6) block_select_kernel(const B
                 lo = p.init;
                 hi = qb - p.local + 1;
             }
-            const float* imp = s_imp + (tv ? t : 0) * nb;
-            float v[kPickRegs];
+            // the lane's candidates as 64-bit keys (importance bits, then the
+            // inverted id: the larger key is the larger importance, ties to
+            // the smaller block; 0 = none), sorted once in descending order;
+            // a pick is the row maximum of the lanes' first keys, and the
+            // lane that holds it moves on to its next key
+            const float* imp = s_imp + (tv ? t : 0) * nbs;
+            unsigned long long key[kPickRegs];
 #pragma unroll
             for (int j = 0; j < kPickRegs; ++j) {
                 const int x = lo + l16 + 16 * j;
-                v[j] = x < hi ? imp[x] : -1.f;
+                key[j] = x < hi ? ((unsigned long long)__float_as_uint(imp[x]) << 32) | (0xFFFFFFFFu - (uint32_t)x)
+                                : 0ull;
             }
+            // Batcher's odd-even merge sort of eight keys (19 compare-exchanges)
+            auto cx = [&](int a, int b) {
+                const unsigned long long hi_ = key[a] > key[b] ? key[a] : key[b];
+                const unsigned long long lo_ = key[a] > key[b] ? key[b] : key[a];
+                key[a] = hi_;
+                key[b] = lo_;
+            };
+            static_assert(kPickRegs == 8, "sorting network for eight keys");
+            cx(0, 1); cx(2, 3); cx(4, 5); cx(6, 7);
+            cx(0, 2); cx(1, 3); cx(4, 6); cx(5, 7);
+            cx(1, 2); cx(5, 6);
+            cx(0, 4); cx(1, 5); cx(2, 6); cx(3, 7);
+            cx(2, 4); cx(3, 5);
+            cx(1, 2); cx(3, 4); cx(5, 6);
             bool go = n < p.topk && lo < hi;
             while (__builtin_amdgcn_ballot_w64(go) != 0ull) {
-                unsigned long long key = 0ull;
-#pragma unroll
-                for (int j = 0; j < kPickRegs; ++j) {
-                    const unsigned long long kj =
-                        v[j] >= 0.f ? ((unsigned long long)__float_as_uint(v[j]) << 32) |
-                                          (0xFFFFFFFFu - (uint32_t)(lo + l16 + 16 * j))
-                                    : 0ull;
-                    key = kj > key ? kj : key;
-                }
-                key = row_max_u64(key);
+                const unsigned long long best = row_max_u64(key[0]);
                 if (go) {
-                    if (key == 0ull) {
+                    if (best == 0ull) {
                         go = false;                     // no candidate left
                     } else {
-                        const int x = (int)(0xFFFFFFFFu - (uint32_t)key);
-                        put(x);
-                        const int r = x - lo;
+                        put((int)(0xFFFFFFFFu - (uint32_t)best));
+                        if (key[0] == best) {           // this lane's key: the next one comes up
 #pragma unroll
-                        for (int j = 0; j < kPickRegs; ++j)
-                            if (l16 == (r & 15) && j == (r >> 4)) v[j] = -1.f;   // used
+                            for (int j = 0; j + 1 < kPickRegs; ++j) key[j] = key[j + 1];
+                            key[kPickRegs - 1] = 0ull;
+                        }
                         go = n < p.topk;
                     }
                 }
@@ -428,7 +588,7 @@ __global__ void __launch_bounds__(kSelectThreads, 6) block_select_kernel(const B
                 if (lane == n) first = x;
                 ++n;
             }
-            float* imp = s_imp + t * nb;
+            float* imp = s_imp + t * nbs;
             const int lo = p.init, hi = qb - p.local + 1;
             while (n < p.topk && lo < hi) {
                 unsigned long long best = 0ull;
@@ -455,7 +615,7 @@ __global__ void __launch_bounds__(kSelectThreads, 6) block_select_kernel(const B
 }
 
 size_t block_select_lds_bytes(int T, int nb_max, int D) {
-    return (((size_t)T * nb_max * 4 + 15) & ~(size_t)15) + 2 * (size_t)kWinChunk * D * 2;
+    return (((size_t)T * select_row_stride(nb_max) * 4 + 15) & ~(size_t)15) + 2 * (size_t)kWinChunk * D * 2;
 }
 
 hipError_t launch_block_select(const BlockSelectParams& p, int D, hipStream_t stream) {
@@ -466,16 +626,28 @@ hipError_t launch_block_select(const BlockSelectParams& p, int D, hipStream_t st
         else hipLaunchKernelGGL(cmp_keys_kernel<128>, dim3(gc), dim3(256), 0, stream, p);
     }
     const size_t lds = block_select_lds_bytes(p.T, p.nb_max, D);
-    static std::atomic<unsigned long long> lds_set[2];     // devices with the LDS limit raised
-    const int di = D == 64 ? 0 : 1;
-    const void* f = D == 64 ? reinterpret_cast<const void*>(&block_select_kernel<64>)
-                            : reinterpret_cast<const void*>(&block_select_kernel<128>);
+    // rows of at most kOnePassChunks chunks of windows: the one-pass kernel
+    // (and 32-bit byte offsets over a sequence's windows)
+    const bool one = (p.ncmp_max + kWinChunk - 1) / kWinChunk <= kOnePassChunks &&
+                     (int64_t)(kOnePassChunks + 1) * kWinChunk * p.Hkv * D * 2 < (int64_t)1 << 31;
+    static std::atomic<unsigned long long> lds_set[4];     // devices with the LDS limit raised
+    const int di = (D == 64 ? 0 : 1) + (one ? 2 : 0);
+    const void* f = D == 64 ? (one ? reinterpret_cast<const void*>(&block_select_kernel<64, kOnePassChunks>)
+                                   : reinterpret_cast<const void*>(&block_select_kernel<64, 0>))
+                            : (one ? reinterpret_cast<const void*>(&block_select_kernel<128, kOnePassChunks>)
+                                   : reinterpret_cast<const void*>(&block_select_kernel<128, 0>));
     hipError_t e = ensure_lds_limit(f, lds_set[di]);
     if (e != hipSuccess) return e;
     const unsigned grid = (unsigned)(p.batch * p.Hkv * p.tiles_per_seq);
     if (grid > 0) {
-        if (D == 64) hipLaunchKernelGGL(block_select_kernel<64>, dim3(grid), dim3(kSelectThreads), lds, stream, p);
-        else hipLaunchKernelGGL(block_select_kernel<128>, dim3(grid), dim3(kSelectThreads), lds, stream, p);
+        const dim3 gd(grid), bd(kSelectThreads);
+        if (D == 64) {
+            if (one) hipLaunchKernelGGL((block_select_kernel<64, kOnePassChunks>), gd, bd, lds, stream, p);
+            else hipLaunchKernelGGL((block_select_kernel<64, 0>), gd, bd, lds, stream, p);
+        } else {
+            if (one) hipLaunchKernelGGL((block_select_kernel<128, kOnePassChunks>), gd, bd, lds, stream, p);
+            else hipLaunchKernelGGL((block_select_kernel<128, 0>), gd, bd, lds, stream, p);
+        }
     }
     return hipGetLastError();
 }

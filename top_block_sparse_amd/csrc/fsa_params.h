@@ -84,6 +84,11 @@ struct DecodeParams {
 };
 
 // Block-index producer (block_select.hip).
+// Row stride, in floats, of its importance table [T][blocks] in LDS: rows of
+// more than 16 blocks are padded to 16 (mod 64) floats, so that 16-lane groups
+// that read or add to four different rows fall in four different bank ranges.
+inline __host__ __device__ int select_row_stride(int nb) { return nb <= 16 ? nb : nb + ((16 - nb) & 63); }
+
 struct BlockSelectParams {
     const uint16_t* q;
     const uint16_t* k;
