@@ -484,21 +484,23 @@ __global__ void __launch_bounds__(kSelectThreads, NCH == 0 ? 6 : 4) block_select
     }
 
     // selection, when a token has at most 16 * kPickRegs candidates: four
-    // tokens per wave, one per 16-lane row.  Each lane keeps its candidates
-    // x = lo + (lane % 16) + 16 j in registers and every pick is a row-wide
-    // argmax (DPP within the row), so a pick costs no LDS round trip.
+    // tokens per wave, one per 16-lane row.  Each lane sorts its candidates
+    // x = lo + (lane % 16) + 16 j once; a pick is a row-wide maximum of the
+    // lanes' first keys (DPP within the row), and the row's first lane stores
+    // the entry to the output list at once.
     if (nblk - p.init <= 16 * kPickRegs) {
         const int grp = lane >> 4, l16 = lane & 15;
+        // keys 2 .. 7 of each lane's sorted list, [6][threads], in the chunk
+        // buffers (unused from here on)
+        unsigned long long* s_key = reinterpret_cast<unsigned long long*>(cbuf);
         for (int tb = 4 * wave; tb < ntok; tb += 4 * kSelectWaves) {
             const int t = tb + grp;
             const bool tv = t < ntok;
             const int ct = tok0 + t + off;
+            int32_t* out = p.blk_idx + ((sb.q0 + tok0 + (tv ? t : 0)) * p.Hkv + g) * (int64_t)p.topk;
             int n = 0;
-            int pick[4] = {-1, -1, -1, -1};             // entry l16 + 16 s of the list
             auto put = [&](int x) {
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4)
-                    if (n == l16 + 16 * s4) pick[s4] = x;
+                if (l16 == 0) out[n] = x;
                 ++n;
             };
             int lo = 0, hi = 0;
@@ -540,29 +542,32 @@ __global__ void __launch_bounds__(kSelectThreads, NCH == 0 ? 6 : 4) block_select
             cx(0, 4); cx(1, 5); cx(2, 6); cx(3, 7);
             cx(2, 4); cx(3, 5);
             cx(1, 2); cx(3, 4); cx(5, 6);
+#pragma unroll
+            for (int j = 2; j < kPickRegs; ++j) s_key[(j - 2) * kSelectThreads + tid] = key[j];
+            unsigned long long head = key[0], nxt = key[1];   // the lane's next two keys
+            int h = 2;                                         // the one after them
             bool go = n < p.topk && lo < hi;
             while (__builtin_amdgcn_ballot_w64(go) != 0ull) {
-                const unsigned long long best = row_max_u64(key[0]);
+                const unsigned long long best = row_max_u64(head);
                 if (go) {
                     if (best == 0ull) {
                         go = false;                     // no candidate left
                     } else {
                         put((int)(0xFFFFFFFFu - (uint32_t)best));
-                        if (key[0] == best) {           // this lane's key: the next one comes up
-#pragma unroll
-                            for (int j = 0; j + 1 < kPickRegs; ++j) key[j] = key[j + 1];
-                            key[kPickRegs - 1] = 0ull;
+                        if (head == best) {             // this lane's key: the next one comes up
+                            head = nxt;
+                            nxt = h < kPickRegs ? s_key[(h - 2) * kSelectThreads + tid] : 0ull;
+                            ++h;
                         }
                         go = n < p.topk;
                     }
                 }
             }
             if (tv) {
-                int32_t* out = p.blk_idx + ((sb.q0 + tok0 + t) * p.Hkv + g) * (int64_t)p.topk;
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4) {
                     const int e = l16 + 16 * s4;
-                    if (e < p.topk) out[e] = e < n ? pick[s4] : -1;
+                    if (e < p.topk && e >= n) out[e] = -1;
                 }
             }
         }
@@ -615,7 +620,10 @@ __global__ void __launch_bounds__(kSelectThreads, NCH == 0 ? 6 : 4) block_select
 }
 
 size_t block_select_lds_bytes(int T, int nb_max, int D) {
-    return (((size_t)T * select_row_stride(nb_max) * 4 + 15) & ~(size_t)15) + 2 * (size_t)kWinChunk * D * 2;
+    // the chunk buffers, which then hold keys 2 .. kPickRegs-1 of each thread
+    const size_t chunks = 2 * (size_t)kWinChunk * D * 2;
+    const size_t keys = (size_t)(kPickRegs - 2) * kSelectThreads * 8;
+    return (((size_t)T * select_row_stride(nb_max) * 4 + 15) & ~(size_t)15) + (chunks > keys ? chunks : keys);
 }
 
 hipError_t launch_block_select(const BlockSelectParams& p, int D, hipStream_t stream) {
