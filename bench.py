@@ -17,8 +17,9 @@ are timed as legs with their own roofline objects, and so are the FP8 decode,
 the sliding window, the backward and the block selection.  Each phase is timed
 over exactly K calls issued back to back between one pair of HIP events on the
 stream the kernels run on, bracketed by device synchronisation, after W
-warm-up steps: the mean per call is that region divided by K (the host clock
-around the region is reported too).  A second pass of K calls, each between
+warm-up steps and at least 20 ms of untimed calls of that phase: the mean per
+call is that region divided by K (the host clock around the region is reported
+too).  A second pass of K calls, each between
 its own events, supplies the per-call median.  The fp64 CPU oracle is timed on
 a bounded token sample of the headline prefill on the host cores, plus the
 small prefill single-threaded and the whole decode workload.
@@ -151,8 +152,27 @@ class Timing:
         return float(np.median(self.per_call))
 
 
+SETTLE_MS = 20.0      # untimed calls of a leg before its timed ones, at least this long
+
+
+def settle(fn, stream):
+    """Untimed calls of fn until they have run SETTLE_MS, so that a leg is
+    timed in the steady state of its own loop rather than just after another
+    leg's (a short leg such as the decode otherwise shows the switch)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1e3 < SETTLE_MS:
+        for _ in range(4):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
 def timed(fn, K, stream):
-    """K calls of fn(i) timed as one region, then K calls timed one by one."""
+    """K calls of fn(i) timed as one region, then K calls timed one by one
+    (after the leg has settled)."""
+    settle(fn, stream)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
