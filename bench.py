@@ -19,10 +19,12 @@ over exactly K calls issued back to back between one pair of HIP events on the
 stream the kernels run on, bracketed by device synchronisation, after W
 warm-up steps and at least 20 ms of untimed calls of that phase: the mean per
 call is that region divided by K (the host clock around the region is reported
-too).  A second pass of K calls, each between
-its own events, supplies the per-call median.  The fp64 CPU oracle is timed on
-a bounded token sample of the headline prefill on the host cores, plus the
-small prefill single-threaded and the whole decode workload.
+too).  A second pass of K calls, each between its own events, supplies the
+per-call median.  Every roofline object also gives its fraction of a peak
+measured on the same GPU (``calibration``: a bf16 GEMM called through
+torch.matmul, and a 2 GiB device copy).  The fp64 CPU oracle is timed on a
+bounded token sample of the headline prefill on the host cores, plus the small
+prefill single-threaded and the whole decode workload.
 """
 
 import argparse
@@ -191,6 +193,43 @@ def timed(fn, K, stream):
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     return Timing(mean, wall, np.array([x.elapsed_time(y) for x, y in evs]))
+
+
+def calibrate(dev, stream, K):
+    """Peaks measured on this GPU, beside the spec ones: a bf16 GEMM called as a
+    library (torch.matmul -> hipBLASLt), and a plain device copy (bytes read
+    plus bytes written per second)."""
+    n = 8192
+    a = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    b = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+    g_t = timed(lambda i: torch.matmul(a, b, out=c), K, stream)
+    g_tflops = 2.0 * n ** 3 / (g_t.mean * 1e-3) / 1e12
+    del a, b, c
+    elems = 1 << 30                                     # 2 GiB of bf16 each way
+    src = torch.empty(elems, device=dev, dtype=torch.bfloat16)
+    src.fill_(1.0)
+    dst = torch.empty_like(src)
+    c_t = timed(lambda i: dst.copy_(src), K, stream)
+    c_bytes = 2 * elems * 2
+    c_gbs = c_bytes / (c_t.mean * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.synchronize()
+    log(f"calibration: bf16 GEMM {n}^3 {g_tflops:.0f} TFLOP/s, copy {c_gbs:.0f} GB/s")
+    return {"gemm_bf16": {"tflops": round(g_tflops, 1), "shape": [n, n, n],
+                          "ms_per_call": round(g_t.mean, 4), "how": "torch.matmul (hipBLASLt)"},
+            "copy": {"gbs": round(c_gbs, 1), "bytes_per_call": c_bytes,
+                     "ms_per_call": round(c_t.mean, 4), "how": "device tensor copy_, read + write"}}
+
+
+def add_calibrated(roofline, cal):
+    """The roofline's fraction of the measured peak of its own bound."""
+    if roofline.get("bound") == "mfma":
+        pk = cal["gemm_bf16"]["tflops"]
+    else:
+        pk = cal["copy"]["gbs"]
+    roofline["calibrated_peak"] = pk
+    roofline["frac_calibrated"] = round(roofline["achieved"] / pk, 4)
 
 
 def mfma_roofline(flops, t, traffic, kernel, extra=None):
@@ -485,6 +524,14 @@ def main():
         "block_select": select_obj,
         "wait_timeouts": timeouts,
     }
+
+    log("calibrating the GEMM and copy peaks")
+    cal = calibrate(dev, stream, K)
+    result["calibration"] = cal
+    for o in [result["roofline"], decode_obj["roofline"], decode_fp8_obj["roofline"],
+              window_obj["roofline"], backward_obj["roofline"], select_obj["roofline"]] + \
+            [po["roofline"] for nm, po in prefill_objs.items() if nm != HEADLINE]:
+        add_calibrated(o, cal)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(head, legs, dd, args.cpu_seconds)
