@@ -202,3 +202,15 @@ def test_block_select_planning(lib, batch, total_q, msq, msk, hkv, G, D, topk, i
     assert settle(want, got, big), (batch, total_q, msq, msk, hkv, G, D, topk, ws, got)
     if got == LAUNCH and ws > 0:
         assert call(ws - 1) == WORKSPACE
+
+
+@pytest.mark.parametrize("G", [1, 4, 128])
+def test_block_select_longest_supported_sequence(lib, G):
+    """2^20 keys (16384 blocks, one 64 KiB importance row plus its padding) is
+    the longest sequence block selection takes; one key more is rejected."""
+    hkv, D = 1, 128
+    for msk, want in ((1 << 20, LAUNCH), ((1 << 20) + 1, NOT_SUPPORTED)):
+        ws = lib.fsa_block_select_workspace_size(1, msk, hkv, D, 32, 16)
+        got = lib.fsa_block_select(FAKE, FAKE, FAKE, FAKE, 1, msk, msk, msk, msk, hkv * G, hkv,
+                                   D, 32, 16, 64, 16, 1, 2, 0.0, FAKE, ws, FAKE, None)
+        assert got == want, (G, msk, got)

@@ -188,7 +188,10 @@ SelectPlan plan_select(int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, i
     if (pl.nb_max < 1) pl.nb_max = 1;
     pl.ncmp_max = max_seqlen_k >= kSelectCmpSize ? (max_seqlen_k - kSelectCmpSize) / kSelectCmpStride + 1 : 0;
     int T = 128 / G;                            // 8 m-tiles of 16 rows
-    const int t_lds = (int)(kSelectLdsBudget / ((size_t)fsa::select_row_stride(pl.nb_max) * 4));
+    // (the table's rows are padded in LDS -- select_row_stride -- by at most 63
+    // floats; the budget is on the unpadded rows, so the padding never changes
+    // which lengths fit, and the padded table stays under 64 KiB + T * 252 B)
+    const int t_lds = (int)(kSelectLdsBudget / ((size_t)pl.nb_max * 4));
     T = T < t_lds ? T : t_lds;
     pl.T = T;                                   // 0: the table does not fit
     pl.mtiles = (T * G + 15) / 16;
