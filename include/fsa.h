@@ -269,7 +269,9 @@ int32_t fsa_topk_decode_auto_splits(int32_t batch, int32_t num_heads_q, int32_t 
  *   out        bf16 [batch, num_heads_q, head_dim]
  *   lse        fp32 [batch, num_heads_q], or NULL
  * The query sits after every cache position, so the bottom-right causal rule
- * leaves every listed position t < cache_seqlens[b] visible.
+ * leaves every listed position t < cache_seqlens[b] visible.  The waves of a
+ * workgroup take batches of the list as they free up, so the fp32 summation
+ * order can change between calls: out may differ in the last bit run to run.
  */
 fsa_status_t fsa_topk_decode(const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* tok_idx, const int32_t* block_table,
