@@ -48,6 +48,15 @@
  *   its G query heads attend to the keys of those blocks only (FSA page:
  *   NSA selected attention with block_size / topk; the Ascend SFA blog:
  *   gather the selected K/V rows, then ordinary attention, -1 = invalid).
+ * - Top-k paged decode: the one query token of each sequence attends to the
+ *   cache positions listed for its kv head (a set, like the block lists);
+ *   position t of sequence b is row t % page_size of page
+ *   block_table[b][t / page_size] of the paged cache, and positions at or
+ *   past cache_seqlens[b] are skipped (FSA page, main features: top-k gather
+ *   KV-cache decoding and paged attention; flash-attention-npu page,
+ *   flash_attn_with_kvcache docstring: k_cache / v_cache
+ *   [num_blocks, page_block_size, nheads_k, headdim], block_table,
+ *   cache_seqlens).
  */
 #ifndef FSA_H_
 #define FSA_H_
