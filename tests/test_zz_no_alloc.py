@@ -84,3 +84,40 @@ def test_noalloc_decode_unsplit_needs_no_scratch():
                                 num_splits=1)
     torch.cuda.synchronize()
     _close((out, lse), (ref_o, ref_l))
+
+
+@pytest.mark.parametrize("splits", [1, 5])
+def test_noalloc_decode_under_graph_capture(splits):
+    """What the entry point is for: a caller that captures its decode step in a
+    HIP graph.  The captured call is replayed three times with new queries and
+    eager work in between, and every replay is checked against an eager
+    fsa_topk_decode on the same inputs."""
+    print(f"[gpu] noalloc decode in a graph, splits={splits}", flush=True)
+    d, tok = _case(8, 16, 4, 4096, 64, 1000, seed=21)
+    g = {k: v.to(DEV) for k, v in (("q", d["q"]), ("k", d["k_cache"]), ("v", d["v_cache"]),
+                                   ("t", tok), ("bt", d["block_table"]),
+                                   ("cs", d["cache_seqlens"]))}
+    out = torch.empty_like(g["q"])
+    lse = torch.empty((8, 16), dtype=torch.float32, device=DEV)
+
+    def call():
+        fsa.fsa_topk_decode_noalloc(g["q"], g["k"], g["v"], g["t"], g["bt"], g["cs"], out, lse,
+                                    num_splits=splits)
+
+    call()                                  # first call on the device: its set-up, eagerly
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    gen = torch.Generator().manual_seed(splits)
+    for r in range(3):
+        g["q"].copy_((torch.randn(g["q"].shape, generator=gen) * (1 + r)).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (out.clone(), lse.clone())
+        ref = fsa.fsa_topk_decode(g["q"], g["k"], g["v"], g["t"], g["bt"], g["cs"],
+                                  num_splits=splits)
+        torch.cuda.synchronize()
+        _close(got, ref)
