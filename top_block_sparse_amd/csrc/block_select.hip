@@ -291,17 +291,6 @@ __global__ void __launch_bounds__(kSelectThreads, NCH == 0 ? 6 : 4) block_select
                 st[kt][i] = wi < nvis ? st[kt][i] : -INFINITY;
             }
     };
-    // the same in log2 units, masked
-    auto scores = [&](int ch, int buf, f32x4_t (&st)[4]) {
-        products(buf, st);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int wi = ch * kWinChunk + kt * 16 + lg * 4 + i;
-                st[kt][i] = wi < nvis ? st[kt][i] * c2 : -INFINITY;
-            }
-    };
 
     float* imp_row = s_imp + (valid ? t_l : 0) * nbs;
     // lanes summed before an atomic: a token's rows within the m-tile (G
@@ -310,9 +299,14 @@ __global__ void __launch_bounds__(kSelectThreads, NCH == 0 ? 6 : 4) block_select
     if constexpr (NCH == 0) {
     // Two passes over the chunks: row max and sum, then probabilities ->
     // block masses of token t_l.  Step st_i runs chunk st_i % nch from buffer
-    // st_i & 1 while the next step's chunk is fetched.
+    // st_i & 1 while the next step's chunk is fetched (every step fetches and
+    // stages one, the last step chunk 0 again, unused, so that the loads are
+    // unconditional).  Scores stay raw; the scale folds into the exponent's
+    // FMA, and chunks every row of the wave sees whole skip the mask.
     float m = -INFINITY, l = 0.f, inv = 0.f;
     const int nsteps = 2 * nch;
+    // the wave's first row has its fewest visible windows
+    const int nvis0 = __builtin_amdgcn_readfirstlane(nvis);
     if (nsteps > 0) {
         fetch(0);
         stage(0);
@@ -320,22 +314,24 @@ __global__ void __launch_bounds__(kSelectThreads, NCH == 0 ? 6 : 4) block_select
     __syncthreads();                                   // table cleared, chunk 0 staged
     for (int si = 0; si < nsteps; ++si) {
         const int ch = si % nch, buf = si & 1;
-        if (si + 1 < nsteps) fetch((si + 1) % nch);
+        fetch((si + 1) % nch);
         f32x4_t st[4];
         if (wave < p.mtiles) {
-            scores(ch, buf, st);
+            products(buf, st);
+            if ((ch + 1) * kWinChunk > nvis0) mask(ch, st);
             if (si < nch) {                                         // pass 1
-                float mx = m;
+                float mx = -INFINITY;
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[kt][i]);
+                mx = fmaxf(m, mx * c2);                             // (c2 > 0; -inf stays -inf)
                 if (mx != -INFINITY) {
                     float sum = 0.f;
 #pragma unroll
                     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) sum += fast_exp2(st[kt][i] - mx);
+                        for (int i = 0; i < 4; ++i) sum += fast_exp2(fmaf(st[kt][i], c2, -mx));
                     l = l * fast_exp2(m - mx) + sum;
                     m = mx;
                 }
@@ -360,7 +356,8 @@ __global__ void __launch_bounds__(kSelectThreads, NCH == 0 ? 6 : 4) block_select
                 for (int kt = 0; kt < 4; ++kt) {
                     float pr[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) pr[i] = st[kt][i] == -INFINITY ? 0.f : fast_exp2(st[kt][i] - m) * inv;
+                    for (int i = 0; i < 4; ++i)
+                        pr[i] = st[kt][i] == -INFINITY ? 0.f : fast_exp2(fmaf(st[kt][i], c2, -m)) * inv;
                     const int blk = ch * (kWinChunk / 4) + kt * 4 + lg;   // block of windows 4blk .. 4blk+3
                     const float own = group_sum(pr[0] + pr[1] + pr[2] + 0.5f * pr[3], gsum);
                     const float nxt = group_sum(0.5f * pr[3], gsum);
@@ -371,7 +368,7 @@ __global__ void __launch_bounds__(kSelectThreads, NCH == 0 ? 6 : 4) block_select
                 }
             }
         }
-        if (si + 1 < nsteps) stage((si + 1) & 1);
+        stage((si + 1) & 1);
         __syncthreads();
     }
     } else {
