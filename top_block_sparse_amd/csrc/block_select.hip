@@ -590,26 +590,44 @@ __global__ void __launch_bounds__(kSelectThreads, NCH == 0 ? 6 : 4) block_select
                 if (lane == n) first = x;
                 ++n;
             }
-            float* imp = s_imp + t * nbs;
+            // lane l's candidates are x = lo + l + 64 j, as 64-bit keys
+            // (importance bits, inverted id; 0 = none).  A lane keeps its
+            // largest key k1 and, until k1 is first taken, its second k2; a
+            // pick is the wave maximum of the k1s.  The lane that held it
+            // moves k2 up the first time and otherwise scans its candidates
+            // again for the largest key below the one just taken, so a scan
+            // happens only for a lane's second and later picks.
+            const float* imp = s_imp + t * nbs;
             const int lo = p.init, hi = qb - p.local + 1;
+            auto key_of = [&](int x) {
+                return ((unsigned long long)__float_as_uint(imp[x]) << 32) | (0xFFFFFFFFu - (uint32_t)x);
+            };
+            unsigned long long k1 = 0ull, k2 = 0ull;
+            for (int x = lo + lane; x < hi; x += 64) {
+                const unsigned long long key = key_of(x);
+                k2 = key > k1 ? k1 : (key > k2 ? key : k2);
+                k1 = key > k1 ? key : k1;
+            }
+            bool k2_held = true;
             while (n < p.topk && lo < hi) {
-                unsigned long long best = 0ull;
-                for (int x = lo + lane; x < hi; x += 64) {
-                    const float v = imp[x];
-                    if (v >= 0.f) {
-                        const unsigned long long key =
-                            ((unsigned long long)__float_as_uint(v) << 32) | (0xFFFFFFFFu - (uint32_t)x);
-                        best = key > best ? key : best;
-                    }
-                }
-                best = wave_max_u64(best);
+                const unsigned long long best = wave_max_u64(k1);
                 if (best == 0ull) break;                    // no candidate left
                 const int x = (int)(0xFFFFFFFFu - (uint32_t)best);
                 if (lane == n) first = x;
-                if (lane == ((x - lo) & 63)) imp[x] = -1.f;  // used
-                __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the mark lands first
-                __builtin_amdgcn_wave_barrier();
                 ++n;
+                if (k1 == best) {                           // (keys are distinct)
+                    if (k2_held) {
+                        k1 = k2;
+                        k2_held = false;
+                    } else {
+                        unsigned long long nb1 = 0ull;      // the largest key below best
+                        for (int y = lo + lane; y < hi; y += 64) {
+                            const unsigned long long key = key_of(y);
+                            nb1 = key < best && key > nb1 ? key : nb1;
+                        }
+                        k1 = nb1;
+                    }
+                }
             }
         }
         if (lane < p.topk) out[lane] = lane < n ? first : -1;   // (topk <= 64)

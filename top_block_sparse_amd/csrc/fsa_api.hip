@@ -193,6 +193,15 @@ SelectPlan plan_select(int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq, i
     // which lengths fit, and the padded table stays under 64 KiB + T * 252 B)
     const int t_lds = (int)(kSelectLdsBudget / ((size_t)pl.nb_max * 4));
     T = T < t_lds ? T : t_lds;
+    // rows over 512 windows run the two-pass kernel, whose 32 KiB of chunk
+    // buffers sit beside the table: at most 40 KiB of table (unpadded) lets
+    // two of its workgroups share a CU (2048 blocks: T = 5, 73.5 -> 63.7 ms
+    // at 131072 tokens); the support rule above is unchanged
+    if (pl.ncmp_max > 512 && T > 0) {
+        int t2 = (int)(40 * 1024 / ((size_t)pl.nb_max * 4));
+        t2 = t2 < 1 ? 1 : t2;
+        T = T < t2 ? T : t2;
+    }
     pl.T = T;                                   // 0: the table does not fit
     pl.mtiles = (T * G + 15) / 16;
     pl.tiles_per_seq = T > 0 ? (int)(((long long)max_seqlen_q + T - 1) / T) : 0;
