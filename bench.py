@@ -14,7 +14,8 @@ One step = one pass of the hot path over resident synthetic inputs:
 (4*d*64*G flops per distinct selected (token, kv head, block) triple).  The
 other prefill workloads (B=2 x 8192 tokens at G=4; varlen 65536+32768 at G=1)
 are timed as legs with their own roofline objects, and so are the FP8 decode,
-the sliding window, the backward and the block selection.  Each phase is timed
+the sliding window, the backward and the block selection (on the B=2 and on
+the long-context inputs).  Each phase is timed
 over exactly K calls issued back to back between one pair of HIP events on the
 stream the kernels run on, bracketed by device synchronisation, after W
 warm-up steps and at least 20 ms of untimed calls of that phase: the mean per
@@ -47,6 +48,7 @@ PREFILL_LEGS = (HEADLINE, PREFILL_B2, VARLEN)
 DECODE = "decode_b32_h32_kv8_d128_L32768_p256_top2048"
 WINDOW_WL = "sliding_window_512_b2_s8192_h32_kv8_d128"
 SELECT_WL = "block_select_b2_s8192_h32_kv8_d128_top16"   # lists for the B=2 prefill workload
+SELECT_LONG_WL = "block_select_long_s131072_h64_kv4_d128_top32"   # ... for the long-context one
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -252,7 +254,7 @@ def main():
                     help="approximate CPU time budget of the oracle's sampled prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=("full", "prefill", "decode", "decode_fp8", "window",
-                                       "backward", "select", "copy"),
+                                       "backward", "select", "select_long", "copy"),
                     default="full",
                     help="profiling runs: launch only one kernel family (or a plain 1 GiB "
                          "device copy used to calibrate HBM byte counters) --steps times, "
@@ -309,6 +311,8 @@ def main():
             legs[name] = PrefillLeg(name, dev, fsa, inputs)
     elif want_p:
         legs[PREFILL_B2] = PrefillLeg(PREFILL_B2, dev, fsa, inputs)
+    elif args.mode == "select_long":
+        legs[HEADLINE] = PrefillLeg(HEADLINE, dev, fsa, inputs)
     b2 = legs.get(PREFILL_B2)
 
     dspec = inputs.DECODE_WORKLOADS[DECODE]
@@ -369,6 +373,23 @@ def main():
             len(pspec.seqlens), pd["max_seqlen_k"], pspec.num_heads_kv, pspec.head_dim), 1),
             dtype=torch.uint8, device=dev)
 
+    if HEADLINE in legs:
+        # block selection over the long-context workload (rows of up to 8191
+        # windows: the two-pass kernel and the wave-per-token picks)
+        lspec, ld_, lg_ = legs[HEADLINE].spec, legs[HEADLINE].host, legs[HEADLINE].g
+        sl_pairs = sum(max(0, (i - 31) // 16 + 1) for s_len in lspec.seqlens for i in range(s_len))
+        sl_flops = 2.0 * lspec.head_dim * lspec.num_heads_q * sl_pairs
+        sl_out = torch.empty((lg_["q"].shape[0], lspec.num_heads_kv, lspec.topk), dtype=torch.int32,
+                             device=dev)
+        sl_ws = torch.empty(max(fsa.fsa_block_select_workspace_size(
+            len(lspec.seqlens), ld_["max_seqlen_k"], lspec.num_heads_kv, lspec.head_dim), 1),
+            dtype=torch.uint8, device=dev)
+
+    def select_long(i=0):
+        fsa.fsa_block_select(lg_["q"], lg_["k"], lg_["cu_seqlens_q"], lg_["cu_seqlens_k"],
+                             ld_["max_seqlen_q"], ld_["max_seqlen_k"], topk=lspec.topk,
+                             out=sl_out, workspace=sl_ws)
+
     def window(i=0):
         fsa.fsa_sliding_window_fwd(pg["q"], pg["k"], pg["v"], pg["cu_seqlens_q"],
                                    pg["cu_seqlens_k"], pd["max_seqlen_q"], pd["max_seqlen_k"],
@@ -399,7 +420,7 @@ def main():
 
     if args.mode != "full":
         step = {"decode": decode, "decode_fp8": decode_fp8, "window": window,
-                "backward": backward, "select": select}[args.mode]
+                "backward": backward, "select": select, "select_long": select_long}[args.mode]
         for i in range(W + K):
             step(i)
         torch.cuda.synchronize()
@@ -415,6 +436,7 @@ def main():
         window()
         backward()
         select()
+        select_long()
     torch.cuda.synchronize()
     fsa.fsa_wait_timeouts(reset=True)
 
@@ -432,6 +454,8 @@ def main():
     b_t = timed(backward, K, stream)
     log(f"timing {K} block-selection calls")
     s_t = timed(select, K, stream)
+    log(f"timing {K} long-context block-selection calls")
+    sl_t = timed(select_long, K, stream)
     timeouts = fsa.fsa_wait_timeouts(reset=True)
     if timeouts:
         log(f"WARNING: {timeouts} ring waits gave up during the timed calls")
@@ -497,7 +521,10 @@ def main():
     select_obj = leg_obj(s_flops, s_t, SELECT_WL, "block_select.hip",
                          "whole call: key-window means + compressed attention, block importance "
                          "and top-k (flops: one q.c product per row and visible window)")
-    for nm, o in (("window", window_obj), ("backward", backward_obj), ("select", select_obj)):
+    select_long_obj = leg_obj(sl_flops, sl_t, SELECT_LONG_WL, "block_select.hip",
+                              "whole call, as block_select, on the long-context workload's q and k")
+    for nm, o in (("window", window_obj), ("backward", backward_obj), ("select", select_obj),
+                  ("select_long", select_long_obj)):
         log(f"{nm}: mean {o['ms_per_call']:.3f} ms  {o['value']:.1f} TFLOP/s (events)")
 
     result = {
@@ -522,6 +549,7 @@ def main():
         "sliding_window": window_obj,
         "backward": backward_obj,
         "block_select": select_obj,
+        "block_select_long": select_long_obj,
         "wait_timeouts": timeouts,
     }
 
@@ -529,7 +557,8 @@ def main():
     cal = calibrate(dev, stream, K)
     result["calibration"] = cal
     for o in [result["roofline"], decode_obj["roofline"], decode_fp8_obj["roofline"],
-              window_obj["roofline"], backward_obj["roofline"], select_obj["roofline"]] + \
+              window_obj["roofline"], backward_obj["roofline"], select_obj["roofline"],
+              select_long_obj["roofline"]] + \
             [po["roofline"] for nm, po in prefill_objs.items() if nm != HEADLINE]:
         add_calibrated(o, cal)
 
