@@ -802,6 +802,8 @@ SELECT_SHAPES = [
     ((4200,), None, 128, 1, 64, 64, 1, 2),             # the largest group and topk
     ((8208,), None, 8, 2, 128, 24, 1, 2),              # 512 windows: eight full chunks, the last
                                                        # window's half in block 128
+    ((12000,), None, 1, 1, 64, 24, 1, 2),              # two passes (749 windows) with the token tile
+                                                       # capped (54, not 128), 186 candidates
 ]
 
 
