@@ -804,6 +804,8 @@ SELECT_SHAPES = [
                                                        # window's half in block 128
     ((12000,), None, 1, 1, 64, 24, 1, 2),              # two passes (749 windows) with the token tile
                                                        # capped (54, not 128), 186 candidates
+    ((9000, 100, 0, 2000), None, 4, 2, 128, 16, 1, 2), # two passes over a varlen batch with short and
+                                                       # empty sequences, wave-per-token picks
 ]
 
 
