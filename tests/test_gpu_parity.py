@@ -667,25 +667,16 @@ def test_bwd_medium_gqa_workload():
 
 
 
+@pytest.mark.timeout(600)
 def test_bwd_full_size_bench_workload():
     """The backward at B=2, S=8192, Hq=32, Hkv=8, d=128, topk 16, launched as the
-    benchmark launches it, compared element by element where the oracle can
-    compute the exact answer from a part of the problem:
-
-    * dQ of a row depends on that row alone, and under the causal mask with
-      S_q = S_k the first n tokens of a sequence form a problem of their own:
-      the oracle runs on those prefixes and every dQ element of them is
-      compared.
-    * Key j is visible only to queries i >= j, so the keys of the last n
-      positions of a sequence receive gradient from the last n queries only.
-      The oracle runs those queries against the whole key range (S_k > S_q,
-      the causal diagonal aligned at the end, so every query sees exactly the
-      keys it sees in the full problem): their dQ rows and the dK, dV rows of
-      the last n keys are exact there and every element is compared.
-    * Every softmax row has sum_j dS_ij = 0, so per (sequence, kv head) the dK
-      rows sum to zero and the dV rows sum to the dO rows of the group's heads
-      (every row sees key 0 here).  Both bounds allow the bf16 rounding of each
-      stored gradient element (2^-9 relative) plus fp32 accumulation.
+    benchmark launches it, compared element by element with the oracle run on
+    the whole problem (every dQ, dK and dV element; the oracle takes about a
+    minute on the host cores).  Independently of the oracle, every softmax row
+    has sum_j dS_ij = 0, so per (sequence, kv head) the dK rows sum to zero and
+    the dV rows sum to the dO rows of the group's heads (every row sees key 0
+    here); both bounds allow the bf16 rounding of each stored gradient element
+    (2^-9 relative) plus fp32 accumulation.
     """
     spec = inputs.PREFILL_WORKLOADS["prefill_b2_s8192_h32_kv8_d128_top16"]
     print("[gpu] backward full size: generating inputs", flush=True)
@@ -711,30 +702,11 @@ def test_bwd_full_size_bench_workload():
             assert (np.abs(k64.sum(axis=0)) <= tol_k).all(), ("sum dK", b, g)
             assert (np.abs(v64.sum(axis=0) - want_v) <= tol_v).all(), ("sum dV", b, g)
 
-    def close(a, r, what):
-        e = np.abs(a - r)
-        assert (e / (1.0 + np.abs(r))).max() <= G_REL, what
-        assert e.mean() <= G_MEAN * max(np.abs(r).mean(), 1e-3), what
-
-    n = 2048
-    dot = torch.from_numpy
-    rows = np.concatenate([np.arange(int(c), int(c) + n) for c in cu[:-1]])
-    sub = {x: dd[x][dot(rows)] for x in ("q", "k", "v", "blk_idx")}
-    cu_sub = torch.arange(0, nseq * n + 1, n, dtype=torch.int32)
-    print(f"[gpu] backward full size: oracle on the first {n} tokens of each sequence", flush=True)
-    rq, _, _ = oracle.selected_attn_bwd(sub["q"], sub["k"], sub["v"], do[dot(rows)],
-                                        sub["blk_idx"], cu_sub, cu_sub, 64)
-    close(dq[rows], rq, "dQ of the prefixes")
-
-    last = np.concatenate([np.arange(int(c) - n, int(c)) for c in cu[1:]])
-    cu_q_sub = torch.arange(0, nseq * n + 1, n, dtype=torch.int32)
-    print(f"[gpu] backward full size: oracle on the last {n} queries of each sequence", flush=True)
-    rq, rk, rv = oracle.selected_attn_bwd(dd["q"][dot(last)], dd["k"], dd["v"], do[dot(last)],
-                                          dd["blk_idx"][dot(last)], cu_q_sub,
-                                          dd["cu_seqlens_k"], 64)
-    close(dq[last], rq, "dQ of the last queries")
-    close(dk[last], rk[last], "dK of the last keys")
-    close(dv[last], rv[last], "dV of the last keys")
+    print("[gpu] backward full size: oracle on the whole problem", flush=True)
+    rq, rk, rv = oracle.selected_attn_bwd(dd["q"], dd["k"], dd["v"], do, dd["blk_idx"],
+                                          dd["cu_seqlens_q"], dd["cu_seqlens_k"], 64)
+    print("[gpu] backward full size: comparing", flush=True)
+    compare_grads((dq, dk, dv), (rq, rk, rv), what="full size")
 
 
 # ------------------------------------------------------------------ block-index producer
