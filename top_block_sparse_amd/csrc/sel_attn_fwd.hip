@@ -428,9 +428,15 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
     uint32_t tgt0 = 0, tgt1 = 0, tgt2 = 0, tgt3 = 0;   // producers: done counts that free each slot
     for (int win_lo = nb_lo; win_lo < nb_range; win_lo += kSelWin) {
         const int win_n = (nb_range - win_lo) < kSelWin ? (nb_range - win_lo) : kSelWin;
+        // The thread index, opaque here: the per-thread addresses and masks of
+        // the union build are derived from it inside the loop, so the compiler
+        // cannot hoist them out and keep them live (and spilled) across the
+        // ring loop.
+        int tid_w = tid;
+        asm volatile("" : "+v"(tid_w));
         if (WIN && p.dense) {
             // every block of the window: the tokens whose key range meets it
-            for (int x = tid; x < win_n; x += kSelThreads) {
+            for (int x = tid_w; x < win_n; x += kSelThreads) {
                 unsigned long long mk = 0ull;
                 {
                     const long long bk = (long long)(win_lo + x) * kBlockKeys;
@@ -447,9 +453,9 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
             }
             lds_barrier();
         } else {
-            for (int x = tid; x < win_n; x += kSelThreads) s_masks[x] = 0ull;   // (only these are read)
+            for (int x = tid_w; x < win_n; x += kSelThreads) s_masks[x] = 0ull;   // (only these are read)
             lds_barrier();
-            for (int e = tid; e < nent; e += kSelThreads) {
+            for (int e = tid_w; e < nent; e += kSelThreads) {
                 const int id = s_ent[e];
                 if (id >= win_lo && id < win_lo + win_n) atomicOr(&s_masks[id - win_lo], 1ull << (e / topk));
             }
@@ -458,14 +464,14 @@ sel_attn_fwd_kernel(const SelFwdParams p) {
         if (wave == 0) {      // ascending compaction of the non-empty blocks
             // m-tile `lane`'s tokens, for the need counts (per window, so
             // that nothing stays live across the ring loop)
-            const unsigned long long cm_lane = mtile_token_mask(lane, G, ntok, p.mtiles);
+            const unsigned long long cm_lane = mtile_token_mask(tid_w & 63, G, ntok, p.mtiles);
             int n = 0;
             for (int c = 0; c < win_n; c += 64) {
-                const int x = c + lane;
+                const int x = c + (tid_w & 63);
                 const unsigned long long m = x < win_n ? s_masks[x] : 0ull;
                 const unsigned long long bal = __ballot(m != 0ull);
                 if (m != 0ull) {
-                    const int pos = n + __popcll(bal & ((1ull << lane) - 1ull));
+                    const int pos = n + __popcll(bal & ((1ull << (tid_w & 63)) - 1ull));
                     // consumers (m-tiles) that need the block
                     const int nc = mtiles_meeting(m, cm_lane, p.mtiles);
                     s_ulist[pos] = win_lo + x;
