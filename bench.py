@@ -12,8 +12,8 @@ One step = one pass of the hot path over resident synthetic inputs:
     still on chip from the previous one.
 ``value`` is that prefill's effective TFLOP/s over the K timed calls
 (4*d*64*G flops per distinct selected (token, kv head, block) triple).  The
-other prefill workloads (B=2 x 8192 tokens at G=4; varlen 65536+32768 at G=1)
-are timed as legs with their own roofline objects, and so are the FP8 decode,
+other prefill workloads (B=2 x 8192 tokens at G=4; varlen 65536+32768 at G=1;
+the small 1024-token case at G=4, d=64, which is launch-bound) are timed as legs with their own roofline objects, and so are the FP8 decode,
 the sliding window, the backward and the block selection (on the B=2 and on
 the long-context inputs).  Each phase is timed
 over exactly K calls issued back to back between one pair of HIP events on the
@@ -44,7 +44,7 @@ HEADLINE = "long_s131072_h64_kv4_d128_top32_zipf"
 PREFILL_B2 = "prefill_b2_s8192_h32_kv8_d128_top16"
 VARLEN = "varlen_65536+32768_h4_kv4_d128_top16"
 SMALL = "prefill_s1024_h4_kv1_d64_top4"
-PREFILL_LEGS = (HEADLINE, PREFILL_B2, VARLEN)
+PREFILL_LEGS = (HEADLINE, PREFILL_B2, VARLEN, SMALL)
 DECODE = "decode_b32_h32_kv8_d128_L32768_p256_top2048"
 WINDOW_WL = "sliding_window_512_b2_s8192_h32_kv8_d128"
 SELECT_WL = "block_select_b2_s8192_h32_kv8_d128_top16"   # lists for the B=2 prefill workload
